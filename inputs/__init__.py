@@ -1,0 +1,17 @@
+"""Seeded synthetic inputs shared by the oracle-side tests, the GPU tests and the benchmark.
+
+This package draws random tensors and builds the learned-parameter inputs (the RoPE
+frequency table and the low-rank bias factors) that the attention operator receives.
+It holds none of the attention arithmetic itself: no rotation, no scores, no softmax.
+"""
+
+from .generate import (  # noqa: F401
+    CONFIGS,
+    WorkloadConfig,
+    round_bf16,
+    qkv,
+    omega_schedule,
+    theta_table,
+    rib_factors,
+    make_inputs,
+)

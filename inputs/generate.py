@@ -1,0 +1,197 @@
+"""Seeded generators for the window-attention workloads.
+
+Workload shapes stand in for the pages' measured settings (no dataset or trained
+weights are used anywhere):
+
+* FlashSwin-T stage 1 at 256 px and patch 4 is a 64x64 token grid with C = 96 = 3 heads
+  x 32; patch 2 makes it 128x128 (FlashSwin page, efficiency and accuracy results).
+* SST super-resolution windows reach 96x96 tokens (RIB/SST page, key contributions).
+
+Q, K, V are i.i.d. N(0, 1) drawn in float32 and rounded once to bfloat16 (round to
+nearest even) for the bf16 workloads; the arrays returned are float32 holding exactly
+those bf16 values, so the oracle and the device see identical numbers.
+
+Learned-parameter inputs:
+
+* ``theta_table``: theta = exp(omega) per rotation pair, omega from the geometric RoPE
+  schedule (FlashSwin page, "How it works", second change: frequencies are
+  parameterised as exp(omega) and initialised from the standard geometric schedule),
+  optionally perturbed by N(0, sigma^2) noise.  The default ("shared") reading gives the
+  y half and the x half the same d/4 frequencies, stored as a d/2-entry table per head.
+* ``rib_factors``: the rank-r bias factors U, V of the RIB page (section 2.1): window-local
+  token coordinates -> Fourier features -> small seeded MLP -> (U, V).  This is an input
+  generator, not part of what the operator computes.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadConfig:
+    name: str
+    dtype: str          # "bf16" or "fp32"
+    B: int
+    Hg: int
+    Wg: int
+    M: int
+    shift: int
+    H: int
+    d: int
+    r: int              # bias rank (0 = no bias)
+    rope: bool
+    omega_noise: float  # std of the N(0, s^2) perturbation of omega
+    seed: int           # base seed; q/k/v use seed, omega noise seed+1000, MLP seed+2000
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.Hg * self.Wg
+
+    @property
+    def N(self) -> int:
+        return self.M * self.M
+
+    def dense_flops(self) -> float:
+        """4 * T * N * d * H: QK^T plus PV over every (query, key) pair of each window."""
+        return 4.0 * self.tokens * self.N * self.d * self.H
+
+    def io_bytes(self) -> int:
+        """q, k, v read once and out written once."""
+        esize = 2 if self.dtype == "bf16" else 4
+        return 4 * self.tokens * self.H * self.d * esize
+
+
+def _cfg(name, dtype, B, Hg, Wg, M, shift, H, d, r, rope, noise, seed):
+    return WorkloadConfig(name, dtype, B, Hg, Wg, M, shift, H, d, r, rope, noise, seed)
+
+
+# The workloads: a tiny fp32 case, a Swin-T stage-1-like layer, a large-window layer,
+# the dense patch-2 grid at M = 32 (plus its M sweep) and the SR-style M = 96 layer with
+# a rank-16 bias.
+CONFIGS = {
+    "tiny_fp32": _cfg("tiny_fp32", "fp32", 1, 16, 16, 8, 0, 2, 32, 0, True, 0.0, 1001),
+    "swin_t_m8": _cfg("swin_t_m8", "bf16", 64, 64, 64, 8, 4, 3, 32, 0, True, 0.1, 1002),
+    "large_m32": _cfg("large_m32", "bf16", 64, 64, 64, 32, 16, 3, 32, 0, True, 0.1, 1003),
+    "dense_p2_m32": _cfg("dense_p2_m32", "bf16", 16, 128, 128, 32, 16, 3, 32, 0, True, 0.1, 1004),
+    "dense_p2_m16": _cfg("dense_p2_m16", "bf16", 16, 128, 128, 16, 8, 3, 32, 0, True, 0.1, 1004),
+    "dense_p2_m8": _cfg("dense_p2_m8", "bf16", 16, 128, 128, 8, 4, 3, 32, 0, True, 0.1, 1004),
+    "sr_m96_rib": _cfg("sr_m96_rib", "bf16", 8, 192, 192, 96, 0, 6, 32, 16, False, 0.0, 1005),
+}
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32.
+
+    NaN stays NaN; values beyond the bf16 range round to +-inf as IEEE rounding does.
+    """
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    bits = a.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    out = (rounded & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    nan = np.isnan(a)
+    if nan.any():
+        out = out.copy()
+        out[nan] = np.nan
+    return out.reshape(a.shape)
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def qkv(shape, seed: int, dtype: str = "bf16"):
+    """Three i.i.d. N(0,1) tensors of ``shape`` ([B, Hg, Wg, H, d]), drawn in the order q, k, v."""
+    rng = _rng(seed)
+    out = []
+    for _ in range(3):
+        t = rng.standard_normal(size=shape, dtype=np.float32)
+        out.append(round_bf16(t) if dtype == "bf16" else t)
+    return tuple(out)
+
+
+def omega_schedule(H: int, d: int, shared: bool = True) -> np.ndarray:
+    """Initial log-frequencies omega per head, float64.
+
+    shared=True: d/4 values per head (one set used by both axes), omega_j = -(4j/d) ln 10000,
+    i.e. the geometric base-10000 schedule of a rotary subspace of d/2 dimensions.
+    shared=False: d/2 values, omega_j = -(2j/d) ln 10000 (the 1D schedule over all d dims).
+    """
+    n = d // 4 if shared else d // 2
+    step = 4.0 / d if shared else 2.0 / d
+    w = -np.arange(n, dtype=np.float64) * step * math.log(10000.0)
+    return np.broadcast_to(w, (H, n)).copy()
+
+
+def theta_table(H: int, d: int, noise_std: float = 0.0, seed: int = 0, shared: bool = True) -> np.ndarray:
+    """Per-rotation-pair frequencies theta[h][j], j in [0, d/2), as float32.
+
+    Pairs j < d/4 rotate the first half of the head dimension (y), pairs j >= d/4 the
+    second half (x).  With shared=True both halves use the same theta = exp(omega).
+    """
+    w = omega_schedule(H, d, shared)
+    if noise_std > 0:
+        w = w + _rng(seed).normal(0.0, noise_std, size=w.shape)
+    th = np.exp(w)
+    if shared:
+        th = np.concatenate([th, th], axis=1)
+    return th.astype(np.float32)
+
+
+def _gelu_erf(x: np.ndarray) -> np.ndarray:
+    from scipy.special import erf
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def rib_factors(H: int, M: int, r: int, seed: int, dtype: str = "bf16", n_freq: int = 4, hidden: int = 64):
+    """Rank-r bias factors U, V of shape [H, M*M, r] for window-local coordinates.
+
+    Coordinates (row, col) in [0, M) are mapped to [-1, 1]; the features are
+    sin/cos(2^k pi yhat), sin/cos(2^k pi xhat) for k < n_freq (16 features for n_freq=4);
+    a seeded two-layer MLP (hidden 64, exact-erf GELU, weights N(0, 1/fan_in), zero
+    biases) maps them to 2*H*r outputs, split into U[h] and V[h].  Computed in float64,
+    then rounded to the workload dtype.
+    """
+    n = np.arange(M * M)
+    rr = (n // M).astype(np.float64)
+    cc = (n % M).astype(np.float64)
+    den = max(M - 1, 1)
+    yh = 2.0 * rr / den - 1.0
+    xh = 2.0 * cc / den - 1.0
+    feats = []
+    for kk in range(n_freq):
+        f = (2.0 ** kk) * math.pi
+        feats += [np.sin(f * yh), np.cos(f * yh), np.sin(f * xh), np.cos(f * xh)]
+    F = np.stack(feats, axis=1)                                  # [N, 4*n_freq]
+    rng = _rng(seed)
+    W1 = rng.normal(0.0, 1.0 / math.sqrt(F.shape[1]), size=(F.shape[1], hidden))
+    W2 = rng.normal(0.0, 1.0 / math.sqrt(hidden), size=(hidden, 2 * H * r))
+    hdn = _gelu_erf(F @ W1)
+    o = hdn @ W2                                                 # [N, 2*H*r]
+    U = o[:, : H * r].reshape(M * M, H, r).transpose(1, 0, 2)
+    V = o[:, H * r:].reshape(M * M, H, r).transpose(1, 0, 2)
+    U = np.ascontiguousarray(U.astype(np.float32))
+    V = np.ascontiguousarray(V.astype(np.float32))
+    if dtype == "bf16":
+        U, V = round_bf16(U), round_bf16(V)
+    return U, V
+
+
+def make_inputs(cfg: WorkloadConfig, batch: int | None = None, shared_theta: bool = True):
+    """All inputs of a workload as float32 numpy arrays (bf16-exact for bf16 workloads).
+
+    Returns dict(q, k, v, theta or None, bias_u or None, bias_v or None).  ``batch``
+    overrides B (a prefix of the same random stream is NOT implied; it is a new draw).
+    """
+    B = cfg.B if batch is None else batch
+    shape = (B, cfg.Hg, cfg.Wg, cfg.H, cfg.d)
+    q, k, v = qkv(shape, cfg.seed, cfg.dtype)
+    theta = theta_table(cfg.H, cfg.d, cfg.omega_noise, cfg.seed + 1000, shared_theta) if cfg.rope else None
+    U = V = None
+    if cfg.r > 0:
+        U, V = rib_factors(cfg.H, cfg.M, cfg.r, cfg.seed + 2000, cfg.dtype)
+    return dict(q=q, k=k, v=v, theta=theta, bias_u=U, bias_v=V)

@@ -1,0 +1,20 @@
+"""CPU oracle (float64, materialised scores) for fused shifted-window attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by the
+CPU-baseline leg of bench.py, never by the HIP library or its binding.
+"""
+
+from .wattn_oracle import (  # noqa: F401
+    local_coords,
+    window_token_coords,
+    region_label,
+    shift_mask,
+    rope_angles,
+    rope_rotate,
+    window_logits,
+    softmax_rows,
+    window_weights,
+    window_head_output,
+    window_attention,
+    unmasked_pairs,
+)
