@@ -1,0 +1,126 @@
+/*
+ * wattn.h -- C ABI of libwattn.so: fused shifted-window softmax attention with
+ * window-local learned 2D RoPE and a folded low-rank position bias, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *
+ *   FLASHSWIN: Unlocking Large Windows and Dense Tokens in Swin Vision Transformers with
+ *   Memory Efficient Attention -- "What it is": attention is restricted to non-overlapping
+ *   M x M windows of the token grid.  "How it works", first change: the window attention
+ *   is one IO-aware fused pass with an online softmax; the N x N score matrix (N = M*M)
+ *   is never stored and the result is exact softmax attention.  Second change: Q and K
+ *   get a window-local learned 2D rotary embedding (first half of the head dimension
+ *   encodes the row y, second half the column x, theta = exp(omega)); in shifted-window
+ *   layers the grid is cyclically shifted, coordinates are recomputed per window, and the
+ *   wrapped windows are masked.  Mixed-precision note (closing developer paragraph):
+ *   bf16 Q/K/V, RoPE applied in fp32, softmax accumulated in fp32.
+ *
+ *   Rank-Factorized Implicit Neural Bias: Scaling Super-Resolution Transformer with
+ *   FlashAttention -- section 2.1: a low-rank bias enters as extra channels,
+ *   [Q_c, Q_p][K_c, K_p]^T = Q_c K_c^T + Q_p K_p^T, so no N x N bias matrix exists.
+ *
+ * For image b, head h and window w of the grid rolled by -shift, with window-local
+ * coordinates p_n = (r_n, c_n) in [0, M)^2 (n = r*M + c):
+ *
+ *   logit[n][m] = <R(p_n) q_n, R(p_m) k_m> / sqrt(d)  +  <bias_u[h][n], bias_v[h][m]>
+ *                 + (0 if n and m lie in the same wrap region of the window, else -inf)
+ *   out_n       = sum_m softmax_m(logit[n][.]) v_m
+ *
+ * q_n is read from, and out_n written to, the token's ORIGINAL grid position
+ * ((Y + shift) mod Hgrid, (X + shift) mod Wgrid) where (Y, X) is its rolled position, so
+ * the cyclic shift and its reversal are part of the call.  R(p) rotates adjacent pairs
+ * (2j, 2j+1) counter-clockwise by r*theta[h][j] for j < d/4 and by c*theta[h][j] for
+ * j >= d/4.  Region labels per axis (rolled coordinate P on an axis of length G):
+ * 0 if P < G - M, 1 if P < G - shift, else 2; a pair is masked iff the labels differ on
+ * either axis (no pair is masked when shift == 0).
+ */
+#ifndef WATTN_H
+#define WATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WATTN_ABI_VERSION 1
+
+/* Element types.  The bf16 modes run QK^T and PV on bf16 matrix cores with fp32 RoPE,
+ * fp32 softmax and fp32 accumulation; they differ only in the type of `out`.  A bf16
+ * `out` adds its own rounding (up to 2^-9 relative) on top of the kernel's error. */
+typedef enum {
+  WATTN_BF16 = 0,          /* q, k, v, bias_u, bias_v and out in bfloat16 */
+  WATTN_FP32 = 1,          /* everything in float32 (plain fp32 arithmetic, no matrix cores) */
+  WATTN_BF16_OUT_FP32 = 2  /* q, k, v, bias_u, bias_v in bfloat16, out in float32 */
+} wattn_dtype_t;
+
+/* Status codes.  Every invalid argument is detected on the host before any HIP call,
+ * and nothing is written when a call fails. */
+typedef enum {
+  WATTN_OK = 0,
+  WATTN_ERR_NULL = 1,     /* q, k, v or out is NULL */
+  WATTN_ERR_SHAPE = 2,    /* a size <= 0, M > WATTN_MAX_M, grid not a multiple of M, or too large */
+  WATTN_ERR_SHIFT = 3,    /* shift outside [0, M) */
+  WATTN_ERR_HEAD_DIM = 4, /* d not supported (this version: d == 32) */
+  WATTN_ERR_RANK = 5,     /* r not in {0, 16}, or bias pointers inconsistent with r */
+  WATTN_ERR_DTYPE = 6,    /* unknown dtype enum */
+  WATTN_ERR_ALIAS = 7,    /* out overlaps an input buffer */
+  WATTN_ERR_HIP = 8,      /* HIP runtime error (no device, launch failure, ...) */
+  WATTN_ERR_POINTER = 9   /* a buffer is not device-accessible memory */
+} wattn_status_t;
+
+#define WATTN_MAX_M 128
+
+/*
+ * wattn_forward -- out = shifted-window attention of (q, k, v); see the header comment.
+ *
+ * q, k, v, out : device pointers, [B][Hgrid][Wgrid][H][d] contiguous (token-major, the
+ *                layout a qkv projection writes), element types given by `dtype`.
+ *                Read-only except `out`.  `out` must not overlap any input.
+ * B, H         : images and heads, >= 1.
+ * Hgrid, Wgrid : token grid; each a positive multiple of M.
+ * M            : window side, 1 <= M <= WATTN_MAX_M (N = M*M tokens per window).
+ * shift        : cyclic shift in [0, M); 0 = regular windows.
+ * d            : head dimension (supported: 32).
+ * theta        : device pointer, float32 [H][d/2] rotation-pair frequencies
+ *                (theta = exp(omega)), or NULL for no rotary embedding.
+ * bias_u,
+ * bias_v       : device pointers, [H][M*M][r] of q's element type, indexed by the
+ *                window-local token index n = r*M + c; both NULL when r == 0.
+ * r            : bias rank, 0 or 16.
+ * dtype        : a wattn_dtype_t value.
+ * stream       : hipStream_t to launch on; NULL = the default stream.
+ *
+ * The call only launches work: it returns after enqueueing on `stream`, allocates no
+ * memory, keeps no state and is safe to call from several threads.  The caller owns
+ * every buffer and must keep it alive until the stream has run the work.  Scale is
+ * d^-1/2 on the content logits; the bias is added unscaled.  NaN or Inf inputs
+ * propagate to the output and are not checked.
+ *
+ * Returns WATTN_OK or one of the WATTN_ERR_* codes above.
+ */
+int wattn_forward(const void* q, const void* k, const void* v, void* out,
+                  int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                  const float* theta, const void* bias_u, const void* bias_v, int r,
+                  int dtype, void* stream);
+
+/*
+ * wattn_pair_count -- number of (query, key) pairs with a finite logit in a call with
+ * these sizes (the masked pairs of wrapped windows excluded).  Pure host arithmetic:
+ * no HIP call, no side effect.  Returns -1 for sizes wattn_forward would reject with
+ * WATTN_ERR_SHAPE or WATTN_ERR_SHIFT.
+ */
+int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* wattn_status_string(int status);
+
+/* WATTN_ABI_VERSION of the loaded library. */
+int wattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WATTN_H */

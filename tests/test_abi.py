@@ -1,0 +1,98 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/wattn.h declares,
+and rejects every invalid argument on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+import vision_transformer_windowed_window_amd as wattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wattn.h")
+
+# fake, never-dereferenced addresses: validation fails before any pointer is used
+P1, P2, P3, P4 = 0x100000, 0x200000, 0x300000, 0x400000
+TH, BU, BV = 0x500000, 0x600000, 0x700000
+
+
+def _lib():
+    return wattn.load_library()
+
+
+def _call(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, theta=None, bu=None, bv=None,
+          r=0, dtype=0):
+    vp = ctypes.c_void_p
+    return _lib().wattn_forward(vp(q), vp(k), vp(v), vp(out), B, H, Hg, Wg, M, s, d, vp(theta), vp(bu), vp(bv), r,
+                                dtype, vp(None))
+
+
+def test_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
+    assert names == {"wattn_forward", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
+    lib = _lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    m = re.search(r"#define WATTN_ABI_VERSION (\d+)", text)
+    assert wattn.abi_version() == int(m.group(1))
+
+
+def test_status_enum_matches_header_and_strings():
+    text = open(HEADER).read()
+    for code, name in wattn.STATUS.items():
+        assert re.search(rf"\b{name} = {code}\b", text), name
+        assert wattn.status_string(code) and wattn.status_string(code) != "unknown status"
+    assert wattn.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
+        (dict(B=0), 2), (dict(H=0), 2), (dict(Hg=0), 2), (dict(Wg=-8), 2), (dict(M=0), 2),
+        (dict(Hg=20), 2), (dict(Wg=12), 2), (dict(M=256, Hg=256, Wg=256), 2),
+        (dict(s=-1), 3), (dict(s=8), 3), (dict(s=9), 3),
+        (dict(d=64), 4), (dict(d=16), 4), (dict(d=33), 4),
+        (dict(r=8, bu=BU, bv=BV), 5), (dict(r=16), 5), (dict(r=16, bu=BU), 5), (dict(r=0, bu=BU, bv=BV), 5),
+        (dict(r=-1), 5),
+        (dict(dtype=3), 6), (dict(dtype=-1), 6),
+        (dict(dtype=2, out=P1 - 16 * 16 * 2 * 32 * 4 + 8), 7),
+        (dict(out=P1), 7), (dict(out=P1 + 100), 7), (dict(out=P2 - 10), 7), (dict(out=TH, theta=TH), 7),
+        (dict(r=16, bu=BU, bv=BV, out=BV + 64), 7),
+    ],
+)
+def test_invalid_arguments_are_rejected_on_the_host(kw, status):
+    assert _call(**kw) == status
+
+
+def test_no_device_reports_hip_error():
+    """With every device hidden, a valid-looking call fails with WATTN_ERR_HIP and launches nothing."""
+    code = (
+        "import ctypes, sys; sys.path.insert(0, %r);"
+        "import vision_transformer_windowed_window_amd as w; L = w.load_library(); v = ctypes.c_void_p;"
+        "print(L.wattn_forward(v(0x100000), v(0x200000), v(0x300000), v(0x400000), 1, 2, 16, 16, 8, 0, 32,"
+        " v(None), v(None), v(None), 0, 0, v(None)))" % ROOT
+    )
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert int(res.stdout.strip().splitlines()[-1]) == 8
+
+
+@pytest.mark.parametrize(
+    "B,H,Hg,Wg,M,s",
+    [(1, 1, 16, 16, 8, 0), (2, 3, 64, 64, 8, 4), (1, 3, 64, 64, 32, 16), (1, 1, 128, 128, 32, 16),
+     (1, 2, 32, 48, 8, 3), (1, 1, 8, 8, 8, 5), (1, 1, 96, 96, 96, 0), (1, 1, 24, 16, 8, 7)],
+)
+def test_pair_count_matches_oracle(B, H, Hg, Wg, M, s):
+    assert wattn.pair_count(B, H, Hg, Wg, M, s) == oracle.unmasked_pairs(B, H, Hg, Wg, M, s)
+
+
+def test_pair_count_rejects_bad_sizes():
+    assert wattn.pair_count(1, 1, 20, 16, 8, 0) == -1
+    assert wattn.pair_count(1, 1, 16, 16, 8, 8) == -1

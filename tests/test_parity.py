@@ -1,0 +1,221 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the same
+seeded inputs.  Bounds: bf16 max|err| <= 1e-2 and relative L2 <= 5e-3; fp32 max|err| <= 1e-5."""
+
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from inputs import CONFIGS, make_inputs, qkv, rib_factors, round_bf16, theta_table
+from parity_util import check, note, oracle_full, oracle_sampled, run_gpu, sample_units
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, Hg, Wg, H, M, dtype, seed, rope=True, r=0, noise=0.1, shared=True, qscale=1.0):
+    q, k, v = qkv((B, Hg, Wg, H, 32), seed, dtype)
+    if qscale != 1.0:
+        q = q * np.float32(qscale)
+        q = round_bf16(q) if dtype == "bf16" else q
+    th = theta_table(H, 32, noise, seed + 1, shared) if rope else None
+    U = V = None
+    if r:
+        U, V = rib_factors(H, M, r, seed + 2, dtype)
+    return dict(q=q, k=k, v=v, theta=th, bias_u=U, bias_v=V)
+
+
+# ------------------------------------------------------------------ small, full compare
+
+SMALL = [
+    # label, B, Hg, Wg, H, M, shift, dtype, rope, r
+    ("fp32_m8_s3_bias", 1, 16, 24, 2, 8, 3, "fp32", True, 16),
+    ("fp32_m16_s0", 1, 32, 16, 1, 16, 0, "fp32", True, 0),
+    ("bf16_m32_s16", 2, 64, 64, 2, 32, 16, "bf16", True, 0),
+    ("bf16_m16_s5_ragged", 1, 48, 32, 2, 16, 5, "bf16", True, 0),
+    ("bf16_m8_s3", 2, 24, 32, 3, 8, 3, "bf16", True, 0),
+    ("bf16_m24_s0_ragged_qtile", 1, 48, 72, 1, 24, 0, "bf16", True, 0),
+    ("bf16_m16_s8_rope_bias", 1, 32, 32, 2, 16, 8, "bf16", True, 16),
+    ("bf16_m48_bias_norope", 1, 48, 96, 1, 48, 0, "bf16", False, 16),
+    ("bf16_single_window_shift", 2, 16, 16, 2, 16, 7, "bf16", True, 0),
+    ("bf16_nonsquare_m16_s4", 1, 32, 64, 2, 16, 4, "bf16", True, 0),
+    ("bf16_m4_s1", 1, 8, 12, 2, 4, 1, "bf16", True, 0),
+    ("bf16_m2_s1", 1, 4, 6, 1, 2, 1, "bf16", True, 0),
+    ("bf16_m1", 1, 3, 5, 2, 1, 0, "bf16", True, 0),
+    ("bf16_m40_s13_bias", 1, 40, 80, 1, 40, 13, "bf16", True, 16),
+    ("bf16_norope_nobias", 1, 32, 32, 2, 16, 8, "bf16", False, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_full_compare(case):
+    label, B, Hg, Wg, H, M, s, dtype, rope, r = case
+    note(f"start {label}")
+    inp = _inputs(B, Hg, Wg, H, M, dtype, seed=zlib.crc32(label.encode()) % 10000, rope=rope, r=r)
+    got = run_gpu(inp, dtype, M, s)
+    check(got, oracle_full(inp, M, s), dtype, label)
+
+
+def test_tiny_fp32_workload():
+    cfg = CONFIGS["tiny_fp32"]
+    note("start tiny_fp32 workload")
+    inp = make_inputs(cfg)
+    got = run_gpu(inp, "fp32", cfg.M, cfg.shift)
+    check(got, oracle_full(inp, cfg.M, cfg.shift), "fp32", "tiny_fp32")
+
+
+def test_unshared_theta_table():
+    note("start unshared theta")
+    inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=77, shared=False)
+    got = run_gpu(inp, "bf16", 16, 8)
+    check(got, oracle_full(inp, 16, 8), "bf16", "unshared_theta")
+
+
+def test_growing_logits_exercise_the_rescale():
+    """A bias that raises every later key tile by 3 (natural-log units) makes the running
+    max grow by more than 2^16 in probability ratio every few tiles, so the exact rescale
+    runs repeatedly; the bias values are exact in bf16."""
+    note("start growing logits")
+    B, Hg, Wg, H, M, r = 1, 32, 64, 2, 32, 16
+    inp = _inputs(B, Hg, Wg, H, M, "bf16", seed=91, rope=True, r=0)
+    U = np.zeros((H, M * M, r), dtype=np.float32)
+    V = np.zeros((H, M * M, r), dtype=np.float32)
+    U[:, :, 0] = 3.0
+    V[:, :, 0] = (np.arange(M * M) // 64).astype(np.float32)
+    inp["bias_u"], inp["bias_v"] = U, V
+    got = run_gpu(inp, "bf16", M, 0)
+    check(got, oracle_full(inp, M, 0), "bf16", "growing_logits")
+    # shrinking logits: the first tile holds the max, later tiles underflow towards 0
+    inp["bias_u"] = -U
+    got = run_gpu(inp, "bf16", M, 0)
+    check(got, oracle_full(inp, M, 0), "bf16", "shrinking_logits")
+
+
+BF16_OUT = [
+    ("bf16out_m8_s3", 2, 24, 32, 3, 8, 3, True, 0),
+    ("bf16out_m32_s16", 1, 64, 64, 2, 32, 16, True, 0),
+    ("bf16out_m16_bias", 1, 32, 32, 2, 16, 8, True, 16),
+]
+
+
+@pytest.mark.parametrize("case", BF16_OUT, ids=[c[0] for c in BF16_OUT])
+def test_bf16_output(case):
+    label, B, Hg, Wg, H, M, s, rope, r = case
+    note(f"start {label}")
+    inp = _inputs(B, Hg, Wg, H, M, "bf16", seed=zlib.crc32(label.encode()) % 10000, rope=rope, r=r)
+    got = run_gpu(inp, "bf16", M, s, out="bf16")
+    check(got, oracle_full(inp, M, s), "bf16", label, out_bf16=True)
+
+
+def test_large_query_scale():
+    """Peaked softmax (logits with std ~2.5)."""
+    note("start large q scale")
+    inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=5, qscale=2.5)
+    got = run_gpu(inp, "bf16", 16, 8)
+    check(got, oracle_full(inp, 16, 8), "bf16", "q_x2.5")
+
+
+# ------------------------------------------------------------ workloads at full size
+
+FULL_SAMPLED = ["swin_t_m8", "large_m32", "dense_p2_m32", "dense_p2_m16", "dense_p2_m8", "sr_m96_rib"]
+
+
+@pytest.mark.parametrize("name", FULL_SAMPLED)
+def test_workload_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    note(f"start {name} full size")
+    inp = make_inputs(cfg)
+    got = run_gpu(inp, cfg.dtype, cfg.M, cfg.shift)
+    assert np.all(np.isfinite(got))
+    count = 3 if cfg.M >= 96 else 12
+    units = sample_units(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, count, seed=cfg.seed)
+    refs = oracle_sampled(inp, cfg.M, cfg.shift, units)
+    g = np.concatenate([got[b, y, x, h, :] for (b, y, x, h, _) in refs])
+    r = np.concatenate([o for (_, _, _, _, o) in refs])
+    check(g, r, cfg.dtype, f"{name} ({len(units)} window-heads)")
+
+
+def test_swin_t_m8_full_compare():
+    cfg = CONFIGS["swin_t_m8"]
+    note("start swin_t_m8 full compare (8 images)")
+    inp = make_inputs(cfg, batch=8)
+    got = run_gpu(inp, cfg.dtype, cfg.M, cfg.shift)
+    check(got, oracle_full(inp, cfg.M, cfg.shift), cfg.dtype, "swin_t_m8 B=8")
+
+
+# --------------------------------------------------------------------- other properties
+
+
+def test_deterministic_bitwise():
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from parity_util import to_device
+
+    note("start determinism")
+    cfg = CONFIGS["large_m32"]
+    t = to_device(make_inputs(cfg, batch=2), "bf16")
+    a = wattn.forward(t["q"], t["k"], t["v"], M=cfg.M, shift=cfg.shift, theta=t["theta"])
+    b = wattn.forward(t["q"], t["k"], t["v"], M=cfg.M, shift=cfg.shift, theta=t["theta"])
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [8, 16, 32])
+def test_memory_flat_in_window_size(M):
+    """No device memory beyond the caller's output is allocated, whatever M."""
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    note(f"start memory M={M}")
+    B, G, H = 2, 64, 3
+    q = torch.randn(B, G, G, H, 32, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn_like(q)
+    v = torch.randn_like(q)
+    th = torch.from_numpy(theta_table(H, 32, 0.1, 3)).cuda()
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.max_memory_allocated()
+    wattn.forward(q, k, v, M=M, shift=M // 2, theta=th, out=out)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() - base == 0
+
+
+def test_runs_on_a_side_stream():
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from parity_util import to_device
+
+    note("start side stream")
+    inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=8)
+    t = to_device(inp, "bf16")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o = wattn.forward(t["q"], t["k"], t["v"], M=16, shift=8, theta=t["theta"])
+    s.synchronize()
+    check(o.float().cpu().numpy().astype(np.float64), oracle_full(inp, 16, 8), "bf16", "side_stream")
+
+
+def test_pointer_checks_with_real_buffers():
+    """A host buffer is rejected before launch; so is an invalid shift."""
+    import ctypes
+
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    note("start pointer checks")
+    L = wattn.load_library()
+    vp = ctypes.c_void_p
+    q = torch.zeros(1, 16, 16, 2, 32, device="cuda", dtype=torch.bfloat16)
+    k, v, o = torch.zeros_like(q), torch.zeros_like(q), torch.zeros_like(q)
+    host = np.zeros(16 * 16 * 2 * 32, dtype=np.uint16)
+    st = L.wattn_forward(vp(host.ctypes.data), vp(k.data_ptr()), vp(v.data_ptr()), vp(o.data_ptr()),
+                         1, 2, 16, 16, 8, 0, 32, vp(None), vp(None), vp(None), 0, 0, vp(None))
+    assert st == 9
+    with pytest.raises(wattn.WattnError):
+        wattn.forward(q, k, v, M=8, shift=8)

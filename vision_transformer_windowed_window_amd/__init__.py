@@ -1,0 +1,165 @@
+"""Fused shifted-window attention for AMD Instinct MI355X -- Python binding of libwattn.so.
+
+This module only marshals arguments: it checks tensor shapes and dtypes, passes device
+pointers and the current HIP stream to the C ABI declared in include/wattn.h, and turns a
+non-zero status into an exception.  Every step of the computation runs in the HIP
+kernels of libwattn.so; there is no fallback.  If the library has not been built, every
+call raises.
+
+    out = forward(q, k, v, M=32, shift=16, theta=theta)
+
+q, k, v: [B, Hgrid, Wgrid, H, 32] contiguous device tensors, bfloat16 or float32.
+theta:   [H, 16] float32 device tensor of rotation-pair frequencies, or None (no RoPE).
+bias_u, bias_v: [H, M*M, 16] device tensors of the input dtype, or None (no bias).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "forward",
+    "pair_count",
+    "abi_version",
+    "status_string",
+    "library_path",
+    "load_library",
+    "WattnError",
+    "BF16",
+    "FP32",
+    "BF16_OUT_FP32",
+    "STATUS",
+]
+
+BF16 = 0
+FP32 = 1
+BF16_OUT_FP32 = 2
+STATUS = {
+    0: "WATTN_OK",
+    1: "WATTN_ERR_NULL",
+    2: "WATTN_ERR_SHAPE",
+    3: "WATTN_ERR_SHIFT",
+    4: "WATTN_ERR_HEAD_DIM",
+    5: "WATTN_ERR_RANK",
+    6: "WATTN_ERR_DTYPE",
+    7: "WATTN_ERR_ALIAS",
+    8: "WATTN_ERR_HIP",
+    9: "WATTN_ERR_POINTER",
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class WattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libwattn.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libwattn.so (built in-tree).  Raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m vision_transformer_windowed_window_amd.build` "
+            "(there is no non-HIP fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.wattn_forward.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, ci, ci, vp]
+    lib.wattn_forward.restype = ci
+    lib.wattn_pair_count.argtypes = [ci] * 6
+    lib.wattn_pair_count.restype = ctypes.c_int64
+    lib.wattn_status_string.argtypes = [ci]
+    lib.wattn_status_string.restype = ctypes.c_char_p
+    lib.wattn_abi_version.argtypes = []
+    lib.wattn_abi_version.restype = ci
+    _LIB = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().wattn_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load_library().wattn_status_string(status).decode()
+
+
+def pair_count(B: int, H: int, Hgrid: int, Wgrid: int, M: int, shift: int) -> int:
+    """Number of (query, key) pairs with a finite logit (host arithmetic in the library)."""
+    return int(load_library().wattn_pair_count(B, H, Hgrid, Wgrid, M, shift))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=None, out=None,
+            out_dtype=None, stream=None):
+    """Shifted-window attention of (q, k, v) on the GPU; returns ``out`` ([B, Hg, Wg, H, d]).
+
+    ``out_dtype`` (or the dtype of a given ``out``) may be torch.float32 for bfloat16
+    inputs; by default the output has the input dtype.  The call is asynchronous on
+    ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    lib = load_library()
+    if q.dtype == torch.bfloat16:
+        dtype = BF16
+    elif q.dtype == torch.float32:
+        dtype = FP32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+    if q.dim() != 5:
+        raise ValueError("q must be [B, Hgrid, Wgrid, H, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, Hg, Wg, H, d = q.shape
+    if theta is not None:
+        if theta.dtype != torch.float32 or not theta.is_cuda or not theta.is_contiguous():
+            raise ValueError("theta must be a contiguous float32 device tensor")
+        if tuple(theta.shape) != (H, d // 2):
+            raise ValueError(f"theta must be [H, d/2] = [{H}, {d // 2}]")
+    r = 0
+    if (bias_u is None) != (bias_v is None):
+        raise ValueError("bias_u and bias_v go together")
+    if bias_u is not None:
+        r = bias_u.shape[-1]
+        for name, t in (("bias_u", bias_u), ("bias_v", bias_v)):
+            if tuple(t.shape) != (H, M * M, r) or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [H, M*M, r] device tensor of q's dtype")
+    if out is not None:
+        out_dtype = out.dtype
+    elif out_dtype is None:
+        out_dtype = q.dtype
+    if out_dtype == torch.float32 and dtype == BF16:
+        dtype = BF16_OUT_FP32
+    elif out_dtype != q.dtype:
+        raise TypeError(f"unsupported output dtype {out_dtype} for {q.dtype} inputs")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous device tensor shaped like q")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.wattn_forward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hg, Wg, M, shift, d,
+        _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
+    )
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return out

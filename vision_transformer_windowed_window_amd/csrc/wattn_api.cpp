@@ -1,0 +1,212 @@
+// wattn_api.cpp -- host side of libwattn.so: argument validation, launch planning and
+// dispatch.  Every argument check runs before the first HIP call, so the error paths are
+// testable on a machine without a GPU.
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "wattn.h"
+#include "wattn_plan.h"
+
+hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
+                             const void* k, const void* v, void* out, const float* theta, const void* bu,
+                             const void* bv, hipStream_t stream);
+hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
+                            void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
+
+namespace {
+
+constexpr int kQueryTile = 256;      // queries per workgroup, both paths
+constexpr int64_t kMaxElems = 1LL << 40;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_shape(int B, int H, int Hgrid, int Wgrid, int M, int shift) {
+  if (B <= 0 || H <= 0 || Hgrid <= 0 || Wgrid <= 0 || M <= 0 || M > WATTN_MAX_M) return WATTN_ERR_SHAPE;
+  if (Hgrid % M != 0 || Wgrid % M != 0) return WATTN_ERR_SHAPE;
+  if (Hgrid > 65535 || Wgrid > 65535) return WATTN_ERR_SHAPE;
+  if (shift < 0 || shift >= M) return WATTN_ERR_SHIFT;
+  return WATTN_OK;
+}
+
+struct AxisSplit {
+  // window groups along one axis: [w0, w0+nw) with region rows [r0, r0+rh)
+  int n;
+  int w0[3], nw[3], r0[3], rh[3];
+};
+
+AxisSplit split_axis(int G, int M, int s) {
+  AxisSplit a{};
+  const int nwin = G / M;
+  if (s == 0) {
+    a.n = 1;
+    a.w0[0] = 0; a.nw[0] = nwin; a.r0[0] = 0; a.rh[0] = M;
+    return a;
+  }
+  int n = 0;
+  if (nwin > 1) {
+    a.w0[n] = 0; a.nw[n] = nwin - 1; a.r0[n] = 0; a.rh[n] = M; ++n;
+  }
+  a.w0[n] = nwin - 1; a.nw[n] = 1; a.r0[n] = 0; a.rh[n] = M - s; ++n;   // tokens that stayed
+  a.w0[n] = nwin - 1; a.nw[n] = 1; a.r0[n] = M - s; a.rh[n] = s; ++n;   // tokens that wrapped
+  a.n = n;
+  return a;
+}
+
+// Returns false if the task count would not fit the launch limits.
+bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
+  P = WattnPlan{};
+  P.B = B; P.H = H; P.Hg = Hg; P.Wg = Wg; P.M = M; P.s = s;
+  const AxisSplit ay = split_axis(Hg, M, s), ax = split_axis(Wg, M, s);
+  WattnSeg segs[WATTN_MAX_SEG];
+  int ns = 0;
+  for (int i = 0; i < ay.n; ++i)
+    for (int j = 0; j < ax.n; ++j) {
+      WattnSeg g{};
+      g.wy0 = ay.w0[i]; g.nwy = ay.nw[i]; g.r0 = ay.r0[i]; g.rh = ay.rh[i];
+      g.wx0 = ax.w0[j]; g.nwx = ax.nw[j]; g.c0 = ax.r0[j]; g.rw = ax.rh[j];
+      g.nqt = (g.rh * g.rw + kQueryTile - 1) / kQueryTile;
+      segs[ns++] = g;
+    }
+  std::stable_sort(segs, segs + ns, [](const WattnSeg& a, const WattnSeg& b) { return a.rh * a.rw > b.rh * b.rw; });
+  int64_t begin = 0;
+  for (int i = 0; i < ns; ++i) {
+    segs[i].task_begin = (int)begin;
+    begin += (int64_t)segs[i].nwy * segs[i].nwx * segs[i].nqt * H * B;
+    if (begin > (1LL << 30)) return false;
+    P.seg[i] = segs[i];
+  }
+  P.nseg = ns;
+  P.ntasks = (int)begin;
+  P.chunk = std::max(1, std::min(16, P.seg[0].nqt * H));
+  const int64_t unit = 8LL * P.chunk;
+  P.grid = (int)(((int64_t)P.ntasks + unit - 1) / unit * unit);
+  return true;
+}
+
+int pointer_ok(const void* p, size_t bytes) {
+  if (p == nullptr) return WATTN_OK;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return WATTN_ERR_POINTER;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return WATTN_ERR_POINTER;
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return WATTN_ERR_POINTER;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), a = reinterpret_cast<uintptr_t>(p);
+  if (a < b || a + bytes > b + size) return WATTN_ERR_POINTER;
+  return WATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Hgrid,
+                             int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
+                             const void* bias_v, int r, int dtype, void* stream) {
+  // ---- argument checks (no HIP call before this block ends)
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return WATTN_ERR_NULL;
+  int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
+  if (st != WATTN_OK) return st;
+  if (d != 32) return WATTN_ERR_HEAD_DIM;
+  if (dtype != WATTN_BF16 && dtype != WATTN_FP32 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
+  if (r != 0 && r != 16) return WATTN_ERR_RANK;
+  if (r == 0 && (bias_u != nullptr || bias_v != nullptr)) return WATTN_ERR_RANK;
+  if (r > 0 && (bias_u == nullptr || bias_v == nullptr)) return WATTN_ERR_RANK;
+  const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
+  if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
+  const size_t esz = (dtype == WATTN_FP32) ? 4 : 2;           // q, k, v, bias_u, bias_v
+  const size_t osz = (dtype == WATTN_BF16) ? 2 : 4;           // out
+  const size_t tbytes = (size_t)elems * esz;
+  const size_t obytes = (size_t)elems * osz;
+  const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
+  const size_t b_bytes = (size_t)H * M * M * r * esz;
+  const Range ro{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + obytes};
+  const Range ins[6] = {
+      {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + tbytes},
+      {reinterpret_cast<uintptr_t>(k), reinterpret_cast<uintptr_t>(k) + tbytes},
+      {reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(v) + tbytes},
+      {reinterpret_cast<uintptr_t>(theta), reinterpret_cast<uintptr_t>(theta) + (theta ? th_bytes : 0)},
+      {reinterpret_cast<uintptr_t>(bias_u), reinterpret_cast<uintptr_t>(bias_u) + (bias_u ? b_bytes : 0)},
+      {reinterpret_cast<uintptr_t>(bias_v), reinterpret_cast<uintptr_t>(bias_v) + (bias_v ? b_bytes : 0)},
+  };
+  for (const Range& x : ins)
+    if (x.hi > x.lo && overlaps(ro, x)) return WATTN_ERR_ALIAS;
+
+  WattnPlan plan;
+  WattnF32Plan fplan{};
+  if (dtype != WATTN_FP32) {
+    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan)) return WATTN_ERR_SHAPE;
+  } else {
+    fplan.B = B; fplan.H = H; fplan.Hg = Hgrid; fplan.Wg = Wgrid; fplan.M = M; fplan.s = shift;
+    fplan.nwx = Wgrid / M;
+    fplan.nw = (Hgrid / M) * fplan.nwx;
+    fplan.nqt = (M * M + kQueryTile - 1) / kQueryTile;
+    const int64_t grid = (int64_t)fplan.nqt * H * fplan.nw * B;
+    if (grid > (1LL << 30)) return WATTN_ERR_SHAPE;
+    fplan.grid = (int)grid;
+  }
+
+  // ---- device checks
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  const void* ptrs[7] = {q, k, v, out, theta, bias_u, bias_v};
+  const size_t sizes[7] = {tbytes, tbytes, tbytes, obytes, th_bytes, b_bytes, b_bytes};
+  for (int i = 0; i < 7; ++i) {
+    st = pointer_ok(ptrs[i], sizes[i]);
+    if (st != WATTN_OK) return st;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype != WATTN_FP32)
+    e = wattn_launch_bf16(plan, r > 0 ? 3 : 2, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, theta,
+                          bias_u, bias_v, s);
+  else
+    e = wattn_launch_f32(fplan, r, q, k, v, out, theta, bias_u, bias_v, s);
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+extern "C" int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift) {
+  if (check_shape(B, H, Hgrid, Wgrid, M, shift) != WATTN_OK) return -1;
+  const AxisSplit ay = split_axis(Hgrid, M, shift), ax = split_axis(Wgrid, M, shift);
+  int64_t total = 0;
+  for (int i = 0; i < ay.n; ++i)
+    for (int j = 0; j < ax.n; ++j) {
+      const int64_t ntok = (int64_t)ay.rh[i] * ax.rh[j];
+      total += (int64_t)ay.nw[i] * ax.nw[j] * ntok * ntok;
+    }
+  return total * B * H;
+}
+
+extern "C" const char* wattn_status_string(int status) {
+  switch (status) {
+    case WATTN_OK: return "ok";
+    case WATTN_ERR_NULL: return "null q, k, v or out pointer";
+    case WATTN_ERR_SHAPE: return "invalid or unsupported sizes (B, H, grid, M)";
+    case WATTN_ERR_SHIFT: return "shift outside [0, M)";
+    case WATTN_ERR_HEAD_DIM: return "unsupported head dimension (supported: 32)";
+    case WATTN_ERR_RANK: return "unsupported bias rank or bias pointers inconsistent with r";
+    case WATTN_ERR_DTYPE: return "unknown dtype";
+    case WATTN_ERR_ALIAS: return "out overlaps an input buffer";
+    case WATTN_ERR_HIP: return "HIP runtime error (no device or launch failure)";
+    case WATTN_ERR_POINTER: return "buffer is not device-accessible memory of the required size";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int wattn_abi_version(void) { return WATTN_ABI_VERSION; }

@@ -1,0 +1,38 @@
+// wattn_plan.h -- launch plan shared by the host API and the kernels of libwattn.so.
+//
+// A shifted-window layer splits every window of the last row band and of the last column
+// band into rectangular wrap regions (the tokens that stayed in place and the tokens that
+// wrapped around from the other edge).  Tokens only attend within their region, so the
+// bf16 path treats each region as an independent, unmasked attention problem; the masked
+// pairs are never computed.  Windows that share a region shape form one segment.
+//
+// Task order (innermost first): query tile, head, window of the segment, image, segment.
+// Segments are sorted by region size, largest first, so heavy tasks are dispatched early.
+#pragma once
+
+#include <stdint.h>
+
+#define WATTN_MAX_SEG 9
+
+struct WattnSeg {
+  int wy0, nwy, wx0, nwx;  // windows of the segment: rows [wy0, wy0+nwy), cols [wx0, wx0+nwx)
+  int r0, rh, c0, rw;      // region inside each window, window-local rows / cols
+  int nqt;                 // query tiles per region
+  int task_begin;          // index of the segment's first task
+};
+
+struct WattnPlan {
+  WattnSeg seg[WATTN_MAX_SEG];
+  int nseg;
+  int ntasks;
+  int B, H, Hg, Wg, M, s;
+  int chunk;  // tasks kept together on one XCD (consecutive tasks share K/V in L2)
+  int grid;   // launched workgroups: ntasks rounded up to a multiple of 8 * chunk
+};
+
+// Plain per-window plan of the fp32 path: one workgroup per (query tile, head, window, image).
+struct WattnF32Plan {
+  int B, H, Hg, Wg, M, s;
+  int nwx, nw, nqt;
+  int grid;
+};
