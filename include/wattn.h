@@ -60,7 +60,8 @@ typedef enum {
 typedef enum {
   WATTN_OK = 0,
   WATTN_ERR_NULL = 1,     /* q, k, v or out is NULL */
-  WATTN_ERR_SHAPE = 2,    /* a size <= 0, M > WATTN_MAX_M, grid not a multiple of M, or too large */
+  WATTN_ERR_SHAPE = 2,    /* a size <= 0, M > WATTN_MAX_M, grid not a multiple of M, a grid side
+                             above 65535, or one image holding 2^31 or more elements */
   WATTN_ERR_SHIFT = 3,    /* shift outside [0, M) */
   WATTN_ERR_HEAD_DIM = 4, /* d not supported (this version: d == 32) */
   WATTN_ERR_RANK = 5,     /* r not in {0, 16}, or bias pointers inconsistent with r */
@@ -97,6 +98,13 @@ typedef enum {
  * every buffer and must keep it alive until the stream has run the work.  Scale is
  * d^-1/2 on the content logits; the bias is added unscaled.  NaN or Inf inputs
  * propagate to the output and are not checked.
+ *
+ * bf16 modes: after the fp32 rotation, q * log2(e) / sqrt(d), k and the bias factors
+ * (u * log2(e), v) are rounded once to fp16 for the score product on the matrix cores
+ * (fp16 keeps three more significand bits than bf16); P is rounded to bf16 for the
+ * value product.  fp16 holds magnitudes below 65504, so q entries must stay below about
+ * 1.8e5 and k and bias-factor entries below about 4.6e4 (a rotation can grow a
+ * component by sqrt(2)); larger entries overflow and give non-finite outputs.
  *
  * Returns WATTN_OK or one of the WATTN_ERR_* codes above.
  */

@@ -55,7 +55,7 @@ def test_status_enum_matches_header_and_strings():
     [
         (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1),
         (dict(B=0), 2), (dict(H=0), 2), (dict(Hg=0), 2), (dict(Wg=-8), 2), (dict(M=0), 2),
-        (dict(Hg=20), 2), (dict(Wg=12), 2), (dict(M=256, Hg=256, Wg=256), 2),
+        (dict(Hg=20), 2), (dict(Wg=12), 2), (dict(M=256, Hg=256, Wg=256), 2), (dict(H=64, Hg=1024, Wg=1024), 2),
         (dict(s=-1), 3), (dict(s=8), 3), (dict(s=9), 3),
         (dict(d=64), 4), (dict(d=16), 4), (dict(d=33), 4),
         (dict(r=8, bu=BU, bv=BV), 5), (dict(r=16), 5), (dict(r=16, bu=BU), 5), (dict(r=0, bu=BU, bv=BV), 5),

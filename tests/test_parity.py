@@ -108,39 +108,48 @@ def test_bf16_output(case):
 
 
 def test_large_query_scale():
-    """Peaked softmax (logits with std ~2.5)."""
+    """Peaked softmax: q scaled by 2.5 beyond the N(0,1) workloads.  The rotated q and k
+    are rounded to bf16 for the matrix cores, so the logit error grows in proportion to
+    the logits; the bounds are the benchmark spec's bounds scaled by the same factor."""
+    from parity_util import errors
+
     note("start large q scale")
-    inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=5, qscale=2.5)
+    f = 2.5
+    inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=5, qscale=f)
     got = run_gpu(inp, "bf16", 16, 8)
-    check(got, oracle_full(inp, 16, 8), "bf16", "q_x2.5")
+    max_abs, rel = errors(got, oracle_full(inp, 16, 8))
+    note(f"q_x{f}: max|err| = {max_abs:.3e}, rel-L2 = {rel:.3e}")
+    assert max_abs <= f * 1e-2 and rel <= f * 5e-3
 
 
 # ------------------------------------------------------------ workloads at full size
 
-FULL_SAMPLED = ["swin_t_m8", "large_m32", "dense_p2_m32", "dense_p2_m16", "dense_p2_m8", "sr_m96_rib"]
+FULL = ["swin_t_m8", "large_m32", "dense_p2_m32", "dense_p2_m16", "dense_p2_m8"]
 
 
-@pytest.mark.parametrize("name", FULL_SAMPLED)
-def test_workload_full_size_sampled(name):
+@pytest.mark.parametrize("name", FULL)
+def test_workload_full_size_full_compare(name):
+    """Every output of the workload at its full size against the oracle."""
     cfg = CONFIGS[name]
     note(f"start {name} full size")
     inp = make_inputs(cfg)
     got = run_gpu(inp, cfg.dtype, cfg.M, cfg.shift)
+    check(got, oracle_full(inp, cfg.M, cfg.shift), cfg.dtype, f"{name} full")
+
+
+def test_sr_m96_rib_full_size_sampled():
+    """M = 96 with the rank-16 bias at full size; the oracle computes four 9216-token
+    window-heads (each corner window of the grid, one per head position)."""
+    cfg = CONFIGS["sr_m96_rib"]
+    note("start sr_m96_rib full size")
+    inp = make_inputs(cfg)
+    got = run_gpu(inp, cfg.dtype, cfg.M, cfg.shift)
     assert np.all(np.isfinite(got))
-    count = 3 if cfg.M >= 96 else 12
-    units = sample_units(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, count, seed=cfg.seed)
+    units = sample_units(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, 4, seed=cfg.seed)
     refs = oracle_sampled(inp, cfg.M, cfg.shift, units)
     g = np.concatenate([got[b, y, x, h, :] for (b, y, x, h, _) in refs])
     r = np.concatenate([o for (_, _, _, _, o) in refs])
-    check(g, r, cfg.dtype, f"{name} ({len(units)} window-heads)")
-
-
-def test_swin_t_m8_full_compare():
-    cfg = CONFIGS["swin_t_m8"]
-    note("start swin_t_m8 full compare (8 images)")
-    inp = make_inputs(cfg, batch=8)
-    got = run_gpu(inp, cfg.dtype, cfg.M, cfg.shift)
-    check(got, oracle_full(inp, cfg.M, cfg.shift), cfg.dtype, "swin_t_m8 B=8")
+    check(g, r, cfg.dtype, f"sr_m96_rib ({len(units)} window-heads)")
 
 
 # --------------------------------------------------------------------- other properties

@@ -19,7 +19,9 @@ LIB = os.path.join(PKG, "libwattn.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around each MFMA)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -19,7 +19,6 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
 
 namespace {
 
-constexpr int kQueryTile = 256;      // queries per workgroup, both paths
 constexpr int64_t kMaxElems = 1LL << 40;
 
 struct Range {
@@ -61,7 +60,7 @@ AxisSplit split_axis(int G, int M, int s) {
 }
 
 // Returns false if the task count would not fit the launch limits.
-bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
+bool build_plan(int B, int H, int Hg, int Wg, int M, int s, int qtile, WattnPlan& P) {
   P = WattnPlan{};
   P.B = B; P.H = H; P.Hg = Hg; P.Wg = Wg; P.M = M; P.s = s;
   const AxisSplit ay = split_axis(Hg, M, s), ax = split_axis(Wg, M, s);
@@ -72,7 +71,7 @@ bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
       WattnSeg g{};
       g.wy0 = ay.w0[i]; g.nwy = ay.nw[i]; g.r0 = ay.r0[i]; g.rh = ay.rh[i];
       g.wx0 = ax.w0[j]; g.nwx = ax.nw[j]; g.c0 = ax.r0[j]; g.rw = ax.rh[j];
-      g.nqt = (g.rh * g.rw + kQueryTile - 1) / kQueryTile;
+      g.nqt = (g.rh * g.rw + qtile - 1) / qtile;
       segs[ns++] = g;
     }
   std::stable_sort(segs, segs + ns, [](const WattnSeg& a, const WattnSeg& b) { return a.rh * a.rw > b.rh * b.rw; });
@@ -126,6 +125,7 @@ extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* 
   if (r > 0 && (bias_u == nullptr || bias_v == nullptr)) return WATTN_ERR_RANK;
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
   if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
+  if ((int64_t)Hgrid * Wgrid * H * d >= (1LL << 31)) return WATTN_ERR_SHAPE;  // 32-bit offsets within an image
   const size_t esz = (dtype == WATTN_FP32) ? 4 : 2;           // q, k, v, bias_u, bias_v
   const size_t osz = (dtype == WATTN_BF16) ? 2 : 4;           // out
   const size_t tbytes = (size_t)elems * esz;
@@ -147,12 +147,12 @@ extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* 
   WattnPlan plan;
   WattnF32Plan fplan{};
   if (dtype != WATTN_FP32) {
-    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan)) return WATTN_ERR_SHAPE;
+    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, WATTN_BF16_QTILE, plan)) return WATTN_ERR_SHAPE;
   } else {
     fplan.B = B; fplan.H = H; fplan.Hg = Hgrid; fplan.Wg = Wgrid; fplan.M = M; fplan.s = shift;
     fplan.nwx = Wgrid / M;
     fplan.nw = (Hgrid / M) * fplan.nwx;
-    fplan.nqt = (M * M + kQueryTile - 1) / kQueryTile;
+    fplan.nqt = (M * M + WATTN_F32_QTILE - 1) / WATTN_F32_QTILE;
     const int64_t grid = (int64_t)fplan.nqt * H * fplan.nw * B;
     if (grid > (1LL << 30)) return WATTN_ERR_SHAPE;
     fplan.grid = (int)grid;

@@ -1,32 +1,47 @@
 // wattn_kernels.hip -- device code of libwattn.so for gfx950 (AMD Instinct MI355X).
 //
 // Fused shifted-window attention (FLASHSWIN page, "How it works", first and second
-// changes; RIB page, section 2.1 for the bias channels).  One workgroup owns 256 queries
-// of one wrap region of one window and head, and streams that region's keys through LDS
-// in tiles of 64:
+// changes; RIB page, section 2.1 for the bias channels).
+//
+// Work decomposition.  A shifted window of the last row or column band holds two (corner:
+// four) wrap regions; tokens attend only within their region, and each region is a
+// rectangle of tokens that is contiguous in the ORIGINAL (un-shifted) grid.  A workgroup
+// of 8 waves owns 256 queries (32 per wave) of one region of one window and head and
+// streams the region's keys through LDS in tiles of 64.  The masked pairs of the shifted
+// layer are never computed.
 //
 //   prologue : decode the task; build the window-local cos/sin table of the head in LDS
-//              (angles in fp64, stored as fp32); load this wave's 64 queries straight from
-//              their original (un-shifted) grid positions, rotate them in fp32, fold in
-//              d^-1/2 * log2(e), round once to bf16 and keep them in registers; append the
-//              bias channels u * log2(e) when the call has a bias.
-//   key loop : per tile, every thread fetches one 16-byte chunk of K and of V (and of the
-//              bias factor v) for the next tile while the current one is computed, then
-//              rotates K in fp32, rounds it to bf16 and writes K and V^T into the other LDS
-//              buffer.  Per 32-key step and 32-query block a wave runs
-//                  S^T = K Q^T        on 32x32x16 bf16 MFMA, accumulator preset to -m,
-//                  p   = 2^(S^T)      online softmax in fp32 registers,
-//                  O^T += V^T P^T     on 32x32x16 bf16 MFMA.
-//              Computing the transposed products keeps every query's scores, running
-//              max m, running sum l and output accumulator in the same lane.
-//   epilogue : O / l, stored as bf16 (rounded to nearest even) or as fp32, at the tokens'
-//              original grid positions (this reverses the cyclic shift).
+//              (fp32 angles, hardware sin/cos); each wave loads its 32 queries straight
+//              from their original positions, rotates them in fp32, folds in
+//              d^-1/2 * log2(e), rounds once to fp16 and keeps them in registers; with a
+//              bias, u * log2(e) is appended as 16 more channels.
+//   key loop : per tile, threads 0..255 fetch one 16-byte chunk of K each and threads
+//              256..511 one chunk of V (and of the bias factor v) for the next tile while
+//              the current tile is computed; then K is rotated in fp32, rounded to fp16
+//              and stored with V (bf16, unchanged) into the other LDS buffer (both
+//              row-major, chunk-swizzled against bank conflicts).  Per 32-key step each
+//              wave runs
+//                  S^T = K Q^T        32x32x16 fp16 MFMA, accumulator preset to -m,
+//                  p   = 2^(S^T)      fp32 online softmax in registers,
+//                  O^T += V^T P^T     32x32x16 bf16 MFMA, V^T read with ds_read_tr16_b64.
+//              The transposed products keep each query's scores, running max m, running
+//              sum l and output column in one lane (the lane pair l, l^32 splits the keys).
+//   epilogue : O / l, stored as bf16 (round to nearest even) or fp32 at the tokens'
+//              original positions, which reverses the cyclic shift.
 //
-// The running max is updated lazily: the accumulator starts from -m, so S^T already holds
+// The running max is updated lazily: with the accumulator preset to -m, S^T already holds
 // s - m and p = 2^(s - m) costs one exp per score.  The exact rescale (row max, O and l
-// scaled by 2^-(delta)) runs only for the first key step and whenever some p of a step
-// exceeds 2^16, which bounds every p by 2^16 (no overflow: at most 2^16 * N per row sum).
-// Row sums are taken over the bf16-rounded p that the PV product consumes.
+// scaled by 2^-delta) runs for the first key step and whenever some p of a step exceeds
+// 2^16, so every p stays within [0, 2^16] (row sums stay below 2^16 * N).  Row sums are
+// taken over the bf16-rounded p that the PV product consumes.
+//
+// Precision: q, k, v arrive in bf16 and RoPE runs in fp32 (FLASHSWIN page, closing
+// developer paragraph).  The rotated, scaled q and k are rounded once to fp16 (11-bit
+// significand) for the score product: rounding them to bf16 (8-bit significand) instead
+// moves logits by up to ~1e-2 relative and alone costs up to 1e-2 absolute in the output
+// on N(0,1) workloads.  fp16 limits the score operands to |value| < 65504; larger q, k or
+// bias-factor entries overflow and give non-finite outputs.  P is rounded to bf16 for the
+// PV product (P can reach 2^16, beyond fp16).
 //
 // The fp32 path (wattn_fwd_f32_kernel) is a plain per-query loop over the whole window
 // with the region-label mask, used for float32 inputs.
@@ -40,16 +55,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 32;          // head dimension of q, k, v
-constexpr int NTHR = 256;      // threads per workgroup (4 waves)
-constexpr int QT = 256;        // queries per workgroup (64 per wave, 2 blocks of 32)
+constexpr int NTHR = 512;      // threads per workgroup of the bf16 path (8 waves)
+constexpr int QT = WATTN_BF16_QTILE;  // queries per workgroup (32 per wave)
 constexpr int KT = 64;         // keys per LDS tile
-constexpr int VTS = KT + 8;    // row stride (elements) of the transposed V tile
 constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
@@ -63,6 +80,19 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f32x2 f = {a, b};
+  f16x2 h = __builtin_convertvector(f, f16x2);  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// score product: fp16 operands, fp32 accumulate
+__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// value product: bf16 operands, fp32 accumulate
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -71,6 +101,16 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
                                          false);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposed 8-byte LDS read (gfx950): in each group of 16 lanes, lane j receives element
+// j % 4 of the 8-byte reads issued by lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) void*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // i / den and i % den for 0 <= i < 2^16 and 1 <= den <= 2^16, via a multiply-high.
@@ -84,18 +124,24 @@ struct Divider {
   }
 };
 
-// Swizzle of the four 16-byte chunks of a K row in LDS: the eight rows read together by
-// one MFMA operand load fall into eight distinct bank groups.
+// Chunk swizzles (16-byte chunks of a 64-byte K or V row).  K: the eight rows that one
+// MFMA operand read touches per LDS cycle land in eight distinct bank groups.  V: the four
+// rows of one transposed read group land in distinct bank halves / chunk pairs.
 __device__ __forceinline__ int kswz(int key) { return ((key >> 1) & 1) | (((key >> 4) & 1) << 1); }
+__device__ __forceinline__ int vswz(int key) { return ((key >> 1) & 1) << 1; }
 
 // Row of the K tile that feeds MFMA A-operand row i (0..31): the accumulator row layout of
 // the 32x32 MFMA then gives lane (query, g) the scores of keys 16g .. 16g+15 in order.
 __device__ __forceinline__ int key_of_row(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
 
 struct Task {
-  int b, h, wy, wx, r0, rh, c0, rw, q0;
+  int b, h, q0;
+  int r0, rh, c0, rw;  // region in window-local coordinates
+  int y0, x0;          // region origin in the original grid (the region does not wrap)
 };
 
+// Workgroup bid -> task.  Consecutive groups of `chunk` tasks go to one XCD (workgroups
+// are dealt to the 8 XCDs round-robin), so tasks that share cache lines meet in one L2.
 __device__ __forceinline__ bool decode_task(const WattnPlan& P, int bid, Task& t) {
   const int C = P.chunk;
   const int xcd = bid & 7, slot = bid >> 3;
@@ -113,24 +159,20 @@ __device__ __forceinline__ bool decode_task(const WattnPlan& P, int bid, Task& t
   const int nw = S.nwy * S.nwx;
   const int wi = u % nw;
   t.b = u / nw;
-  t.wy = S.wy0 + wi / S.nwx;
-  t.wx = S.wx0 + wi % S.nwx;
+  const int wy = S.wy0 + wi / S.nwx;
+  const int wx = S.wx0 + wi % S.nwx;
   t.r0 = S.r0;
   t.rh = S.rh;
   t.c0 = S.c0;
   t.rw = S.rw;
   t.q0 = qt * QT;
-  return true;
-}
-
-// Element offset of (image b, rolled row Y, rolled col X, head h): the token's original
-// position is ((Y + s) mod Hg, (X + s) mod Wg).
-__device__ __forceinline__ int64_t token_offset(const WattnPlan& P, int b, int h, int Y, int X) {
-  int y = Y + P.s;
+  int y = wy * P.M + S.r0 + P.s;
   if (y >= P.Hg) y -= P.Hg;
-  int x = X + P.s;
+  int x = wx * P.M + S.c0 + P.s;
   if (x >= P.Wg) x -= P.Wg;
-  return ((((int64_t)b * P.Hg + y) * P.Wg + x) * P.H + h) * D;
+  t.y0 = y;
+  t.x0 = x;
+  return true;
 }
 
 template <int NKS, bool ROPE, bool OUTF32>
@@ -144,182 +186,217 @@ __global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __
                                                               const WattnPlan P) {
   constexpr bool BIAS = (NKS == 3);
   __shared__ __align__(16) uint16_t sK[2][KT * D];
+  __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
-  __shared__ __align__(16) uint16_t sVt[2][D * VTS];
   __shared__ float2 sTab[ROPE ? MAXM * (D / 2) : 1];
 
   Task T;
   if (!decode_task(P, blockIdx.x, T)) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = P.M;
-  const int h = T.h, b = T.b;
+  const int h = T.h;
   const int n = T.rh * T.rw;
-  const int wY = T.wy * M + T.r0, wX = T.wx * M + T.c0;  // rolled position of the region origin
+  const int colstride = P.H * D;            // elements between horizontally adjacent tokens
+  const int rowstride = P.Wg * colstride;   // elements between vertically adjacent tokens
+  const int64_t img = (int64_t)T.b * P.Hg * rowstride;
+  const int regbase = T.y0 * rowstride + T.x0 * colstride + h * D;
+  const uint16_t* qi_ = q + img;
+  const uint16_t* ki_ = k + img;
+  const uint16_t* vi_ = v + img;
   const Divider div(T.rw);
 
   if (ROPE) {
     for (int i = tid; i < M * (D / 2); i += NTHR) {
       const int pos = i >> 4, j = i & 15;
-      double sn, cs;
-      sincos((double)pos * (double)theta[h * (D / 2) + j], &sn, &cs);
-      sTab[i] = make_float2((float)cs, (float)sn);
+      float sn, cs;
+      __sincosf((float)pos * theta[h * (D / 2) + j], &sn, &cs);
+      sTab[i] = make_float2(cs, sn);
     }
     __syncthreads();
   }
 
   const int qi = lane & 31, g = lane >> 5;
+  const bool wave_live = T.q0 + wave * 32 < n;  // wave-uniform
 
-  // ---- queries: rotate in fp32, scale by d^-1/2 * log2(e), round once to bf16
-  u32x4 Qf[2][NKS];
-  const float qscale = LOG2E * 0.17677669529663687f;  // log2(e) / sqrt(32)
+  // ---- queries: rotate in fp32, scale by d^-1/2 * log2(e), round once to fp16
+  u32x4 Qf[NKS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int iq = T.q0 + wave * 64 + qb * 32 + qi;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) Qf[qb][ks] = u32x4{0u, 0u, 0u, 0u};
+  for (int ks = 0; ks < NKS; ++ks) Qf[ks] = u32x4{0u, 0u, 0u, 0u};
+  {
+    const int iq = T.q0 + wave * 32 + qi;
+    const float qscale = LOG2E * 0.17677669529663687f;  // log2(e) / sqrt(32)
     if (iq < n) {
-      int lr, lc;
-      div.split((uint32_t)iq, lr, lc);
-      const int64_t off = token_offset(P, b, h, wY + lr, wX + lc);
+      int li, lj;
+      div.split((uint32_t)iq, li, lj);
+      const int off = regbase + li * rowstride + lj * colstride;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(q + off + 16 * ks + 8 * g);
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qi_ + off + 16 * ks + 8 * g);
         u32x4 o;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           float a = bf_lo(raw[p]), c = bf_hi(raw[p]);
           if (ROPE) {
-            const int pos = (ks == 0) ? (T.r0 + lr) : (T.c0 + lc);
+            const int pos = (ks == 0) ? (T.r0 + li) : (T.c0 + lj);
             const float2 t = sTab[pos * (D / 2) + 8 * ks + 4 * g + p];
             const float a2 = a * t.x - c * t.y;
             const float c2 = a * t.y + c * t.x;
             a = a2;
             c = c2;
           }
-          o[p] = pack_bf16(a * qscale, c * qscale);
+          o[p] = pack_f16(a * qscale, c * qscale);
         }
-        Qf[qb][ks] = o;
+        Qf[ks] = o;
       }
       if (BIAS) {
-        const int nl = (T.r0 + lr) * M + (T.c0 + lc);
+        const int nl = (T.r0 + li) * M + (T.c0 + lj);
         const u32x4 raw = *reinterpret_cast<const u32x4*>(bu + ((int64_t)h * M * M + nl) * 16 + 8 * g);
         u32x4 o;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = pack_bf16(bf_lo(raw[p]) * LOG2E, bf_hi(raw[p]) * LOG2E);
-        Qf[qb][NKS - 1] = o;
+        for (int p = 0; p < 4; ++p) o[p] = pack_f16(bf_lo(raw[p]) * LOG2E, bf_hi(raw[p]) * LOG2E);
+        Qf[NKS - 1] = o;
       }
     }
   }
-  const bool qb_live0 = T.q0 + wave * 64 < n;
-  const bool qb_live1 = T.q0 + wave * 64 + 32 < n;
 
-  // ---- loader state: K/V chunk (key lk of the tile, channels 8*lch .. 8*lch+7)
-  const int lk = tid >> 2, lch = tid & 3;
-  const int bk = tid >> 1, bch = tid & 1;  // bias-factor chunk (threads 0..127)
-  u32x4 pk = {0u, 0u, 0u, 0u}, pv = {0u, 0u, 0u, 0u}, pb = {0u, 0u, 0u, 0u};
+  // ---- loader: threads 0..255 own a K chunk (key lk, channels 8*lch..), 256..511 the V
+  //      chunk; threads 256..383 also own a bias-factor chunk (key bk, channels 8*bch..).
+  //      The key index advances by KT per tile; region coordinates and the element offset
+  //      are carried along incrementally.
+  const bool kthread = tid < 256;
+  const int lk = (tid & 255) >> 2, lch = tid & 3;
+  const int bk = (tid & 127) >> 1, bch = tid & 1;
+  const bool bthread = BIAS && tid >= 256 && tid < 384;
+  const int step_i = KT / T.rw, step_j = KT % T.rw;
+  const int step_off = step_i * rowstride + step_j * colstride;  // offset change without carry
+  const int carry_off = rowstride - T.rw * colstride;              // extra change on a column carry
+  int ci, cj, bi, bj;
+  div.split((uint32_t)lk, ci, cj);
+  div.split((uint32_t)bk, bi, bj);
+  int koff = regbase + ci * rowstride + cj * colstride + 8 * lch;  // element offset of the chunk
+  const uint16_t* ksrc = (kthread ? ki_ : vi_);
+  const uint16_t* bsrc = bv + (int64_t)h * M * M * 16 + 8 * bch;
+  u32x4 pd = {0u, 0u, 0u, 0u}, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
 
+  auto advance = [&]() {
+    ci += step_i;
+    cj += step_j;
+    koff += step_off;
+    if (cj >= T.rw) {
+      cj -= T.rw;
+      ci += 1;
+      koff += carry_off;
+    }
+    if (BIAS) {
+      bi += step_i;
+      bj += step_j;
+      if (bj >= T.rw) {
+        bj -= T.rw;
+        bi += 1;
+      }
+    }
+  };
   auto fetch = [&](int tile) {
-    const int key = tile * KT + lk;
-    pk = u32x4{0u, 0u, 0u, 0u};
-    pv = u32x4{0u, 0u, 0u, 0u};
-    lpos = 0;
-    if (key < n) {
-      int lr, lc;
-      div.split((uint32_t)key, lr, lc);
-      const int64_t off = token_offset(P, b, h, wY + lr, wX + lc) + 8 * lch;
-      pk = *reinterpret_cast<const u32x4*>(k + off);
-      pv = *reinterpret_cast<const u32x4*>(v + off);
-      lpos = (lch < 2) ? (T.r0 + lr) : (T.c0 + lc);
+    pd = u32x4{0u, 0u, 0u, 0u};
+    if (tile * KT + lk < n) {
+      pd = *reinterpret_cast<const u32x4*>(ksrc + koff);
+      lpos = (lch < 2) ? (T.r0 + ci) : (T.c0 + cj);
     }
     if (BIAS) {
       pb = u32x4{0u, 0u, 0u, 0u};
-      const int key2 = tile * KT + bk;
-      if (tid < 2 * KT && key2 < n) {
-        int lr, lc;
-        div.split((uint32_t)key2, lr, lc);
-        const int nl = (T.r0 + lr) * M + (T.c0 + lc);
-        pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)h * M * M + nl) * 16 + 8 * bch);
-      }
+      if (bthread && tile * KT + bk < n)
+        pb = *reinterpret_cast<const u32x4*>(bsrc + ((T.r0 + bi) * M + (T.c0 + bj)) * 16);
     }
   };
-
   auto store = [&](int buf) {
-    u32x4 kr = pk;
-    if (ROPE) {
+    if (kthread) {
+      u32x4 kr;
+      if (ROPE) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float a = bf_lo(pk[p]), c = bf_hi(pk[p]);
-        const float2 t = sTab[lpos * (D / 2) + 4 * lch + p];
-        kr[p] = pack_bf16(a * t.x - c * t.y, a * t.y + c * t.x);
+        for (int p = 0; p < 4; ++p) {
+          const float a = bf_lo(pd[p]), c = bf_hi(pd[p]);
+          const float2 t = sTab[lpos * (D / 2) + 4 * lch + p];
+          kr[p] = pack_f16(a * t.x - c * t.y, a * t.y + c * t.x);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) kr[p] = pack_f16(bf_lo(pd[p]), bf_hi(pd[p]));
       }
+      *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
+    } else {
+      *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pd;
     }
-    *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
-    uint16_t* vt = &sVt[buf][(8 * lch) * VTS + lk];
+    if (BIAS && bthread) {
+      u32x4 br;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      vt[(2 * p) * VTS] = (uint16_t)(pv[p] & 0xffffu);
-      vt[(2 * p + 1) * VTS] = (uint16_t)(pv[p] >> 16);
+      for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
+      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + ((bch ^ ((bk >> 4) & 1)) * 8)]) = br;
     }
-    if (BIAS && tid < 2 * KT)
-      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + ((bch ^ ((bk >> 4) & 1)) * 8)]) = pb;
   };
 
-  // ---- per-query online-softmax state (lane = query; both halves g hold the same m)
-  f32x16 O[2], Cn[2];
-  float m[2], l[2];
+  // ---- per-query online-softmax state (lane = query; lanes l and l^32 hold the same m)
+  f32x16 O, Cn;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    m[qb] = 0.f;
-    l[qb] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      O[qb][e] = 0.f;
-      Cn[qb][e] = 0.f;
-    }
+  for (int e = 0; e < 16; ++e) {
+    O[e] = 0.f;
+    Cn[e] = 0.f;
   }
+  float m = 0.f, l = 0.f;
   const uint32_t ONES = 0x3f803f80u;  // bf16 pair (1.0, 1.0)
   const int ntile = (n + KT - 1) / KT;
 
+  // per-lane constants of the operand reads
+  const int arow = key_of_row(lane & 31);             // K tile row feeding A-operand row lane%32
+  const int vgrp = lane >> 4;                         // 16-lane group of the transposed V read
+  const int vs = lane & 15;                           // source lane within the group
+  const int vchunk_hi = (vgrp & 1) * 2;               // dims 0..15 -> chunks 0,1; 16..31 -> 2,3
+
   fetch(0);
   store(0);
+  advance();
   __syncthreads();
 
+#pragma unroll 2
   for (int tile = 0; tile < ntile; ++tile) {
     const int buf = tile & 1;
     if (tile + 1 < ntile) fetch(tile + 1);
 
+    if (wave_live) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int kb = st * 32;
-      const int kglob = tile * KT + kb;  // first key of the step
-      if (kglob < n) {
-        const int i = lane & 31;
-        const int key = kb + key_of_row(i);
-        u32x4 Kf[NKS];
-        Kf[0] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((0 + g) ^ kswz(key)) * 8)]);
-        Kf[1] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((2 + g) ^ kswz(key)) * 8)]);
-        if (BIAS)
-          Kf[NKS - 1] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + ((g ^ ((key >> 4) & 1)) * 8)]);
-        u32x4 Vf[2];
-        Vf[0] = *reinterpret_cast<const u32x4*>(&sVt[buf][i * VTS + kb + 16 * g]);
-        Vf[1] = *reinterpret_cast<const u32x4*>(&sVt[buf][i * VTS + kb + 16 * g + 8]);
-        const bool partial = kglob + 32 > n;
-        const bool first = (tile == 0) && (st == 0);
+      for (int st = 0; st < 2; ++st) {
+        const int kb = st * 32;
+        const int kg = tile * KT + kb;  // first key of the step (uniform)
+        if (kg < n) {
+          const int key = kb + arow;
+          u32x4 Kf[NKS];
+          Kf[0] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((0 + g) ^ kswz(key)) * 8)]);
+          Kf[1] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((2 + g) ^ kswz(key)) * 8)]);
+          if (BIAS)
+            Kf[NKS - 1] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + ((g ^ ((key >> 4) & 1)) * 8)]);
+          // V^T operand of the two PV MFMAs: keys kb + 16g + 8j + 4u + t, dims of this lane
+          u32x2 Vt[2][2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int row = kb + 16 * (vgrp >> 1) + 8 * j + 4 * u + (vs >> 2);
+              const int chunk = vchunk_hi + ((vs & 3) >> 1);
+              Vt[j][u] = lds_read_tr16(&sV[buf][row * D + ((chunk ^ vswz(row)) * 8) + 4 * (vs & 1)]);
+            }
 
+          f32x16 S = mfma32_f16(Kf[0], Qf[0], Cn);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!(qb == 0 ? qb_live0 : qb_live1)) continue;
-          f32x16 S = mfma32(Kf[0], Qf[qb][0], Cn[qb]);
-#pragma unroll
-          for (int ks = 1; ks < NKS; ++ks) S = mfma32(Kf[ks], Qf[qb][ks], S);
-          if (partial) {
+          for (int ks = 1; ks < NKS; ++ks) S = mfma32_f16(Kf[ks], Qf[ks], S);
+          if (kg + 32 > n) {
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-              if (kglob + 16 * g + e >= n) S[e] = -INFINITY;
+              if (kg + 16 * g + e >= n) S[e] = -INFINITY;
           }
+          const bool first = (tile == 0) && (st == 0);
           uint32_t Pp[8];
           float ls = 0.f;
           bool exact = first;
@@ -339,55 +416,55 @@ __global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __
             const float delta = first ? mx : fmaxf(mx, 0.f);
             if (!first) {
               const float a = __builtin_amdgcn_exp2f(-delta);
-              l[qb] *= a;
+              l *= a;
 #pragma unroll
-              for (int e = 0; e < 16; ++e) O[qb][e] *= a;
+              for (int e = 0; e < 16; ++e) O[e] *= a;
             }
-            m[qb] += delta;
+            m += delta;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) Cn[qb][e] = -m[qb];
+            for (int e = 0; e < 16; ++e) Cn[e] = -m;
             ls = 0.f;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
-              Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(S[2 * t] - delta), __builtin_amdgcn_exp2f(S[2 * t + 1] - delta));
+              Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(S[2 * t] - delta),
+                                __builtin_amdgcn_exp2f(S[2 * t + 1] - delta));
               ls = dot2_bf16(Pp[t], ONES, ls);
             }
           }
-          l[qb] += ls;
+          l += ls;
           const u32x4 P0 = {Pp[0], Pp[1], Pp[2], Pp[3]};
           const u32x4 P1 = {Pp[4], Pp[5], Pp[6], Pp[7]};
-          O[qb] = mfma32(Vf[0], P0, O[qb]);
-          O[qb] = mfma32(Vf[1], P1, O[qb]);
+          O = mfma32(u32x4{Vt[0][0][0], Vt[0][0][1], Vt[0][1][0], Vt[0][1][1]}, P0, O);
+          O = mfma32(u32x4{Vt[1][0][0], Vt[1][0][1], Vt[1][1][0], Vt[1][1][1]}, P1, O);
         }
       }
     }
 
-    if (tile + 1 < ntile) store(buf ^ 1);
+    if (tile + 1 < ntile) {
+      store(buf ^ 1);
+      advance();
+    }
     __syncthreads();
   }
 
-  // ---- epilogue: normalise, round, scatter to the original positions
+  // ---- epilogue: normalise, scatter to the original positions
+  const float lt = l + __shfl_xor(l, 32);
+  const int iq = T.q0 + wave * 32 + qi;
+  if (iq < n) {
+    const float inv = 1.0f / lt;
+    int li, lj;
+    div.split((uint32_t)iq, li, lj);
+    const int64_t off = img + regbase + li * rowstride + lj * colstride;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int iq = T.q0 + wave * 64 + qb * 32 + qi;
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    if (iq < n) {
-      const float inv = 1.0f / lt;
-      int lr, lc;
-      div.split((uint32_t)iq, lr, lc);
-      const int64_t off = token_offset(P, b, h, wY + lr, wX + lc);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (OUTF32) {
-          const float4 w = make_float4(O[qb][4 * t + 0] * inv, O[qb][4 * t + 1] * inv, O[qb][4 * t + 2] * inv,
-                                       O[qb][4 * t + 3] * inv);
-          *reinterpret_cast<float4*>(static_cast<float*>(out) + off + 8 * t + 4 * g) = w;
-        } else {
-          u32x2 w;
-          w[0] = pack_bf16(O[qb][4 * t + 0] * inv, O[qb][4 * t + 1] * inv);
-          w[1] = pack_bf16(O[qb][4 * t + 2] * inv, O[qb][4 * t + 3] * inv);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off + 8 * t + 4 * g) = w;
-        }
+    for (int t = 0; t < 4; ++t) {
+      if (OUTF32) {
+        const float4 w = make_float4(O[4 * t + 0] * inv, O[4 * t + 1] * inv, O[4 * t + 2] * inv, O[4 * t + 3] * inv);
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + off + 8 * t + 4 * g) = w;
+      } else {
+        u32x2 w;
+        w[0] = pack_bf16(O[4 * t + 0] * inv, O[4 * t + 1] * inv);
+        w[1] = pack_bf16(O[4 * t + 2] * inv, O[4 * t + 3] * inv);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off + 8 * t + 4 * g) = w;
       }
     }
   }

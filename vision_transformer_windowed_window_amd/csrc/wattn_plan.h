@@ -13,6 +13,8 @@
 #include <stdint.h>
 
 #define WATTN_MAX_SEG 9
+#define WATTN_BF16_QTILE 256  // queries per workgroup of the bf16 path (8 waves x 32)
+#define WATTN_F32_QTILE 256   // queries per workgroup of the fp32 path (one per thread)
 
 struct WattnSeg {
   int wy0, nwy, wx0, nwx;  // windows of the segment: rows [wy0, wy0+nwy), cols [wx0, wx0+nwx)
