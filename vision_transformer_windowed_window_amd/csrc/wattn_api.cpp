@@ -84,7 +84,7 @@ bool build_plan(int B, int H, int Hg, int Wg, int M, int s, int qtile, WattnPlan
   }
   P.nseg = ns;
   P.ntasks = (int)begin;
-  P.chunk = std::max(1, std::min(16, P.seg[0].nqt * H));
+  P.chunk = P.ntasks >= 128 ? 16 : std::max(1, (P.ntasks + 7) / 8);
   const int64_t unit = 8LL * P.chunk;
   P.grid = (int)(((int64_t)P.ntasks + unit - 1) / unit * unit);
   return true;

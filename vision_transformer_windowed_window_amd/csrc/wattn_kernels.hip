@@ -6,28 +6,35 @@
 // Work decomposition.  A shifted window of the last row or column band holds two (corner:
 // four) wrap regions; tokens attend only within their region, and each region is a
 // rectangle of tokens that is contiguous in the ORIGINAL (un-shifted) grid.  A workgroup
-// of 8 waves owns 256 queries (32 per wave) of one region of one window and head and
-// streams the region's keys through LDS in tiles of 64.  The masked pairs of the shifted
-// layer are never computed.
+// of 8 waves owns 256 queries (32 per wave, two blocks of 16) of one region of one window
+// and head and streams the region's keys through LDS in tiles of 128.  The masked pairs of
+// the shifted layer are never computed.
 //
-//   prologue : decode the task; build the window-local cos/sin table of the head in LDS
-//              (fp32 angles, hardware sin/cos); each wave loads its 32 queries straight
-//              from their original positions, rotates them in fp32, folds in
-//              d^-1/2 * log2(e), rounds once to fp16 and keeps them in registers; with a
-//              bias, u * log2(e) is appended as 16 more channels.
-//   key loop : per tile, threads 0..255 fetch one 16-byte chunk of K each and threads
-//              256..511 one chunk of V (and of the bias factor v) for the next tile while
-//              the current tile is computed; then K is rotated in fp32, rounded to fp16
-//              and stored with V (bf16, unchanged) into the other LDS buffer (both
-//              row-major, chunk-swizzled against bank conflicts).  Per 32-key step each
-//              wave runs
-//                  S^T = K Q^T        32x32x16 fp16 MFMA, accumulator preset to -m,
+//   prologue : decode the task; issue the global loads of the head's angles, the wave's
+//              queries and the first K/V tile together; build the window-local cos/sin
+//              table in LDS (fp32 angles, hardware sin/cos); rotate the queries in fp32,
+//              fold in d^-1/2 * log2(e), round once to fp16 and keep them in registers;
+//              with a bias, u * log2(e) forms a second (zero-padded) k = 32 operand.
+//   key loop : per tile, every thread fetches one 16-byte chunk of K and the matching
+//              chunk of V (threads 0..255 also one of the bias factor v) for the next tile
+//              while the current tile is computed; then K is rotated in fp32, rounded to
+//              fp16 and stored with V (bf16, unchanged) into the other LDS buffer (both
+//              row-major, chunk-swizzled against bank conflicts).  Per 32-key step and
+//              16-query block each wave runs
+//                  S^T = K Q^T        16x16x32 fp16 MFMA (k = d = 32), accumulator preset
+//                                     to -m, one product per 16 keys,
 //                  p   = 2^(S^T)      fp32 online softmax in registers,
-//                  O^T += V^T P^T     32x32x16 bf16 MFMA, V^T read with ds_read_tr16_b64.
+//                  O^T += V^T P^T     16x16x32 bf16 MFMA per 16 dims, V^T read with
+//                                     ds_read_b64_tr_b16.
 //              The transposed products keep each query's scores, running max m, running
-//              sum l and output column in one lane (the lane pair l, l^32 splits the keys).
+//              sum l and output column in one lane column: lanes c, c+16, c+32, c+48 hold
+//              query c of a block and split its keys (and output dims) four ways.
 //   epilogue : O / l, stored as bf16 (round to nearest even) or fp32 at the tokens'
 //              original positions, which reverses the cyclic shift.
+//
+// All chained products use the same MFMA instruction (16x16x32), so they complete in issue
+// order: a shorter MFMA issued right after a longer one could otherwise write registers the
+// longer one still reads as its accumulator input.
 //
 // The running max is updated lazily: with the accumulator preset to -m, S^T already holds
 // s - m and p = 2^(s - m) costs one exp per score.  The exact rescale (row max, O and l
@@ -49,6 +56,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+
 #include "wattn_plan.h"
 
 namespace {
@@ -58,7 +66,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -66,7 +74,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 32;          // head dimension of q, k, v
 constexpr int NTHR = 512;      // threads per workgroup of the bf16 path (8 waves)
 constexpr int QT = WATTN_BF16_QTILE;  // queries per workgroup (32 per wave)
-constexpr int KT = 64;         // keys per LDS tile
+constexpr int KT = 128;        // keys per LDS tile (four 32-key steps)
 constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
@@ -86,16 +94,16 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// score product: fp16 operands, fp32 accumulate
-__device__ __forceinline__ f32x16 mfma32_f16(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+// score product: fp16 operands (k = 32 channels in one instruction), fp32 accumulate
+__device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                 0, 0);
 }
 
-// value product: bf16 operands, fp32 accumulate
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+// value product: bf16 operands (k = 32 keys), fp32 accumulate
+__device__ __forceinline__ f32x4 mfma16_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -113,26 +121,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// i / den and i % den for 0 <= i < 2^16 and 1 <= den <= 2^16, via a multiply-high.
-struct Divider {
-  uint32_t den, magic;
-  __device__ explicit Divider(uint32_t d) : den(d), magic(d == 1 ? 0u : 0xffffffffu / d + 1u) {}
-  __device__ __forceinline__ void split(uint32_t i, int& qt, int& rm) const {
-    const uint32_t qq = (den == 1) ? i : __umulhi(i, magic);
-    qt = (int)qq;
-    rm = (int)(i - qq * den);
-  }
-};
-
-// Chunk swizzles (16-byte chunks of a 64-byte K or V row).  K: the eight rows that one
-// MFMA operand read touches per LDS cycle land in eight distinct bank groups.  V: the four
-// rows of one transposed read group land in distinct bank halves / chunk pairs.
-__device__ __forceinline__ int kswz(int key) { return ((key >> 1) & 1) | (((key >> 4) & 1) << 1); }
+// LDS swizzles.  K and V tiles are row-major (64 bytes per key); the 16-byte chunk index
+// of a row is XORed with a few bits of the key so that the lanes served in one LDS cycle
+// hit distinct banks.  K: the eight keys 8j + 4b + {0..3} (j = 0, 1) read by one group of
+// eight lanes.  V: the four keys of one transposed read group.  Bias factor tile (32 bytes
+// per key): the 16-byte half index is XORed with bit 3 of the key.
+__device__ __forceinline__ int kswz(int key) { return ((key >> 1) & 1) | (((key >> 3) & 1) << 1); }
 __device__ __forceinline__ int vswz(int key) { return ((key >> 1) & 1) << 1; }
-
-// Row of the K tile that feeds MFMA A-operand row i (0..31): the accumulator row layout of
-// the 32x32 MFMA then gives lane (query, g) the scores of keys 16g .. 16g+15 in order.
-__device__ __forceinline__ int key_of_row(int i) { return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3); }
+__device__ __forceinline__ int bswz(int key) { return (key >> 3) & 1; }
 
 struct Task {
   int b, h, q0;
@@ -140,17 +136,22 @@ struct Task {
   int y0, x0;          // region origin in the original grid (the region does not wrap)
 };
 
-// Workgroup bid -> task.  Consecutive groups of `chunk` tasks go to one XCD (workgroups
-// are dealt to the 8 XCDs round-robin), so tasks that share cache lines meet in one L2.
-__device__ __forceinline__ bool decode_task(const WattnPlan& P, int bid, Task& t) {
+// Workgroup -> task.  Groups of `chunk` consecutive tasks (query tiles of one region and
+// head, which share K/V) go to one XCD (workgroups are dealt to the 8 XCDs round-robin), so
+// their K/V lines meet in one L2.  The grid is a multiple of 8 * chunk.
+__device__ __forceinline__ int task_of_block(const WattnPlan& P, int bid) {
   const int C = P.chunk;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int task = ((slot / C) * 8 + xcd) * C + (slot % C);
+  return ((slot / C) * 8 + xcd) * C + (slot % C);
+}
+
+__device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, Task& t) {
   if (task >= P.ntasks) return false;
-  WattnSeg S = P.seg[0];
+  int si = 0;
 #pragma unroll
   for (int i = 1; i < WATTN_MAX_SEG; ++i)
-    if (i < P.nseg && task >= P.seg[i].task_begin) S = P.seg[i];
+    if (i < P.nseg && task >= P.seg[i].task_begin) si = i;
+  const WattnSeg& S = P.seg[si];  // read on demand (dynamic index), not kept live across tasks
   int u = task - S.task_begin;
   const int qt = u % S.nqt;
   u /= S.nqt;
@@ -175,6 +176,43 @@ __device__ __forceinline__ bool decode_task(const WattnPlan& P, int bid, Task& t
   return true;
 }
 
+// Wave-uniform quantities of one task.
+struct TaskCtx {
+  Task t;
+  int n;                 // tokens of the region
+  int64_t img;           // element offset of the image
+  int regbase;           // element offset (within the image) of the region origin, head h
+  int ntile;             // key tiles
+  int step_i, step_j;    // region coordinates advanced per tile
+  int step_off;          // element offset advanced per tile without a column carry
+  int carry_off;         // extra offset on a column carry
+  uint32_t den, magic;   // division by the region width
+};
+
+__device__ __forceinline__ TaskCtx make_ctx(const WattnPlan& P, const Task& t) {
+  TaskCtx X;
+  X.t = t;
+  X.n = t.rh * t.rw;
+  const int colstride = P.H * D, rowstride = P.Wg * colstride;
+  X.img = (int64_t)t.b * P.Hg * rowstride;
+  X.regbase = t.y0 * rowstride + t.x0 * colstride + t.h * D;
+  X.ntile = (X.n + KT - 1) / KT;
+  X.step_i = KT / t.rw;
+  X.step_j = KT % t.rw;
+  X.step_off = X.step_i * rowstride + X.step_j * colstride;
+  X.carry_off = rowstride - t.rw * colstride;
+  X.den = (uint32_t)t.rw;
+  X.magic = (t.rw == 1) ? 0u : 0xffffffffu / (uint32_t)t.rw + 1u;
+  return X;
+}
+
+// i / den and i % den for 0 <= i < 2^16 (den <= 2^16), via a multiply-high.
+__device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt, int& rm) {
+  const uint32_t qq = (X.den == 1) ? i : __umulhi(i, X.magic);
+  qt = (int)qq;
+  rm = (int)(i - qq * X.den);
+}
+
 template <int NKS, bool ROPE, bool OUTF32>
 __global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
@@ -190,281 +228,335 @@ __global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
   __shared__ float2 sTab[ROPE ? MAXM * (D / 2) : 1];
 
-  Task T;
-  if (!decode_task(P, blockIdx.x, T)) return;
-
   const int tid = threadIdx.x;
+  Task T0;
+  if (!decode_task(P, task_of_block(P, blockIdx.x), T0)) return;
+  const TaskCtx X = make_ctx(P, T0);
+
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = P.M;
-  const int h = T.h;
-  const int n = T.rh * T.rw;
   const int colstride = P.H * D;            // elements between horizontally adjacent tokens
   const int rowstride = P.Wg * colstride;   // elements between vertically adjacent tokens
-  const int64_t img = (int64_t)T.b * P.Hg * rowstride;
-  const int regbase = T.y0 * rowstride + T.x0 * colstride + h * D;
-  const uint16_t* qi_ = q + img;
-  const uint16_t* ki_ = k + img;
-  const uint16_t* vi_ = v + img;
-  const Divider div(T.rw);
 
-  if (ROPE) {
-    for (int i = tid; i < M * (D / 2); i += NTHR) {
-      const int pos = i >> 4, j = i & 15;
-      float sn, cs;
-      __sincosf((float)pos * theta[h * (D / 2) + j], &sn, &cs);
-      sTab[i] = make_float2(cs, sn);
-    }
-    __syncthreads();
-  }
+  // Lane (c, g): column c of every 16x16 MFMA block, k-group / row-group g.
+  const int c = lane & 15, g = lane >> 4;
+  const bool tab_thread = ROPE && tid < M * (D / 2);  // one table entry per thread (M <= 32)
 
-  const int qi = lane & 31, g = lane >> 5;
-  const bool wave_live = T.q0 + wave * 32 < n;  // wave-uniform
-
-  // ---- queries: rotate in fp32, scale by d^-1/2 * log2(e), round once to fp16
-  u32x4 Qf[NKS];
+  // ---- per-task loads that are issued ahead of their use: the head's angle for this
+  //      thread's table entry, and this lane's raw query chunks (bias: u chunks).
+  float th = 0.f;
+  u32x4 qraw[2];
+  u32x4 braw[2];
+  int qpos[2];
+  auto load_task_inputs = [&](const TaskCtx& Y) {
+    if (tab_thread) th = theta[Y.t.h * (D / 2) + (tid & 15)];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) Qf[ks] = u32x4{0u, 0u, 0u, 0u};
-  {
-    const int iq = T.q0 + wave * 32 + qi;
-    const float qscale = LOG2E * 0.17677669529663687f;  // log2(e) / sqrt(32)
-    if (iq < n) {
-      int li, lj;
-      div.split((uint32_t)iq, li, lj);
-      const int off = regbase + li * rowstride + lj * colstride;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qi_ + off + 16 * ks + 8 * g);
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float a = bf_lo(raw[p]), c = bf_hi(raw[p]);
-          if (ROPE) {
-            const int pos = (ks == 0) ? (T.r0 + li) : (T.c0 + lj);
-            const float2 t = sTab[pos * (D / 2) + 8 * ks + 4 * g + p];
-            const float a2 = a * t.x - c * t.y;
-            const float c2 = a * t.y + c * t.x;
-            a = a2;
-            c = c2;
-          }
-          o[p] = pack_f16(a * qscale, c * qscale);
+    for (int a = 0; a < 2; ++a) {
+      qraw[a] = u32x4{0u, 0u, 0u, 0u};
+      braw[a] = u32x4{0u, 0u, 0u, 0u};
+      qpos[a] = 0;
+      const int iq = Y.t.q0 + wave * 32 + 16 * a + c;
+      if (iq < Y.n) {
+        int li, lj;
+        split_idx(Y, (uint32_t)iq, li, lj);
+        const int off = Y.regbase + li * rowstride + lj * colstride;
+        qraw[a] = *reinterpret_cast<const u32x4*>(q + Y.img + off + 8 * g);
+        qpos[a] = (g < 2) ? (Y.t.r0 + li) : (Y.t.c0 + lj);  // channels 0..15 carry y, 16..31 x
+        if (BIAS && g < 2) {
+          const int nl = (Y.t.r0 + li) * M + (Y.t.c0 + lj);
+          braw[a] = *reinterpret_cast<const u32x4*>(bu + ((int64_t)Y.t.h * M * M + nl) * 16 + 8 * g);
         }
-        Qf[ks] = o;
-      }
-      if (BIAS) {
-        const int nl = (T.r0 + li) * M + (T.c0 + lj);
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(bu + ((int64_t)h * M * M + nl) * 16 + 8 * g);
-        u32x4 o;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) o[p] = pack_f16(bf_lo(raw[p]) * LOG2E, bf_hi(raw[p]) * LOG2E);
-        Qf[NKS - 1] = o;
       }
     }
-  }
+  };
+  // window-local cos/sin table of the head (fp32 angles, hardware sin/cos)
+  auto build_table = [&](const TaskCtx& Y) {
+    if (ROPE) {
+      if (tab_thread) {
+        float sn, cs;
+        __sincosf((float)(tid >> 4) * th, &sn, &cs);
+        sTab[tid] = make_float2(cs, sn);
+      }
+      for (int i = tid + NTHR; i < M * (D / 2); i += NTHR) {  // windows wider than 32
+        const int pos = i >> 4, j = i & 15;
+        float sn, cs;
+        __sincosf((float)pos * theta[Y.t.h * (D / 2) + j], &sn, &cs);
+        sTab[i] = make_float2(cs, sn);
+      }
+    }
+  };
+  // queries (B operand of the score product): query block a holds queries q0 + 32 wave +
+  // 16 a + c; this lane keeps channels 8g .. 8g+7, rotated in fp32, scaled by
+  // d^-1/2 * log2(e) and rounded once to fp16.  Bias: a second k = 32 operand holding
+  // u * log2(e) in channels 0..15 (lanes g = 0, 1) and zeros in channels 16..31.
+  u32x4 Qf[2];
+  u32x4 Qb[2];
+  auto make_queries = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float qscale = LOG2E * 0.17677669529663687f;  // log2(e) / sqrt(32)
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float x0 = bf_lo(qraw[a][p]), x1 = bf_hi(qraw[a][p]);
+        if (ROPE) {
+          const float2 t = sTab[qpos[a] * (D / 2) + 4 * g + p];
+          const float r0 = x0 * t.x - x1 * t.y;
+          const float r1 = x0 * t.y + x1 * t.x;
+          x0 = r0;
+          x1 = r1;
+        }
+        o[p] = pack_f16(x0 * qscale, x1 * qscale);
+      }
+      Qf[a] = o;
+      Qb[a] = u32x4{0u, 0u, 0u, 0u};
+      if (BIAS) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(braw[a][p]) * LOG2E, bf_hi(braw[a][p]) * LOG2E);
+      }
+    }
+  };
 
-  // ---- loader: threads 0..255 own a K chunk (key lk, channels 8*lch..), 256..511 the V
-  //      chunk; threads 256..383 also own a bias-factor chunk (key bk, channels 8*bch..).
-  //      The key index advances by KT per tile; region coordinates and the element offset
-  //      are carried along incrementally.
-  const bool kthread = tid < 256;
-  const int lk = (tid & 255) >> 2, lch = tid & 3;
-  const int bk = (tid & 127) >> 1, bch = tid & 1;
-  const bool bthread = BIAS && tid >= 256 && tid < 384;
-  const int step_i = KT / T.rw, step_j = KT % T.rw;
-  const int step_off = step_i * rowstride + step_j * colstride;  // offset change without carry
-  const int carry_off = rowstride - T.rw * colstride;              // extra change on a column carry
-  int ci, cj, bi, bj;
-  div.split((uint32_t)lk, ci, cj);
-  div.split((uint32_t)bk, bi, bj);
-  int koff = regbase + ci * rowstride + cj * colstride + 8 * lch;  // element offset of the chunk
-  const uint16_t* ksrc = (kthread ? ki_ : vi_);
-  const uint16_t* bsrc = bv + (int64_t)h * M * M * 16 + 8 * bch;
-  u32x4 pd = {0u, 0u, 0u, 0u}, pb = {0u, 0u, 0u, 0u};
+  // ---- loader: thread t owns the 16-byte chunk lch = t % 4 of key lk = t / 4 of a tile in
+  //      both K and V (same element offset); threads 0..255 also own the 16-byte half
+  //      bch = t % 2 of the bias-factor row of key bk = t / 2.  The key index advances by
+  //      KT per tile; region coordinates and the element offset are carried along.  Keys
+  //      past the region end load the region's last key (finite data; their scores are
+  //      masked, so their probabilities are exactly 0).
+  const int lk = tid >> 2, lch = tid & 3;
+  const int bk = (tid & 255) >> 1, bch = tid & 1;
+  const bool bthread = BIAS && tid < 256;
+  int ci, cj, bi, bj, koff, klast;
+  u32x4 pk, pv, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
-
-  auto advance = [&]() {
-    ci += step_i;
-    cj += step_j;
-    koff += step_off;
-    if (cj >= T.rw) {
-      cj -= T.rw;
+  auto loader_init = [&](const TaskCtx& Y) {
+    split_idx(Y, (uint32_t)lk, ci, cj);
+    split_idx(Y, (uint32_t)bk, bi, bj);
+    koff = Y.regbase + ci * rowstride + cj * colstride + 8 * lch;
+    int li, lj;
+    split_idx(Y, (uint32_t)(Y.n - 1), li, lj);
+    klast = Y.regbase + li * rowstride + lj * colstride + 8 * lch;
+  };
+  auto advance = [&](const TaskCtx& Y) {
+    ci += Y.step_i;
+    cj += Y.step_j;
+    koff += Y.step_off;
+    if (cj >= Y.t.rw) {
+      cj -= Y.t.rw;
       ci += 1;
-      koff += carry_off;
+      koff += Y.carry_off;
     }
     if (BIAS) {
-      bi += step_i;
-      bj += step_j;
-      if (bj >= T.rw) {
-        bj -= T.rw;
+      bi += Y.step_i;
+      bj += Y.step_j;
+      if (bj >= Y.t.rw) {
+        bj -= Y.t.rw;
         bi += 1;
       }
     }
   };
-  auto fetch = [&](int tile) {
-    pd = u32x4{0u, 0u, 0u, 0u};
-    if (tile * KT + lk < n) {
-      pd = *reinterpret_cast<const u32x4*>(ksrc + koff);
-      lpos = (lch < 2) ? (T.r0 + ci) : (T.c0 + cj);
-    }
-    if (BIAS) {
-      pb = u32x4{0u, 0u, 0u, 0u};
-      if (bthread && tile * KT + bk < n)
-        pb = *reinterpret_cast<const u32x4*>(bsrc + ((T.r0 + bi) * M + (T.c0 + bj)) * 16);
+  auto fetch = [&](const TaskCtx& Y, int tile) {
+    const bool valid = tile * KT + lk < Y.n;
+    const int off = valid ? koff : klast;
+    pk = *reinterpret_cast<const u32x4*>(k + Y.img + off);
+    pv = *reinterpret_cast<const u32x4*>(v + Y.img + off);
+    lpos = (lch < 2) ? (Y.t.r0 + ci) : (Y.t.c0 + cj);
+    if (BIAS && bthread) {
+      const bool bvalid = tile * KT + bk < Y.n;
+      const int key = bvalid ? (Y.t.r0 + bi) * M + (Y.t.c0 + bj) : 0;
+      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)Y.t.h * M * M + key) * 16 + 8 * bch);
     }
   };
   auto store = [&](int buf) {
-    if (kthread) {
-      u32x4 kr;
-      if (ROPE) {
+    u32x4 kr;
+    if (ROPE) {
+      const int lp = min(lpos, MAXM - 1);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float a = bf_lo(pd[p]), c = bf_hi(pd[p]);
-          const float2 t = sTab[lpos * (D / 2) + 4 * lch + p];
-          kr[p] = pack_f16(a * t.x - c * t.y, a * t.y + c * t.x);
-        }
-      } else {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) kr[p] = pack_f16(bf_lo(pd[p]), bf_hi(pd[p]));
+      for (int p = 0; p < 4; ++p) {
+        const float x0 = bf_lo(pk[p]), x1 = bf_hi(pk[p]);
+        const float2 t = sTab[lp * (D / 2) + 4 * lch + p];
+        kr[p] = pack_f16(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
       }
-      *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
     } else {
-      *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pd;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) kr[p] = pack_f16(bf_lo(pk[p]), bf_hi(pk[p]));
     }
+    *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
+    *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pv;
     if (BIAS && bthread) {
       u32x4 br;
 #pragma unroll
       for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
-      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + ((bch ^ ((bk >> 4) & 1)) * 8)]) = br;
+      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = br;
     }
   };
 
-  // ---- per-query online-softmax state (lane = query; lanes l and l^32 hold the same m)
-  f32x16 O, Cn;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    O[e] = 0.f;
-    Cn[e] = 0.f;
-  }
-  float m = 0.f, l = 0.f;
-  const uint32_t ONES = 0x3f803f80u;  // bf16 pair (1.0, 1.0)
-  const int ntile = (n + KT - 1) / KT;
-
   // per-lane constants of the operand reads
-  const int arow = key_of_row(lane & 31);             // K tile row feeding A-operand row lane%32
-  const int vgrp = lane >> 4;                         // 16-lane group of the transposed V read
-  const int vs = lane & 15;                           // source lane within the group
-  const int vchunk_hi = (vgrp & 1) * 2;               // dims 0..15 -> chunks 0,1; 16..31 -> 2,3
+  const int krow = 8 * (c >> 2) + (c & 3);  // K tile row (within a step) of A-operand row c, key block 0
+  const int vrow = 8 * g + (c >> 2);        // V tile row (within a step) of the transposed read, half 0
+  const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
+  const uint32_t ONES = 0x3f803f80u;        // bf16 pair (1.0, 1.0)
 
-  fetch(0);
+  // ---- prologue: the global loads of the angle table, the queries and the first K/V tile
+  //      are issued together, so their latencies overlap.
+  load_task_inputs(X);
+  loader_init(X);
+  fetch(X, 0);
+  build_table(X);
+  if (ROPE) __syncthreads();
+  make_queries();
   store(0);
-  advance();
+  advance(X);
   __syncthreads();
 
-#pragma unroll 2
-  for (int tile = 0; tile < ntile; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntile) fetch(tile + 1);
+  // ---- online-softmax state per query block a (lanes c, c+16, c+32, c+48 share a query)
+  f32x4 O[2][2];  // [dim block][query block]: dims 16 db + 4 g + e of query 16 a + c
+  f32x4 Cn[2];    // -m broadcast, the accumulator preset of the score product
+  float m[2], l[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    O[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    O[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Cn[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[a] = 0.f;
+    l[a] = 0.f;
+  }
+  const int n = X.n;
+  const bool wave_live = X.t.q0 + wave * 32 < n;  // wave-uniform
 
-    if (wave_live) {
+  // one key tile: four 32-key steps of the score product, online softmax and value product
+  auto compute_tile = [&](int buf, int tile) {
+      if (wave_live) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int kb = st * 32;
-        const int kg = tile * KT + kb;  // first key of the step (uniform)
-        if (kg < n) {
-          const int key = kb + arow;
-          u32x4 Kf[NKS];
-          Kf[0] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((0 + g) ^ kswz(key)) * 8)]);
-          Kf[1] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + (((2 + g) ^ kswz(key)) * 8)]);
-          if (BIAS)
-            Kf[NKS - 1] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + ((g ^ ((key >> 4) & 1)) * 8)]);
-          // V^T operand of the two PV MFMAs: keys kb + 16g + 8j + 4u + t, dims of this lane
-          u32x2 Vt[2][2];
+        for (int st = 0; st < KT / 32; ++st) {
+          const int kb = st * 32;
+          const int kg = tile * KT + kb;  // first key of the step (uniform)
+          if (kg < n) {
+            // score operand A: key kb + 8(c/4) + 4b + c%4, channels 8g .. 8g+7 (fp16)
+            u32x4 Kf[2];
+            u32x4 Kb[2];
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int row = kb + 16 * (vgrp >> 1) + 8 * j + 4 * u + (vs >> 2);
-              const int chunk = vchunk_hi + ((vs & 3) >> 1);
-              Vt[j][u] = lds_read_tr16(&sV[buf][row * D + ((chunk ^ vswz(row)) * 8) + 4 * (vs & 1)]);
+            for (int b = 0; b < 2; ++b) {
+              const int key = kb + krow + 4 * b;
+              Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
+              if (BIAS) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
             }
+            // value operand A (V^T): dims 16 db + c, keys kb + 8g + 4hh + t via transposed reads
+            u32x2 Vt[2][2];
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const int row = kb + vrow + 4 * hh;
+                const int ch = 2 * db + vch;
+                Vt[db][hh] = lds_read_tr16(&sV[buf][row * D + ((ch ^ vswz(row)) * 8) + vsub]);
+              }
 
-          f32x16 S = mfma32_f16(Kf[0], Qf[0], Cn);
+            // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus m
+            f32x4 S[2][2];
 #pragma unroll
-          for (int ks = 1; ks < NKS; ++ks) S = mfma32_f16(Kf[ks], Qf[ks], S);
-          if (kg + 32 > n) {
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (kg + 16 * g + e >= n) S[e] = -INFINITY;
-          }
-          const bool first = (tile == 0) && (st == 0);
-          uint32_t Pp[8];
-          float ls = 0.f;
-          bool exact = first;
-          if (!first) {
+              for (int b = 0; b < 2; ++b) {
+                // bias channels first (the same k = 32 instruction as the score product, so
+                // chained products complete in issue order)
+                S[a][b] = BIAS ? mfma16_f16(Kb[b], Qb[a], Cn[a]) : Cn[a];
+                S[a][b] = mfma16_f16(Kf[b], Qf[a], S[a][b]);
+              }
+            if (kg + 32 > n) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(S[2 * t]), __builtin_amdgcn_exp2f(S[2 * t + 1]));
-              ls = dot2_bf16(Pp[t], ONES, ls);
+              for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    if (kg + 8 * g + 4 * b + e >= n) S[a][b][e] = -INFINITY;
             }
-            exact = __any(ls > RESCALE_LIMIT);
-          }
-          if (exact) {
-            float mx = S[0];
+            const bool first = (tile == 0) && (st == 0);
 #pragma unroll
-            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float delta = first ? mx : fmaxf(mx, 0.f);
-            if (!first) {
-              const float a = __builtin_amdgcn_exp2f(-delta);
-              l *= a;
+            for (int a = 0; a < 2; ++a) {
+              uint32_t Pp[4];
+              float ls = 0.f;
+              bool exact = first;
+              if (!first) {
 #pragma unroll
-              for (int e = 0; e < 16; ++e) O[e] *= a;
+                for (int t = 0; t < 4; ++t) {
+                  const f32x4& s = S[a][t >> 1];
+                  const int e0 = 2 * (t & 1);
+                  Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0]), __builtin_amdgcn_exp2f(s[e0 + 1]));
+                  ls = dot2_bf16(Pp[t], ONES, ls);
+                }
+                exact = __any(ls > RESCALE_LIMIT);
+              }
+              if (exact) {
+                float mx = fmaxf(fmaxf(S[a][0][0], S[a][0][1]), fmaxf(S[a][0][2], S[a][0][3]));
+                mx = fmaxf(mx, fmaxf(fmaxf(S[a][1][0], S[a][1][1]), fmaxf(S[a][1][2], S[a][1][3])));
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float delta = first ? mx : fmaxf(mx, 0.f);
+                if (!first) {
+                  const float f = __builtin_amdgcn_exp2f(-delta);
+                  l[a] *= f;
+                  O[0][a] *= f;
+                  O[1][a] *= f;
+                }
+                m[a] += delta;
+                Cn[a] = f32x4{-m[a], -m[a], -m[a], -m[a]};
+                ls = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const f32x4& s = S[a][t >> 1];
+                  const int e0 = 2 * (t & 1);
+                  Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0] - delta), __builtin_amdgcn_exp2f(s[e0 + 1] - delta));
+                  ls = dot2_bf16(Pp[t], ONES, ls);
+                }
+              }
+              l[a] += ls;
+              const u32x4 Pa = {Pp[0], Pp[1], Pp[2], Pp[3]};  // keys kb + 8g .. 8g+7 of query 16a + c
+#pragma unroll
+              for (int db = 0; db < 2; ++db)
+                O[db][a] = mfma16_bf16(u32x4{Vt[db][0][0], Vt[db][0][1], Vt[db][1][0], Vt[db][1][1]}, Pa, O[db][a]);
             }
-            m += delta;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Cn[e] = -m;
-            ls = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(S[2 * t] - delta),
-                                __builtin_amdgcn_exp2f(S[2 * t + 1] - delta));
-              ls = dot2_bf16(Pp[t], ONES, ls);
-            }
           }
-          l += ls;
-          const u32x4 P0 = {Pp[0], Pp[1], Pp[2], Pp[3]};
-          const u32x4 P1 = {Pp[4], Pp[5], Pp[6], Pp[7]};
-          O = mfma32(u32x4{Vt[0][0][0], Vt[0][0][1], Vt[0][1][0], Vt[0][1][1]}, P0, O);
-          O = mfma32(u32x4{Vt[1][0][0], Vt[1][0][1], Vt[1][1][0], Vt[1][1][1]}, P1, O);
         }
       }
-    }
+  };
 
-    if (tile + 1 < ntile) {
+
+  for (int tile = 0; tile < X.ntile; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < X.ntile;
+    if (more) fetch(X, tile + 1);
+    compute_tile(buf, tile);
+    if (more) {
       store(buf ^ 1);
-      advance();
+      advance(X);
     }
     __syncthreads();
   }
 
   // ---- epilogue: normalise, scatter to the original positions
-  const float lt = l + __shfl_xor(l, 32);
-  const int iq = T.q0 + wave * 32 + qi;
-  if (iq < n) {
-    const float inv = 1.0f / lt;
-    int li, lj;
-    div.split((uint32_t)iq, li, lj);
-    const int64_t off = img + regbase + li * rowstride + lj * colstride;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (OUTF32) {
-        const float4 w = make_float4(O[4 * t + 0] * inv, O[4 * t + 1] * inv, O[4 * t + 2] * inv, O[4 * t + 3] * inv);
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + off + 8 * t + 4 * g) = w;
-      } else {
-        u32x2 w;
-        w[0] = pack_bf16(O[4 * t + 0] * inv, O[4 * t + 1] * inv);
-        w[1] = pack_bf16(O[4 * t + 2] * inv, O[4 * t + 3] * inv);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off + 8 * t + 4 * g) = w;
+  for (int a = 0; a < 2; ++a) {
+    float lt = l[a] + __shfl_xor(l[a], 16);
+    lt += __shfl_xor(lt, 32);
+    const int iq = X.t.q0 + wave * 32 + 16 * a + c;
+    if (iq < n) {
+      const float inv = 1.0f / lt;
+      int li, lj;
+      split_idx(X, (uint32_t)iq, li, lj);
+      const int64_t off = X.img + X.regbase + li * rowstride + lj * colstride;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const f32x4 o = O[db][a] * inv;
+        if (OUTF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + off + 16 * db + 4 * g) =
+              make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          const u32x2 wv = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + off + 16 * db + 4 * g) = wv;
+        }
       }
     }
   }
@@ -626,12 +718,13 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
 // ------------------------------------------------------------------------------------
 
 template <int NKS, bool ROPE, bool OUTF32>
-static void launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
-                             const float* theta, const void* bu, const void* bv, hipStream_t stream) {
+static hipError_t launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
+                                   const float* theta, const void* bu, const void* bv, hipStream_t stream) {
   hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(NTHR), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, theta, static_cast<const uint16_t*>(bu),
                      static_cast<const uint16_t*>(bv), plan);
+  return hipGetLastError();
 }
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
@@ -639,16 +732,15 @@ hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out
                              const void* bv, hipStream_t stream) {
   const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: launch_bf16_inst<2, false, false>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 1: launch_bf16_inst<2, false, true>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 2: launch_bf16_inst<2, true, false>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 3: launch_bf16_inst<2, true, true>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 4: launch_bf16_inst<3, false, false>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 5: launch_bf16_inst<3, false, true>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    case 6: launch_bf16_inst<3, true, false>(plan, q, k, v, out, theta, bu, bv, stream); break;
-    default: launch_bf16_inst<3, true, true>(plan, q, k, v, out, theta, bu, bv, stream); break;
+    case 0: return launch_bf16_inst<2, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 1: return launch_bf16_inst<2, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 2: return launch_bf16_inst<2, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 3: return launch_bf16_inst<2, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 4: return launch_bf16_inst<3, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 5: return launch_bf16_inst<3, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 6: return launch_bf16_inst<3, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    default: return launch_bf16_inst<3, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,

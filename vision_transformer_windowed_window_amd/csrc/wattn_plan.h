@@ -7,7 +7,8 @@
 // pairs are never computed.  Windows that share a region shape form one segment.
 //
 // Task order (innermost first): query tile, head, window of the segment, image, segment.
-// Segments are sorted by region size, largest first, so heavy tasks are dispatched early.
+// Segments are sorted by region size, largest first.  The bf16 kernel is persistent: a grid
+// of at most the resident workgroup count walks the task list in rounds of `grid` tasks.
 #pragma once
 
 #include <stdint.h>
@@ -29,7 +30,7 @@ struct WattnPlan {
   int ntasks;
   int B, H, Hg, Wg, M, s;
   int chunk;  // tasks kept together on one XCD (consecutive tasks share K/V in L2)
-  int grid;   // launched workgroups: ntasks rounded up to a multiple of 8 * chunk
+  int grid;   // launched workgroups (a multiple of 8 * chunk); round r holds tasks [r grid, r grid + grid)
 };
 
 // Plain per-window plan of the fp32 path: one workgroup per (query tile, head, window, image).
