@@ -214,7 +214,7 @@ __device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt,
 }
 
 template <int NKS, bool ROPE, bool OUTF32>
-__global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               void* __restrict__ out,
@@ -426,101 +426,119 @@ __global__ __launch_bounds__(NTHR) void wattn_fwd_bf16_kernel(const uint16_t* __
   const bool wave_live = X.t.q0 + wave * 32 < n;  // wave-uniform
 
   // one key tile: four 32-key steps of the score product, online softmax and value product
-  auto compute_tile = [&](int buf, int tile) {
-      if (wave_live) {
+  // LDS operand fragments of one 32-key step
+  struct Frags {
+    u32x4 Kf[2];  // score operand A: key kb + 8(c/4) + 4b + c%4, channels 8g .. 8g+7 (fp16)
+    u32x4 Kb[2];  // bias operand A: channels 8(g%2) .. 8(g%2)+7 of the same keys
+    u32x4 V[2];   // value operand A (V^T): dims 16 db + c, keys kb + 8g .. 8g+7
+  };
+  auto load_frags = [&](int buf, int kb, Frags& F) {
 #pragma unroll
-        for (int st = 0; st < KT / 32; ++st) {
-          const int kb = st * 32;
-          const int kg = tile * KT + kb;  // first key of the step (uniform)
-          if (kg < n) {
-            // score operand A: key kb + 8(c/4) + 4b + c%4, channels 8g .. 8g+7 (fp16)
-            u32x4 Kf[2];
-            u32x4 Kb[2];
+    for (int b = 0; b < 2; ++b) {
+      const int key = kb + krow + 4 * b;
+      F.Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
+      if (BIAS) F.Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+    }
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int key = kb + krow + 4 * b;
-              Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
-              if (BIAS) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
-            }
-            // value operand A (V^T): dims 16 db + c, keys kb + 8g + 4hh + t via transposed reads
-            u32x2 Vt[2][2];
+    for (int db = 0; db < 2; ++db) {
+      u32x2 h[2];
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                const int row = kb + vrow + 4 * hh;
-                const int ch = 2 * db + vch;
-                Vt[db][hh] = lds_read_tr16(&sV[buf][row * D + ((ch ^ vswz(row)) * 8) + vsub]);
-              }
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = kb + vrow + 4 * hh;
+        const int ch = 2 * db + vch;
+        h[hh] = lds_read_tr16(&sV[buf][row * D + ((ch ^ vswz(row)) * 8) + vsub]);
+      }
+      F.V[db] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+    }
+  };
 
-            // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus m
-            f32x4 S[2][2];
+  // one key tile: up to four 32-key steps; the fragments of step st + 1 are read from LDS
+  // while step st is computed
+  auto compute_tile = [&](int buf, int tile) {
+    if (!wave_live) return;
+    const int nst = min(KT / 32, (n - tile * KT + 31) / 32);  // steps holding keys (uniform)
+    Frags F[2];
+    load_frags(buf, 0, F[0]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+    for (int st = 0; st < KT / 32; ++st) {
+      if (st < nst) {
+        const int kg = tile * KT + st * 32;  // first key of the step (uniform)
+        const Frags& cur = F[st & 1];
+        if (st + 1 < nst) load_frags(buf, (st + 1) * 32, F[(st + 1) & 1]);
+
+        // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus m
+        f32x4 S[2][2];
 #pragma unroll
-              for (int b = 0; b < 2; ++b) {
-                // bias channels first (the same k = 32 instruction as the score product, so
-                // chained products complete in issue order)
-                S[a][b] = BIAS ? mfma16_f16(Kb[b], Qb[a], Cn[a]) : Cn[a];
-                S[a][b] = mfma16_f16(Kf[b], Qf[a], S[a][b]);
-              }
-            if (kg + 32 > n) {
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-              for (int a = 0; a < 2; ++a)
+          for (int b = 0; b < 2; ++b) {
+            // bias channels first (the same k = 32 instruction as the score product, so
+            // chained products complete in issue order)
+            S[a][b] = BIAS ? mfma16_f16(cur.Kb[b], Qb[a], Cn[a]) : Cn[a];
+            S[a][b] = mfma16_f16(cur.Kf[b], Qf[a], S[a][b]);
+          }
+        if (kg + 32 > n) {
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+          for (int a = 0; a < 2; ++a)
 #pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    if (kg + 8 * g + 4 * b + e >= n) S[a][b][e] = -INFINITY;
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (kg + 8 * g + 4 * b + e >= n) S[a][b][e] = -INFINITY;
+        }
+        const bool first = (tile == 0) && (st == 0);
+        uint32_t Pp[2][4];
+        float ls[2] = {0.f, 0.f};
+        bool exact = first;
+        if (!first) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f32x4& s = S[a][t >> 1];
+              const int e0 = 2 * (t & 1);
+              Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0]), __builtin_amdgcn_exp2f(s[e0 + 1]));
             }
-            const bool first = (tile == 0) && (st == 0);
+            ls[a] = dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, 0.f)) +
+                    dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, 0.f));
+          }
+          exact = __any(fmaxf(ls[0], ls[1]) > RESCALE_LIMIT);
+        }
+        if (exact) {
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-              uint32_t Pp[4];
-              float ls = 0.f;
-              bool exact = first;
-              if (!first) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const f32x4& s = S[a][t >> 1];
-                  const int e0 = 2 * (t & 1);
-                  Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0]), __builtin_amdgcn_exp2f(s[e0 + 1]));
-                  ls = dot2_bf16(Pp[t], ONES, ls);
-                }
-                exact = __any(ls > RESCALE_LIMIT);
-              }
-              if (exact) {
-                float mx = fmaxf(fmaxf(S[a][0][0], S[a][0][1]), fmaxf(S[a][0][2], S[a][0][3]));
-                mx = fmaxf(mx, fmaxf(fmaxf(S[a][1][0], S[a][1][1]), fmaxf(S[a][1][2], S[a][1][3])));
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float delta = first ? mx : fmaxf(mx, 0.f);
-                if (!first) {
-                  const float f = __builtin_amdgcn_exp2f(-delta);
-                  l[a] *= f;
-                  O[0][a] *= f;
-                  O[1][a] *= f;
-                }
-                m[a] += delta;
-                Cn[a] = f32x4{-m[a], -m[a], -m[a], -m[a]};
-                ls = 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                  const f32x4& s = S[a][t >> 1];
-                  const int e0 = 2 * (t & 1);
-                  Pp[t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0] - delta), __builtin_amdgcn_exp2f(s[e0 + 1] - delta));
-                  ls = dot2_bf16(Pp[t], ONES, ls);
-                }
-              }
-              l[a] += ls;
-              const u32x4 Pa = {Pp[0], Pp[1], Pp[2], Pp[3]};  // keys kb + 8g .. 8g+7 of query 16a + c
-#pragma unroll
-              for (int db = 0; db < 2; ++db)
-                O[db][a] = mfma16_bf16(u32x4{Vt[db][0][0], Vt[db][0][1], Vt[db][1][0], Vt[db][1][1]}, Pa, O[db][a]);
+          for (int a = 0; a < 2; ++a) {
+            float mx = fmaxf(fmaxf(S[a][0][0], S[a][0][1]), fmaxf(S[a][0][2], S[a][0][3]));
+            mx = fmaxf(mx, fmaxf(fmaxf(S[a][1][0], S[a][1][1]), fmaxf(S[a][1][2], S[a][1][3])));
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float delta = first ? mx : fmaxf(mx, 0.f);
+            if (!first) {
+              const float f = __builtin_amdgcn_exp2f(-delta);
+              l[a] *= f;
+              O[0][a] *= f;
+              O[1][a] *= f;
             }
+            m[a] += delta;
+            Cn[a] = f32x4{-m[a], -m[a], -m[a], -m[a]};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const f32x4& s = S[a][t >> 1];
+              const int e0 = 2 * (t & 1);
+              Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0] - delta), __builtin_amdgcn_exp2f(s[e0 + 1] - delta));
+            }
+            ls[a] = dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, 0.f)) +
+                    dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, 0.f));
           }
         }
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          l[a] += ls[a];
+          const u32x4 Pa = {Pp[a][0], Pp[a][1], Pp[a][2], Pp[a][3]};  // keys kb + 8g .. 8g+7 of query 16a + c
+#pragma unroll
+          for (int db = 0; db < 2; ++db) O[db][a] = mfma16_bf16(cur.V[db], Pa, O[db][a]);
+        }
       }
+    }
   };
 
 
