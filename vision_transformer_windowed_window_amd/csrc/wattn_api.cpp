@@ -60,9 +60,22 @@ AxisSplit split_axis(int G, int M, int s) {
 }
 
 // Returns false if the task count would not fit the launch limits.
-bool build_plan(int B, int H, int Hg, int Wg, int M, int s, int qtile, WattnPlan& P) {
+// Waves per workgroup of the bf16 path: wide workgroups amortise each staged K/V tile over
+// more queries; narrow ones keep waves busy when windows (and their wrap regions) are small.
+int waves_for_window(int M) {
+#ifdef WATTN_FORCE_NW
+  (void)M;
+  return WATTN_FORCE_NW;
+#else
+  return M >= 24 ? 8 : (M >= 12 ? 4 : 2);
+#endif
+}
+
+bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
   P = WattnPlan{};
   P.B = B; P.H = H; P.Hg = Hg; P.Wg = Wg; P.M = M; P.s = s;
+  P.nw = waves_for_window(M);
+  const int qtile = 32 * P.nw;
   const AxisSplit ay = split_axis(Hg, M, s), ax = split_axis(Wg, M, s);
   WattnSeg segs[WATTN_MAX_SEG];
   int ns = 0;
@@ -147,7 +160,7 @@ extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* 
   WattnPlan plan;
   WattnF32Plan fplan{};
   if (dtype != WATTN_FP32) {
-    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, WATTN_BF16_QTILE, plan)) return WATTN_ERR_SHAPE;
+    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan)) return WATTN_ERR_SHAPE;
   } else {
     fplan.B = B; fplan.H = H; fplan.Hg = Hgrid; fplan.Wg = Wgrid; fplan.M = M; fplan.s = shift;
     fplan.nwx = Wgrid / M;

@@ -6,9 +6,10 @@
 // Work decomposition.  A shifted window of the last row or column band holds two (corner:
 // four) wrap regions; tokens attend only within their region, and each region is a
 // rectangle of tokens that is contiguous in the ORIGINAL (un-shifted) grid.  A workgroup
-// of 8 waves owns 256 queries (32 per wave, two blocks of 16) of one region of one window
-// and head and streams the region's keys through LDS in tiles of 128.  The masked pairs of
-// the shifted layer are never computed.
+// of NW waves (2, 4 or 8, picked by the host from the window side) owns 32 NW queries (32
+// per wave, two blocks of 16) of one region of one window and head and streams the
+// region's keys through LDS in tiles of 16 NW keys.  The masked pairs of the shifted layer
+// are never computed.
 //
 //   prologue : decode the task; issue the global loads of the head's angles, the wave's
 //              queries and the first K/V tile together; build the window-local cos/sin
@@ -16,7 +17,7 @@
 //              fold in d^-1/2 * log2(e), round once to fp16 and keep them in registers;
 //              with a bias, u * log2(e) forms a second (zero-padded) k = 32 operand.
 //   key loop : per tile, every thread fetches one 16-byte chunk of K and the matching
-//              chunk of V (threads 0..255 also one of the bias factor v) for the next tile
+//              chunk of V (half the threads also one of the bias factor v) for the next tile
 //              while the current tile is computed; then K is rotated in fp32, rounded to
 //              fp16 and stored with V (bf16, unchanged) into the other LDS buffer (both
 //              row-major, chunk-swizzled against bank conflicts).  Per 32-key step and
@@ -72,9 +73,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 32;          // head dimension of q, k, v
-constexpr int NTHR = 512;      // threads per workgroup of the bf16 path (8 waves)
-constexpr int QT = WATTN_BF16_QTILE;  // queries per workgroup (32 per wave)
-constexpr int KT = 128;        // keys per LDS tile (four 32-key steps)
 constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
@@ -111,6 +109,25 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          false);
 }
 
+// Sum / max over the lane pairs (l, l ^ 16) and (l, l ^ 32): the gfx950 swap instructions hand
+// every lane the pair {x[l], x[l ^ 16]} (or ^ 32) without a trip through LDS.
+__device__ __forceinline__ float xsum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xsum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Transposed 8-byte LDS read (gfx950): in each group of 16 lanes, lane j receives element
@@ -145,7 +162,7 @@ __device__ __forceinline__ int task_of_block(const WattnPlan& P, int bid) {
   return ((slot / C) * 8 + xcd) * C + (slot % C);
 }
 
-__device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, Task& t) {
+__device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, int QT, Task& t) {
   if (task >= P.ntasks) return false;
   int si = 0;
 #pragma unroll
@@ -189,7 +206,7 @@ struct TaskCtx {
   uint32_t den, magic;   // division by the region width
 };
 
-__device__ __forceinline__ TaskCtx make_ctx(const WattnPlan& P, const Task& t) {
+__device__ __forceinline__ TaskCtx make_ctx(const WattnPlan& P, const Task& t, int KT) {
   TaskCtx X;
   X.t = t;
   X.n = t.rh * t.rw;
@@ -213,8 +230,9 @@ __device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt,
   rm = (int)(i - qq * X.den);
 }
 
-template <int NKS, bool ROPE, bool OUTF32>
-__global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
+// NW waves per workgroup (2, 4 or 8): 32 NW queries, key tiles of 16 NW keys.
+template <int NW, int NKS, bool ROPE, bool OUTF32>
+__global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               void* __restrict__ out,
@@ -223,15 +241,18 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
                                                               const uint16_t* __restrict__ bv,
                                                               const WattnPlan P) {
   constexpr bool BIAS = (NKS == 3);
+  constexpr int NTHR = 64 * NW;  // threads
+  constexpr int QT = 32 * NW;    // queries (two 16-query blocks per wave)
+  constexpr int KT = 16 * NW;    // keys per LDS tile: each thread stages one 16-byte chunk of K and of V
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
-  __shared__ float2 sTab[ROPE ? MAXM * (D / 2) : 1];
+  extern __shared__ float2 sTab[];  // M x 16 cos/sin entries of the head (dynamic size)
 
   const int tid = threadIdx.x;
   Task T0;
-  if (!decode_task(P, task_of_block(P, blockIdx.x), T0)) return;
-  const TaskCtx X = make_ctx(P, T0);
+  if (!decode_task(P, task_of_block(P, blockIdx.x), QT, T0)) return;
+  const TaskCtx X = make_ctx(P, T0, KT);
 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -241,7 +262,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
 
   // Lane (c, g): column c of every 16x16 MFMA block, k-group / row-group g.
   const int c = lane & 15, g = lane >> 4;
-  const bool tab_thread = ROPE && tid < M * (D / 2);  // one table entry per thread (M <= 32)
+  const bool tab_thread = ROPE && tid < M * (D / 2);  // one table entry per thread
 
   // ---- per-task loads that are issued ahead of their use: the head's angle for this
   //      thread's table entry, and this lane's raw query chunks (bias: u chunks).
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
         __sincosf((float)(tid >> 4) * th, &sn, &cs);
         sTab[tid] = make_float2(cs, sn);
       }
-      for (int i = tid + NTHR; i < M * (D / 2); i += NTHR) {  // windows wider than 32
+      for (int i = tid + NTHR; i < M * (D / 2); i += NTHR) {  // the entries beyond one per thread
         const int pos = i >> 4, j = i & 15;
         float sn, cs;
         __sincosf((float)pos * theta[Y.t.h * (D / 2) + j], &sn, &cs);
@@ -319,14 +340,14 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
   };
 
   // ---- loader: thread t owns the 16-byte chunk lch = t % 4 of key lk = t / 4 of a tile in
-  //      both K and V (same element offset); threads 0..255 also own the 16-byte half
-  //      bch = t % 2 of the bias-factor row of key bk = t / 2.  The key index advances by
+  //      both K and V (same element offset); threads 0 .. 2 KT - 1 also own the 16-byte
+  //      half bch = t % 2 of the bias-factor row of key bk = t / 2.  The key index advances by
   //      KT per tile; region coordinates and the element offset are carried along.  Keys
   //      past the region end load the region's last key (finite data; their scores are
   //      masked, so their probabilities are exactly 0).
   const int lk = tid >> 2, lch = tid & 3;
-  const int bk = (tid & 255) >> 1, bch = tid & 1;
-  const bool bthread = BIAS && tid < 256;
+  const int bk = (tid % (2 * KT)) >> 1, bch = tid & 1;
+  const bool bthread = BIAS && tid < 2 * KT;
   int ci, cj, bi, bj, koff, klast;
   u32x4 pk, pv, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
@@ -371,7 +392,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
   auto store = [&](int buf) {
     u32x4 kr;
     if (ROPE) {
-      const int lp = min(lpos, MAXM - 1);
+      const int lp = min(lpos, M - 1);  // keys past the region end: any in-table row
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float x0 = bf_lo(pk[p]), x1 = bf_hi(pk[p]);
@@ -468,6 +489,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
 
         // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus m
         f32x4 S[2][2];
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -477,6 +499,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
             S[a][b] = BIAS ? mfma16_f16(cur.Kb[b], Qb[a], Cn[a]) : Cn[a];
             S[a][b] = mfma16_f16(cur.Kf[b], Qf[a], S[a][b]);
           }
+        __builtin_amdgcn_s_setprio(0);
         if (kg + 32 > n) {
 #pragma unroll
           for (int a = 0; a < 2; ++a)
@@ -509,8 +532,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
           for (int a = 0; a < 2; ++a) {
             float mx = fmaxf(fmaxf(S[a][0][0], S[a][0][1]), fmaxf(S[a][0][2], S[a][0][3]));
             mx = fmaxf(mx, fmaxf(fmaxf(S[a][1][0], S[a][1][1]), fmaxf(S[a][1][2], S[a][1][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = xmax32(xmax16(mx));
             const float delta = first ? mx : fmaxf(mx, 0.f);
             if (!first) {
               const float f = __builtin_amdgcn_exp2f(-delta);
@@ -557,8 +579,7 @@ __global__ __launch_bounds__(NTHR, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(
   // ---- epilogue: normalise, scatter to the original positions
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    float lt = l[a] + __shfl_xor(l[a], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xsum32(xsum16(l[a]));
     const int iq = X.t.q0 + wave * 32 + 16 * a + c;
     if (iq < n) {
       const float inv = 1.0f / lt;
@@ -735,29 +756,42 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
 // Launchers (C++ linkage, internal to the library)
 // ------------------------------------------------------------------------------------
 
-template <int NKS, bool ROPE, bool OUTF32>
+template <int NW, int NKS, bool ROPE, bool OUTF32>
 static hipError_t launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
                                    const float* theta, const void* bu, const void* bv, hipStream_t stream) {
-  hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(NTHR), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  const size_t table_bytes = ROPE ? (size_t)plan.M * (D / 2) * sizeof(float2) : 0;
+  hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NW, NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, theta, static_cast<const uint16_t*>(bu),
                      static_cast<const uint16_t*>(bv), plan);
   return hipGetLastError();
 }
 
+template <int NW>
+static hipError_t launch_bf16_nw(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
+                                 const void* k, const void* v, void* out, const float* theta, const void* bu,
+                                 const void* bv, hipStream_t stream) {
+  const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+  switch (sel) {
+    case 0: return launch_bf16_inst<NW, 2, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 1: return launch_bf16_inst<NW, 2, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 2: return launch_bf16_inst<NW, 2, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 3: return launch_bf16_inst<NW, 2, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 4: return launch_bf16_inst<NW, 3, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 5: return launch_bf16_inst<NW, 3, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 6: return launch_bf16_inst<NW, 3, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
+    default: return launch_bf16_inst<NW, 3, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
+  }
+}
+
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
                              const void* bv, hipStream_t stream) {
-  const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
-  switch (sel) {
-    case 0: return launch_bf16_inst<2, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 1: return launch_bf16_inst<2, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 2: return launch_bf16_inst<2, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 3: return launch_bf16_inst<2, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 4: return launch_bf16_inst<3, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 5: return launch_bf16_inst<3, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 6: return launch_bf16_inst<3, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    default: return launch_bf16_inst<3, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
+  switch (plan.nw) {
+    case 2: return launch_bf16_nw<2>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
+    case 4: return launch_bf16_nw<4>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
+    case 8: return launch_bf16_nw<8>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

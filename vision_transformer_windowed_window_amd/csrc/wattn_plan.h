@@ -7,14 +7,12 @@
 // pairs are never computed.  Windows that share a region shape form one segment.
 //
 // Task order (innermost first): query tile, head, window of the segment, image, segment.
-// Segments are sorted by region size, largest first.  The bf16 kernel is persistent: a grid
-// of at most the resident workgroup count walks the task list in rounds of `grid` tasks.
+// Segments are sorted by region size, largest first.
 #pragma once
 
 #include <stdint.h>
 
 #define WATTN_MAX_SEG 9
-#define WATTN_BF16_QTILE 256  // queries per workgroup of the bf16 path (8 waves x 32)
 #define WATTN_F32_QTILE 256   // queries per workgroup of the fp32 path (one per thread)
 
 struct WattnSeg {
@@ -29,8 +27,9 @@ struct WattnPlan {
   int nseg;
   int ntasks;
   int B, H, Hg, Wg, M, s;
+  int nw;     // waves per workgroup of the bf16 path (2, 4 or 8); a task covers 32 nw queries
   int chunk;  // tasks kept together on one XCD (consecutive tasks share K/V in L2)
-  int grid;   // launched workgroups (a multiple of 8 * chunk); round r holds tasks [r grid, r grid + grid)
+  int grid;   // launched workgroups: ntasks rounded up to a multiple of 8 * chunk
 };
 
 // Plain per-window plan of the fp32 path: one workgroup per (query tile, head, window, image).
