@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
-  extern __shared__ float2 sTab[];  // M x 16 cos/sin entries of the head (dynamic size)
+  extern __shared__ float2 sTab[];  // 16 x M cos/sin entries of the head, pair-major (dynamic size)
 
   const int tid = threadIdx.x;
   Task T0;
@@ -297,13 +297,13 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       if (tab_thread) {
         float sn, cs;
         __sincosf((float)(tid >> 4) * th, &sn, &cs);
-        sTab[tid] = make_float2(cs, sn);
+        sTab[(tid & 15) * M + (tid >> 4)] = make_float2(cs, sn);
       }
       for (int i = tid + NTHR; i < M * (D / 2); i += NTHR) {  // the entries beyond one per thread
         const int pos = i >> 4, j = i & 15;
         float sn, cs;
         __sincosf((float)pos * theta[Y.t.h * (D / 2) + j], &sn, &cs);
-        sTab[i] = make_float2(cs, sn);
+        sTab[j * M + pos] = make_float2(cs, sn);
       }
     }
   };
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       for (int p = 0; p < 4; ++p) {
         float x0 = bf_lo(qraw[a][p]), x1 = bf_hi(qraw[a][p]);
         if (ROPE) {
-          const float2 t = sTab[qpos[a] * (D / 2) + 4 * g + p];
+          const float2 t = sTab[(4 * g + p) * M + qpos[a]];
           const float r0 = x0 * t.x - x1 * t.y;
           const float r1 = x0 * t.y + x1 * t.x;
           x0 = r0;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float x0 = bf_lo(pk[p]), x1 = bf_hi(pk[p]);
-        const float2 t = sTab[lp * (D / 2) + 4 * lch + p];
+        const float2 t = sTab[(4 * lch + p) * M + lp];
         kr[p] = pack_f16(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
       }
     } else {
