@@ -39,9 +39,11 @@
 //
 // The running max is updated lazily: with the accumulator preset to -m, S^T already holds
 // s - m and p = 2^(s - m) costs one exp per score.  The exact rescale (row max, O and l
-// scaled by 2^-delta) runs for the first key step and whenever some p of a step exceeds
-// 2^16, so every p stays within [0, 2^16] (row sums stay below 2^16 * N).  Row sums are
-// taken over the bf16-rounded p that the PV product consumes.
+// scaled by 2^-delta) runs for the first key step and whenever the eight p a lane adds to
+// its row sum in one step exceed 2^16 in total, so every p that reaches O stays within
+// [0, 2^16] up to rounding (row sums stay below 2^16 * N).  Row sums are taken over the
+// bf16-rounded p that the PV product consumes, chained into the running sum with dot2
+// instructions; the step's share is the difference to the sum before the step.
 //
 // Precision: q, k, v arrive in bf16 and RoPE runs in fp32 (FLASHSWIN page, closing
 // developer paragraph).  The rotated, scaled q and k are rounded once to fp16 (11-bit
@@ -141,10 +143,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // LDS swizzles.  K and V tiles are row-major (64 bytes per key); the 16-byte chunk index
 // of a row is XORed with a few bits of the key so that the lanes served in one LDS cycle
 // hit distinct banks.  K: the eight keys 8j + 4b + {0..3} (j = 0, 1) read by one group of
-// eight lanes.  V: the four keys of one transposed read group.  Bias factor tile (32 bytes
-// per key): the 16-byte half index is XORed with bit 3 of the key.
+// eight lanes.  V: a transposed 8-byte read serves 32 lanes per cycle, lane groups g = 0
+// and g = 1 reading keys 8 apart that would otherwise share 32 of the 64 banks; flipping
+// bit 1 of the chunk index with bit 3 of the key sends them to the other half.  Bias
+// factor tile (32 bytes per key): the 16-byte half index is XORed with bit 3 of the key.
 __device__ __forceinline__ int kswz(int key) { return ((key >> 1) & 1) | (((key >> 3) & 1) << 1); }
-__device__ __forceinline__ int vswz(int key) { return ((key >> 1) & 1) << 1; }
+__device__ __forceinline__ int vswz(int key) { return ((key >> 3) & 1) << 1; }
 __device__ __forceinline__ int bswz(int key) { return (key >> 3) & 1; }
 
 struct Task {
@@ -511,7 +515,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
         }
         const bool first = (tile == 0) && (st == 0);
         uint32_t Pp[2][4];
-        float ls[2] = {0.f, 0.f};
+        float ln[2];  // this lane's share of the row sum after the step
         bool exact = first;
         if (!first) {
 #pragma unroll
@@ -522,10 +526,10 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
               const int e0 = 2 * (t & 1);
               Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0]), __builtin_amdgcn_exp2f(s[e0 + 1]));
             }
-            ls[a] = dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, 0.f)) +
-                    dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, 0.f));
+            ln[a] = dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, l[a]))));
           }
-          exact = __any(fmaxf(ls[0], ls[1]) > RESCALE_LIMIT);
+          // the step's own sum (all p >= 0): above the limit iff some p is near or above it
+          exact = __any(fmaxf(ln[0] - l[0], ln[1] - l[1]) > RESCALE_LIMIT);
         }
         if (exact) {
 #pragma unroll
@@ -548,13 +552,12 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
               const int e0 = 2 * (t & 1);
               Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0] - delta), __builtin_amdgcn_exp2f(s[e0 + 1] - delta));
             }
-            ls[a] = dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, 0.f)) +
-                    dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, 0.f));
+            ln[a] = dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, l[a]))));
           }
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-          l[a] += ls[a];
+          l[a] = ln[a];
           const u32x4 Pa = {Pp[a][0], Pp[a][1], Pp[a][2], Pp[a][3]};  // keys kb + 8g .. 8g+7 of query 16a + c
 #pragma unroll
           for (int db = 0; db < 2; ++db) O[db][a] = mfma16_bf16(cur.V[db], Pa, O[db][a]);
