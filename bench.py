@@ -31,6 +31,8 @@ WARMUP_MAX_STEPS = 20000
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SRC = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "csrc", "wattn_kernels.hip")
+PIPE_RATES = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "pipe_rates")
+MFMA_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 / _f16
 
 
 def parse():
@@ -62,6 +64,40 @@ def traffic_from_profiles(workload: str, out_dtype: str):
     if rec.get("kernel_sha") != kernel_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def pipe_bound(exps: float, mfma_flops: float, kernel_s: float):
+    """Least time the workload's exponentials and matrix products take on this GPU.
+
+    Runs the pipe_rates program (built with the library) as a child process; it times the
+    v_exp_f32 and 16x16x32 MFMA rates per SIMD.  Every executed (query, key) pair costs one
+    exponential; the products cost mfma_flops.  Returns None if the program is missing or fails.
+    """
+    import subprocess
+
+    if not os.path.exists(PIPE_RATES):
+        return None
+    try:
+        res = subprocess.run([PIPE_RATES], capture_output=True, text=True, timeout=120)
+        rates = json.loads(res.stdout.strip().splitlines()[-1]) if res.returncode == 0 else None
+    except Exception:
+        rates = None
+    if not rates:
+        return None
+    ns = rates["ns_per_instruction"]
+    simds = rates["simds"]
+    t_exp = exps / 64.0 * ns["exp_f32"] / simds * 1e-3          # us, 64 lanes per instruction
+    t_mfma = mfma_flops / MFMA_FLOPS * ns["mfma_f32_16x16x32_bf16"] / simds * 1e-3
+    return {
+        "source": "vision_transformer_windowed_window_amd/pipe_rates",
+        "ns_per_instruction": ns,
+        "exp_us": t_exp,
+        "mfma_us": t_mfma,
+        "kernel_us": kernel_s * 1e6,
+        "kernel_vs_exp_plus_mfma": (t_exp + t_mfma) / (kernel_s * 1e6),
+        "mfma_fma_split_vs_serial": rates["split_mfma_fma_ns_per_iteration"] / rates["serial_mfma_fma_ns_per_iteration"],
+        "mfma_exp_interleaved_vs_serial": rates["interleaved_4mfma_16exp_ns"] / rates["serial_4mfma_16exp_ns"],
+    }
 
 
 def cpu_baseline(cfg, budget_s: float):
@@ -224,6 +260,7 @@ def main():
         "peak_extra_device_bytes": int(peak_extra),
         "roofline": roof,
     }
+    rec["pipe_bound"] = pipe_bound(float(pairs), executed, avg_kern_s)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -1,4 +1,4 @@
-"""Build libwattn.so in-tree with hipcc for gfx950.
+"""Build libwattn.so and the pipe_rates program in-tree with hipcc for gfx950.
 
 Usage: python -m vision_transformer_windowed_window_amd.build
 """
@@ -16,6 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwattn.so")
+PIPE_RATES = os.path.join(PKG, "pipe_rates")  # instruction-rate probe run by bench.py
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -42,7 +43,7 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/ into libwattn.so next to this file and return its path."""
+    """Compile csrc/ into libwattn.so and pipe_rates next to this file; return the library path."""
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="wattn_build_") as tmp:
         kobj = os.path.join(tmp, "wattn_kernels.o")
@@ -56,6 +57,11 @@ def build(verbose: bool = False) -> str:
         _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", out_tmp], verbose)
         shutil.move(out_tmp, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
+        exe_tmp = os.path.join(tmp, "pipe_rates")
+        _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, os.path.join(CSRC, "pipe_rates.hip"),
+              "-o", exe_tmp], verbose)
+        shutil.move(exe_tmp, PIPE_RATES + ".tmp")
+        os.replace(PIPE_RATES + ".tmp", PIPE_RATES)
     return LIB
 
 

@@ -234,6 +234,10 @@ __device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt,
   rm = (int)(i - qq * X.den);
 }
 
+// Row stride (entries) of the cos/sin table for the window sides each width serves (up to 18, 26
+// and 128); 32 * stride bytes is 64 mod 256, so the four chunks of a key read distinct banks.
+__host__ __device__ constexpr int table_stride(int NW) { return NW == 2 ? 18 : (NW == 4 ? 26 : 130); }
+
 // NW waves per workgroup (2, 4 or 8): 32 NW queries, key tiles of 16 NW keys.
 template <int NW, int NKS, bool ROPE, bool OUTF32>
 __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
@@ -251,7 +255,8 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
-  extern __shared__ float2 sTab[];  // 16 x M cos/sin entries of the head, pair-major (dynamic size)
+  constexpr int TSTR = table_stride(NW);
+  extern __shared__ float2 sTab[];  // 16 rows of TSTR cos/sin entries of the head, pair-major (dynamic size)
 
   const int tid = threadIdx.x;
   Task T0;
@@ -301,13 +306,13 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       if (tab_thread) {
         float sn, cs;
         __sincosf((float)(tid >> 4) * th, &sn, &cs);
-        sTab[(tid & 15) * M + (tid >> 4)] = make_float2(cs, sn);
+        sTab[(tid & 15) * TSTR + (tid >> 4)] = make_float2(cs, sn);
       }
       for (int i = tid + NTHR; i < M * (D / 2); i += NTHR) {  // the entries beyond one per thread
         const int pos = i >> 4, j = i & 15;
         float sn, cs;
         __sincosf((float)pos * theta[Y.t.h * (D / 2) + j], &sn, &cs);
-        sTab[j * M + pos] = make_float2(cs, sn);
+        sTab[j * TSTR + pos] = make_float2(cs, sn);
       }
     }
   };
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       for (int p = 0; p < 4; ++p) {
         float x0 = bf_lo(qraw[a][p]), x1 = bf_hi(qraw[a][p]);
         if (ROPE) {
-          const float2 t = sTab[(4 * g + p) * M + qpos[a]];
+          const float2 t = sTab[(4 * g + p) * TSTR + qpos[a]];
           const float r0 = x0 * t.x - x1 * t.y;
           const float r1 = x0 * t.y + x1 * t.x;
           x0 = r0;
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float x0 = bf_lo(pk[p]), x1 = bf_hi(pk[p]);
-        const float2 t = sTab[(4 * lch + p) * M + lp];
+        const float2 t = sTab[(4 * lch + p) * TSTR + lp];
         kr[p] = pack_f16(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
       }
     } else {
@@ -762,7 +767,8 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
 template <int NW, int NKS, bool ROPE, bool OUTF32>
 static hipError_t launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
                                    const float* theta, const void* bu, const void* bv, hipStream_t stream) {
-  const size_t table_bytes = ROPE ? (size_t)plan.M * (D / 2) * sizeof(float2) : 0;
+  if (ROPE && plan.M > table_stride(NW)) return hipErrorInvalidValue;
+  const size_t table_bytes = ROPE ? (size_t)table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NW, NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, theta, static_cast<const uint16_t*>(bu),
