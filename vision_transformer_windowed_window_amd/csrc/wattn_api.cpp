@@ -89,15 +89,25 @@ bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
     }
   std::stable_sort(segs, segs + ns, [](const WattnSeg& a, const WattnSeg& b) { return a.rh * a.rw > b.rh * b.rw; });
   int64_t begin = 0;
+  const int ktile = 16 * P.nw;  // keys per LDS tile of the bf16 kernel
   for (int i = 0; i < ns; ++i) {
-    segs[i].task_begin = (int)begin;
-    begin += (int64_t)segs[i].nwy * segs[i].nwx * segs[i].nqt * H * B;
+    WattnSeg& g = segs[i];
+    g.task_begin = (int)begin;
+    begin += (int64_t)g.nwy * g.nwx * g.nqt * H * B;
     if (begin > (1LL << 30)) return false;
-    P.seg[i] = segs[i];
+    g.nqt_r = wattn_recip((uint32_t)g.nqt);
+    g.nwin_r = wattn_recip((uint32_t)(g.nwy * g.nwx));
+    g.nwx_r = wattn_recip((uint32_t)g.nwx);
+    g.step_i = ktile / g.rw;
+    g.step_j = ktile % g.rw;
+    g.rw_magic = g.rw == 1 ? 0u : 0xffffffffu / (uint32_t)g.rw + 1u;
+    P.seg[i] = g;
   }
   P.nseg = ns;
   P.ntasks = (int)begin;
   P.chunk = P.ntasks >= 128 ? 16 : std::max(1, (P.ntasks + 7) / 8);
+  P.H_r = wattn_recip((uint32_t)H);
+  P.chunk_r = wattn_recip((uint32_t)P.chunk);
   const int64_t unit = 8LL * P.chunk;
   P.grid = (int)(((int64_t)P.ntasks + unit - 1) / unit * unit);
   return true;

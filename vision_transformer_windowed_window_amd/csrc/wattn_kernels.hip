@@ -155,15 +155,30 @@ struct Task {
   int b, h, q0;
   int r0, rh, c0, rw;  // region in window-local coordinates
   int y0, x0;          // region origin in the original grid (the region does not wrap)
+  int step_i, step_j;  // one key tile as region rows and columns
+  uint32_t rw_magic;   // multiplier of the index split by rw
 };
 
 // Workgroup -> task.  Groups of `chunk` consecutive tasks (query tiles of one region and
 // head, which share K/V) go to one XCD (workgroups are dealt to the 8 XCDs round-robin), so
 // their K/V lines meet in one L2.  The grid is a multiple of 8 * chunk.
+// x / d and x % d for uniform 0 <= x < 2^31, 1 <= d, with r = recip(d) from the host: the
+// multiply-high under-estimates the quotient by at most one.
+__device__ __forceinline__ void udivmod(uint32_t x, uint32_t d, uint32_t r, uint32_t& q, uint32_t& m) {
+  q = __umulhi(x, r);
+  m = x - q * d;
+  if (m >= d) {
+    q += 1;
+    m -= d;
+  }
+}
+
 __device__ __forceinline__ int task_of_block(const WattnPlan& P, int bid) {
-  const int C = P.chunk;
-  const int xcd = bid & 7, slot = bid >> 3;
-  return ((slot / C) * 8 + xcd) * C + (slot % C);
+  const uint32_t C = (uint32_t)P.chunk;
+  const uint32_t xcd = (uint32_t)bid & 7, slot = (uint32_t)bid >> 3;
+  uint32_t grp, sub;
+  udivmod(slot, C, P.chunk_r, grp, sub);
+  return (int)((grp * 8 + xcd) * C + sub);
 }
 
 __device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, int QT, Task& t) {
@@ -173,21 +188,23 @@ __device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, int QT
   for (int i = 1; i < WATTN_MAX_SEG; ++i)
     if (i < P.nseg && task >= P.seg[i].task_begin) si = i;
   const WattnSeg& S = P.seg[si];  // read on demand (dynamic index), not kept live across tasks
-  int u = task - S.task_begin;
-  const int qt = u % S.nqt;
-  u /= S.nqt;
-  t.h = u % P.H;
-  u /= P.H;
-  const int nw = S.nwy * S.nwx;
-  const int wi = u % nw;
-  t.b = u / nw;
-  const int wy = S.wy0 + wi / S.nwx;
-  const int wx = S.wx0 + wi % S.nwx;
+  uint32_t u = (uint32_t)(task - S.task_begin), qt, h, wi, b, wr, wc;
+  udivmod(u, (uint32_t)S.nqt, S.nqt_r, u, qt);
+  udivmod(u, (uint32_t)P.H, P.H_r, u, h);
+  udivmod(u, (uint32_t)(S.nwy * S.nwx), S.nwin_r, b, wi);
+  udivmod(wi, (uint32_t)S.nwx, S.nwx_r, wr, wc);
+  t.h = (int)h;
+  t.b = (int)b;
+  t.step_i = S.step_i;
+  t.step_j = S.step_j;
+  t.rw_magic = S.rw_magic;
+  const int wy = S.wy0 + (int)wr;
+  const int wx = S.wx0 + (int)wc;
   t.r0 = S.r0;
   t.rh = S.rh;
   t.c0 = S.c0;
   t.rw = S.rw;
-  t.q0 = qt * QT;
+  t.q0 = (int)qt * QT;
   int y = wy * P.M + S.r0 + P.s;
   if (y >= P.Hg) y -= P.Hg;
   int x = wx * P.M + S.c0 + P.s;
@@ -218,12 +235,12 @@ __device__ __forceinline__ TaskCtx make_ctx(const WattnPlan& P, const Task& t, i
   X.img = (int64_t)t.b * P.Hg * rowstride;
   X.regbase = t.y0 * rowstride + t.x0 * colstride + t.h * D;
   X.ntile = (X.n + KT - 1) / KT;
-  X.step_i = KT / t.rw;
-  X.step_j = KT % t.rw;
+  X.step_i = t.step_i;
+  X.step_j = t.step_j;
   X.step_off = X.step_i * rowstride + X.step_j * colstride;
   X.carry_off = rowstride - t.rw * colstride;
   X.den = (uint32_t)t.rw;
-  X.magic = (t.rw == 1) ? 0u : 0xffffffffu / (uint32_t)t.rw + 1u;
+  X.magic = t.rw_magic;
   return X;
 }
 
