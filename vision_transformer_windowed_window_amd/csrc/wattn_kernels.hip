@@ -405,9 +405,10 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
   };
   auto fetch = [&](const TaskCtx& Y, int tile) {
     const bool valid = tile * KT + lk < Y.n;
-    const int off = valid ? koff : klast;
-    pk = *reinterpret_cast<const u32x4*>(k + Y.img + off);
-    pv = *reinterpret_cast<const u32x4*>(v + Y.img + off);
+    // a 32-bit byte offset from the image base (a scalar address): no 64-bit address arithmetic
+    const uint32_t off = (uint32_t)(valid ? koff : klast) * 2u;
+    pk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(k + Y.img) + off);
+    pv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(v + Y.img) + off);
     lpos = (lch < 2) ? (Y.t.r0 + ci) : (Y.t.c0 + cj);
     if (BIAS && bthread) {
       const bool bvalid = tile * KT + bk < Y.n;
