@@ -17,4 +17,6 @@ from .wattn_oracle import (  # noqa: F401
     window_head_output,
     window_attention,
     unmasked_pairs,
+    window_attention_lse,
+    window_attention_backward,
 )

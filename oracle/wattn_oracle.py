@@ -229,3 +229,113 @@ def unmasked_pairs(B, H, Hg, Wg, M, shift) -> int:
             else:
                 total += (M * M) ** 2
     return total * B * H
+
+
+# --------------------------------------------------------------------------------------
+# Row statistic and backward pass (gradients of a scalar loss sum(dout * out))
+# --------------------------------------------------------------------------------------
+
+def window_attention_lse(q, k, M, shift=0, theta=None, bias_u=None, bias_v=None) -> np.ndarray:
+    """Natural-log log-sum-exp of every query row's logits (masked logits excluded):
+    lse[b, y, x, h] = log sum_m exp(S[n, m]) for the query stored at original (y, x)."""
+    q = np.asarray(q)
+    B, Hg, Wg, H, d = q.shape
+    out = np.zeros((B, Hg, Wg, H), dtype=np.float64)
+    th, bu, bv = _f64(theta), _f64(bias_u), _f64(bias_v)
+    for b in range(B):
+        for wy in range(Hg // M):
+            for wx in range(Wg // M):
+                Y, X, y, x, r, c = window_token_coords(Hg, Wg, M, shift, wy, wx)
+                for h in range(H):
+                    S = window_logits(q[b, y, x, h, :], np.asarray(k)[b, y, x, h, :], r, c,
+                                      None if th is None else th[h], None if bu is None else bu[h],
+                                      None if bv is None else bv[h])
+                    if shift > 0:
+                        S = S + shift_mask(Y, X, Hg, Wg, M, shift)
+                    m = np.max(S, axis=-1)
+                    out[b, y, x, h] = m + np.log(np.sum(np.exp(S - m[:, None]), axis=-1))
+    return out
+
+
+def _rope_rotate_back(g: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """Gradient through rope_rotate: the transpose of the rotation (rotate by -ang)."""
+    return rope_rotate(g, -ang)
+
+
+def _pair_cross(g: np.ndarray, xr: np.ndarray) -> np.ndarray:
+    """d(loss)/d(angle) of every (row, pair) for a rotated vector xr with gradient g:
+    the derivative of a rotation by phi is the rotation followed by a quarter turn,
+    (a, b) -> (-b, a), so d/dphi = g . J xr = -g[2j] xr[2j+1] + g[2j+1] xr[2j]."""
+    return -g[..., 0::2] * xr[..., 1::2] + g[..., 1::2] * xr[..., 0::2]
+
+
+def window_attention_backward(q, k, v, dout, M, shift=0, theta=None, bias_u=None, bias_v=None):
+    """Gradients of loss = sum(dout * window_attention(...)) with respect to every input.
+
+    Returns a dict of float64 arrays: dq, dk, dv [B, Hg, Wg, H, d]; dtheta [H, d/2] (or
+    None); dbias_u, dbias_v [H, M*M, r] (or None).  Per window and head it follows the
+    forward steps backwards on the materialised matrices:
+      O = P V, P = softmax(S):        dV = P^T dO,  dP = dO V^T,
+                                      dS = P * (dP - rowsum(dO * O))   (0 where masked),
+      S = s (R q)(R k)^T + U V_b^T:    d(Rq) = s dS (Rk),  d(Rk) = s dS^T (Rq),
+                                      dU = dS V_b,  dV_b = dS^T U,
+      Rq = rotate(q, angle):          dq = rotate(d(Rq), -angle),
+                                      d angle[n, j] = d(Rq)[n] . J (Rq)[n] on pair j,
+      angle[n, j] = pos[n, j] theta[j]: dtheta[j] += pos[n, j] * d angle[n, j]
+    (and the same for k), with s = d^-1/2 and pos the window-local row (first half of
+    the pairs) or column (second half).  The bias factors are shared by all windows and
+    images, so their gradients sum over them.
+    """
+    q = np.asarray(q)
+    B, Hg, Wg, H, d = q.shape
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout, dtype=np.float64)
+    th, bu, bv = _f64(theta), _f64(bias_u), _f64(bias_v)
+    sc = 1.0 / math.sqrt(d)
+    dq = np.zeros((B, Hg, Wg, H, d))
+    dk = np.zeros((B, Hg, Wg, H, d))
+    dv = np.zeros((B, Hg, Wg, H, d))
+    dth = None if th is None else np.zeros_like(th)
+    dbu = None if bu is None else np.zeros_like(bu)
+    dbv = None if bv is None else np.zeros_like(bv)
+    d4 = d // 4
+    for b in range(B):
+        for wy in range(Hg // M):
+            for wx in range(Wg // M):
+                Y, X, y, x, r, c = window_token_coords(Hg, Wg, M, shift, wy, wx)
+                for h in range(H):
+                    qw = np.asarray(q[b, y, x, h, :], dtype=np.float64)
+                    kw = np.asarray(k[b, y, x, h, :], dtype=np.float64)
+                    vw = np.asarray(v[b, y, x, h, :], dtype=np.float64)
+                    go = dout[b, y, x, h, :]
+                    if th is not None:
+                        ang = rope_angles(th[h], r, c)
+                        qr, kr = rope_rotate(qw, ang), rope_rotate(kw, ang)
+                    else:
+                        qr, kr = qw, kw
+                    S = sc * (qr @ kr.T)
+                    if bu is not None:
+                        S = S + bu[h] @ bv[h].T
+                    if shift > 0:
+                        S = S + shift_mask(Y, X, Hg, Wg, M, shift)
+                    P = softmax_rows(S)
+                    O = P @ vw
+                    dP = go @ vw.T
+                    dS = P * (dP - np.sum(go * O, axis=-1, keepdims=True))
+                    dv[b, y, x, h, :] = P.T @ go
+                    dqr = sc * (dS @ kr)
+                    dkr = sc * (dS.T @ qr)
+                    if th is not None:
+                        dq[b, y, x, h, :] = _rope_rotate_back(dqr, ang)
+                        dk[b, y, x, h, :] = _rope_rotate_back(dkr, ang)
+                        dang = _pair_cross(dqr, qr) + _pair_cross(dkr, kr)  # [N, d/2]
+                        pos = np.concatenate([np.repeat(r[:, None], d4, 1), np.repeat(c[:, None], d4, 1)], 1)
+                        dth[h] += np.sum(pos * dang, axis=0)
+                    else:
+                        dq[b, y, x, h, :] = dqr
+                        dk[b, y, x, h, :] = dkr
+                    if bu is not None:
+                        dbu[h] += dS @ bv[h]
+                        dbv[h] += dS.T @ bu[h]
+    return {"dq": dq, "dk": dk, "dv": dv, "dtheta": dth, "dbias_u": dbu, "dbias_v": dbv}
