@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define WATTN_ABI_VERSION 1
+#define WATTN_ABI_VERSION 2
 
 /* Element types.  The bf16 modes run QK^T and PV on bf16 matrix cores with fp32 RoPE,
  * fp32 softmax and fp32 accumulation; they differ only in the type of `out`.  A bf16
@@ -112,6 +112,59 @@ int wattn_forward(const void* q, const void* k, const void* v, void* out,
                   int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
                   const float* theta, const void* bias_u, const void* bias_v, int r,
                   int dtype, void* stream);
+
+/*
+ * wattn_forward_lse -- wattn_forward that also stores the row statistic the backward pass
+ * needs: lse[b][y][x][h] = log sum_m exp(logit[n][m]) (natural log, over the keys the query
+ * sees) for the query token stored at original position (y, x).
+ *
+ * lse : float32 device pointer, [B][Hgrid][Wgrid][H], written (caller-owned).  It must not
+ *       overlap any other argument buffer (WATTN_ERR_ALIAS); NULL gives WATTN_ERR_NULL.
+ * dtype must be WATTN_BF16 or WATTN_BF16_OUT_FP32 (WATTN_ERR_DTYPE otherwise).  All other
+ * arguments, checks and numerics are those of wattn_forward.
+ *
+ * The row statistic is the softmax normaliser of the FLASHSWIN page's fused kernel ("How it
+ * works", first change: online softmax per tile); keeping it makes the backward pass an
+ * exact recomputation of the same softmax.
+ */
+int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                      int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                      const float* theta, const void* bias_u, const void* bias_v, int r,
+                      int dtype, void* stream);
+
+/*
+ * wattn_backward -- gradients of loss = sum(dout * out) of the shifted-window attention
+ * (the FLASHSWIN page's memory claims cover the scores "and their gradient": the backward
+ * pass recomputes P per tile from q, k and lse and never stores an N x N matrix).
+ *
+ * Inputs (device pointers, caller-owned, read only):
+ *   q, k, v : bfloat16 [B][Hgrid][Wgrid][H][d], the forward pass's inputs.
+ *   out     : the forward pass's output, dout: the gradient of the loss with respect to it;
+ *             both [B][Hgrid][Wgrid][H][d], bfloat16 for dtype WATTN_BF16 and float32 for
+ *             WATTN_BF16_OUT_FP32.
+ *   lse     : float32 [B][Hgrid][Wgrid][H] from wattn_forward_lse on the same inputs.
+ *   theta   : float32 [H][d/2] as in the forward pass, or NULL (no RoPE).
+ * Outputs (device pointers, caller-owned, overwritten):
+ *   delta   : float32 [B][Hgrid][Wgrid][H], scratch: rowsum(dout * out) per query.
+ *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
+ *   dtheta  : float32 [H][d/2] (zeroed, then accumulated with atomic adds, so its last bits
+ *             depend on the order of the additions); required iff theta is not NULL.
+ * bias_u, bias_v, r, dbias_u, dbias_v : must be NULL, NULL, 0, NULL, NULL in this version
+ *             (WATTN_ERR_RANK otherwise): the bias gradient is not implemented.
+ * Sizes, shift and d follow wattn_forward.  No output may overlap an input or another
+ * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: a fill kernel for dtheta and two
+ * attention kernels (one per query tile: delta, dq, the q part of dtheta; one per key tile:
+ * dk, dv, the k part of dtheta).
+ *
+ * Numerics: the scores are recomputed as in the forward pass (fp16 operands, P =
+ * exp2(s log2(e) - lse log2(e)) in fp32); P is rounded to bf16 for dv, dS = P (dP - delta)
+ * to fp16 for dq and dk; everything accumulates in fp32.
+ */
+int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta,
+                   int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                   const float* theta, const void* bias_u, const void* bias_v, int r,
+                   float* dbias_u, float* dbias_v, int dtype, void* stream);
 
 /*
  * wattn_pair_count -- number of (query, key) pairs with a finite logit in a call with

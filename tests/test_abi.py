@@ -34,7 +34,8 @@ def _call(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, thet
 def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
-    assert names == {"wattn_forward", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
+    assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_pair_count",
+                     "wattn_status_string", "wattn_abi_version"}
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -96,3 +97,54 @@ def test_pair_count_matches_oracle(B, H, Hg, Wg, M, s):
 def test_pair_count_rejects_bad_sizes():
     assert wattn.pair_count(1, 1, 20, 16, 8, 0) == -1
     assert wattn.pair_count(1, 1, 16, 16, 8, 8) == -1
+
+
+# ---- the row-statistic forward and the backward pass: host-side rejections
+LS, DL, G1, G2, G3, DT = 0x800000, 0x900000, 0xA00000, 0xB00000, 0xC00000, 0xD00000
+
+
+def _call_lse(lse=LS, dtype=0, **kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, theta=None, bu=None, bv=None, r=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_forward_lse(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(lse), a["B"], a["H"],
+                                    a["Hg"], a["Wg"], a["M"], a["s"], a["d"], vp(a["theta"]), vp(a["bu"]),
+                                    vp(a["bv"]), a["r"], dtype, vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(lse=None), 1), (dict(q=None), 1), (dict(dtype=1), 6), (dict(M=0), 2), (dict(s=8), 3),
+        (dict(lse=P1), 7), (dict(lse=P4 + 4), 7), (dict(lse=TH, theta=TH), 7),
+    ],
+)
+def test_forward_lse_rejects_invalid_arguments(kw, status):
+    assert _call_lse(**kw) == status
+
+
+def _call_bwd(**kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, dout=0x480000, lse=LS, delta=DL, dq=G1, dk=G2, dv=G3, dtheta=None, B=1, H=2,
+             Hg=16, Wg=16, M=8, s=0, d=32, theta=None, bu=None, bv=None, r=0, dbu=None, dbv=None, dtype=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_backward(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(a["dout"]), vp(a["lse"]),
+                                 vp(a["delta"]), vp(a["dq"]), vp(a["dk"]), vp(a["dv"]), vp(a["dtheta"]), a["B"],
+                                 a["H"], a["Hg"], a["Wg"], a["M"], a["s"], a["d"], vp(a["theta"]), vp(a["bu"]),
+                                 vp(a["bv"]), a["r"], vp(a["dbu"]), vp(a["dbv"]), a["dtype"], vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), 1), (dict(dout=None), 1), (dict(lse=None), 1), (dict(delta=None), 1), (dict(dq=None), 1),
+        (dict(dk=None), 1), (dict(dv=None), 1), (dict(theta=TH), 1), (dict(dtheta=DT), 1),
+        (dict(B=0), 2), (dict(Hg=20), 2), (dict(s=-1), 3), (dict(d=64), 4),
+        (dict(dtype=1), 6), (dict(dtype=3), 6),
+        (dict(r=16, bu=BU, bv=BV), 5), (dict(dbu=0xE00000), 5),
+        (dict(dq=P1), 7), (dict(dk=G1 + 64), 7), (dict(dv=LS), 7), (dict(delta=G3 + 4), 7),
+        (dict(theta=TH, dtheta=TH), 7), (dict(theta=TH, dtheta=G1), 7),
+    ],
+)
+def test_backward_rejects_invalid_arguments(kw, status):
+    assert _call_bwd(**kw) == status

@@ -1,0 +1,90 @@
+"""GPU parity of the row-statistic forward pass and of the backward pass: the HIP path
+(through the C ABI) against the float64 oracle on the same seeded inputs.
+
+Bounds.  lse: max|err| <= 1e-2 (the forward pass's bound; lse is a log-sum-exp of logits
+that carry the same fp16 operand rounding).  Gradients: relative L2 <= 1e-2 and
+max|err| <= 2e-2 * max|ref| per tensor.  The backward pass rounds three more operands than
+the forward pass (P to bf16 for dv, dS to fp16 for dq and dk, and dout to bf16), each with
+a relative error up to 2^-9 (bf16) or 2^-12 (fp16) per element, and each gradient entry sums
+M^2 such products; twice the forward pass's relative-L2 bound covers them.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from inputs import qkv, round_bf16, theta_table
+from parity_util import errors, note
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX_ABS = 1e-2
+GRAD_REL_L2 = 1e-2
+GRAD_MAX_REL = 2e-2
+
+
+def _setup(B, Hg, Wg, H, M, seed, rope=True, out_f32=True):
+    q, k, v = qkv((B, Hg, Wg, H, 32), seed, "bf16")
+    th = theta_table(H, 32, 0.1, seed + 1) if rope else None
+    rng = np.random.default_rng(seed + 7)
+    dout = rng.normal(size=(B, Hg, Wg, H, 32)).astype(np.float32)
+    if not out_f32:
+        dout = round_bf16(dout)
+    return q, k, v, th, dout
+
+
+def _gpu(q, k, v, th, dout, M, s, out_f32):
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    dev = torch.device("cuda:0")
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    tq, tk, tv = t(q), t(k), t(v)
+    tth = None if th is None else t(th, torch.float32)
+    out, lse = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, out_dtype=odt, return_lse=True)
+    plain = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, out_dtype=odt)
+    dq, dk, dv, dth = wattn.backward(tq, tk, tv, out, t(dout, odt), lse, M=M, shift=s, theta=tth)
+    torch.cuda.synchronize()
+    f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
+    return dict(out=f(out), plain=f(plain), lse=f(lse), dq=f(dq), dk=f(dk), dv=f(dv), dtheta=f(dth))
+
+
+CASES = [
+    # label, B, Hg, Wg, H, M, shift, rope, fp32 out
+    ("m8_s4", 1, 16, 16, 2, 8, 4, True, True),
+    ("m16_s8", 2, 32, 32, 3, 16, 8, True, True),
+    ("m32_s16", 1, 64, 64, 2, 32, 16, True, True),
+    ("m16_s5_ragged", 1, 48, 32, 2, 16, 5, True, True),
+    ("m12_s0_norope", 1, 24, 36, 2, 12, 0, False, True),
+    ("m8_s3_bf16_out", 2, 24, 32, 2, 8, 3, True, False),
+    ("m4_s1", 1, 8, 12, 2, 4, 1, True, True),
+    ("m24_s10", 1, 48, 48, 1, 24, 10, True, True),
+    ("m48_s13", 1, 96, 96, 1, 48, 13, True, True),
+    ("m32_s16_bf16_out", 1, 64, 64, 1, 32, 16, True, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(case):
+    label, B, Hg, Wg, H, M, s, rope, out_f32 = case
+    note(f"backward {label}: B={B} grid={Hg}x{Wg} H={H} M={M} shift={s} rope={rope} fp32_out={out_f32}")
+    q, k, v, th, dout = _setup(B, Hg, Wg, H, M, 900 + M + s, rope, out_f32)
+    got = _gpu(q, k, v, th, dout, M, s, out_f32)
+    # the row-statistic forward pass writes the same output as the plain one, bit for bit
+    assert np.array_equal(got["out"], got["plain"])
+    lse_ref = oracle.window_attention_lse(q, k, M, s, th)
+    lerr, _ = errors(got["lse"], lse_ref)
+    note(f"  lse max|err| {lerr:.3e}")
+    assert lerr <= LSE_MAX_ABS
+    ref = oracle.window_attention_backward(q, k, v, dout, M, s, th)
+    names = ["dq", "dk", "dv"] + (["dtheta"] if rope else [])
+    for name in names:
+        mx, rel = errors(got[name], ref[name])
+        scale = float(np.max(np.abs(ref[name])))
+        note(f"  {name}: max|err| {mx:.3e} (max|ref| {scale:.3e}), rel-L2 {rel:.3e}")
+        assert rel <= GRAD_REL_L2, name
+        assert mx <= GRAD_MAX_REL * scale, name
+    if not rope:
+        assert got["dtheta"] is None

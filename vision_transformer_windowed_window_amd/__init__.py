@@ -7,6 +7,8 @@ kernels of libwattn.so; there is no fallback.  If the library has not been built
 call raises.
 
     out = forward(q, k, v, M=32, shift=16, theta=theta)
+    out, lse = forward(q, k, v, M=32, shift=16, theta=theta, return_lse=True)
+    dq, dk, dv, dtheta = backward(q, k, v, out, dout, lse, M=32, shift=16, theta=theta)
 
 q, k, v: [B, Hgrid, Wgrid, H, 32] contiguous device tensors, bfloat16 or float32.
 theta:   [H, 16] float32 device tensor of rotation-pair frequencies, or None (no RoPE).
@@ -20,6 +22,7 @@ import os
 
 __all__ = [
     "forward",
+    "backward",
     "pair_count",
     "abi_version",
     "status_string",
@@ -77,6 +80,10 @@ def load_library() -> ctypes.CDLL:
     vp, ci = ctypes.c_void_p, ctypes.c_int
     lib.wattn_forward.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, ci, ci, vp]
     lib.wattn_forward.restype = ci
+    lib.wattn_forward_lse.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, vp, vp, vp, ci, ci, vp]
+    lib.wattn_forward_lse.restype = ci
+    lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
+    lib.wattn_backward.restype = ci
     lib.wattn_pair_count.argtypes = [ci] * 6
     lib.wattn_pair_count.restype = ctypes.c_int64
     lib.wattn_status_string.argtypes = [ci]
@@ -105,12 +112,14 @@ def _ptr(t):
 
 
 def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=None, out=None,
-            out_dtype=None, stream=None):
+            out_dtype=None, stream=None, return_lse: bool = False):
     """Shifted-window attention of (q, k, v) on the GPU; returns ``out`` ([B, Hg, Wg, H, d]).
 
     ``out_dtype`` (or the dtype of a given ``out``) may be torch.float32 for bfloat16
     inputs; by default the output has the input dtype.  The call is asynchronous on
-    ``stream`` (default: torch's current stream).
+    ``stream`` (default: torch's current stream).  With ``return_lse`` (bfloat16 inputs)
+    it returns ``(out, lse)``, lse being the float32 [B, Hg, Wg, H] natural-log log-sum-exp
+    of every query row that ``backward`` needs.
     """
     import torch
 
@@ -156,10 +165,57 @@ def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=
         raise ValueError("out must be a contiguous device tensor shaped like q")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.wattn_forward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hg, Wg, M, shift, d,
-        _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
+    if return_lse:
+        lse = torch.empty((B, Hg, Wg, H), dtype=torch.float32, device=q.device)
+        st = lib.wattn_forward_lse(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hg, Wg, M, shift, d,
+            _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
+        )
+    else:
+        st = lib.wattn_forward(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, Hg, Wg, M, shift, d,
+            _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
+        )
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return (out, lse) if return_lse else out
+
+
+def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, stream=None):
+    """Gradients of sum(dout * out) for the call ``out, lse = forward(q, k, v, ...,
+    return_lse=True)``; returns float32 ``(dq, dk, dv, dtheta)`` (dtheta is None without
+    theta).  q, k, v are bfloat16; out and dout are both bfloat16 or both float32."""
+    import torch
+
+    lib = load_library()
+    if q.dtype != torch.bfloat16:
+        raise TypeError("backward takes bfloat16 q, k, v")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    if out.dtype != dout.dtype or out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out and dout must both be bfloat16 or both float32")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if t.shape != q.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor shaped like q")
+    B, Hg, Wg, H, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hg, Wg, H) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, Hg, Wg, H] tensor")
+    if theta is not None and (theta.dtype != torch.float32 or tuple(theta.shape) != (H, d // 2)
+                              or not theta.is_contiguous()):
+        raise ValueError(f"theta must be a contiguous float32 [{H}, {d // 2}] tensor")
+    dtype = BF16 if out.dtype == torch.bfloat16 else BF16_OUT_FP32
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = (torch.empty(q.shape, **f32) for _ in range(3))
+    delta = torch.empty((B, Hg, Wg, H), **f32)
+    dtheta = None if theta is None else torch.empty((H, d // 2), **f32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.wattn_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dtheta), B, H, Hg, Wg, M, shift, d, _ptr(theta), None, None, 0, None, None, dtype,
+        ctypes.c_void_p(stream),
     )
     if st != 0:
         raise WattnError(st, status_string(st))
-    return out
+    return dq, dk, dv, dtheta

@@ -13,7 +13,10 @@
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
-                             const void* bv, hipStream_t stream);
+                             const void* bv, float* lse, hipStream_t stream);
+hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
+                            const void* v, const void* out, const void* dout, const float* lse, float* delta,
+                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -71,10 +74,10 @@ int waves_for_window(int M) {
 #endif
 }
 
-bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P) {
+bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P, int nw) {
   P = WattnPlan{};
   P.B = B; P.H = H; P.Hg = Hg; P.Wg = Wg; P.M = M; P.s = s;
-  P.nw = waves_for_window(M);
+  P.nw = nw;
   const int qtile = 32 * P.nw;
   const AxisSplit ay = split_axis(Hg, M, s), ax = split_axis(Wg, M, s);
   WattnSeg segs[WATTN_MAX_SEG];
@@ -132,11 +135,10 @@ int pointer_ok(const void* p, size_t bytes) {
   return WATTN_OK;
 }
 
-}  // namespace
-
-extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Hgrid,
-                             int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
-                             const void* bias_v, int r, int dtype, void* stream) {
+// Forward pass shared by wattn_forward and wattn_forward_lse (lse may be NULL).
+int forward_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hgrid,
+                 int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u, const void* bias_v,
+                 int r, int dtype, void* stream) {
   // ---- argument checks (no HIP call before this block ends)
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return WATTN_ERR_NULL;
   int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
@@ -166,11 +168,19 @@ extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* 
   };
   for (const Range& x : ins)
     if (x.hi > x.lo && overlaps(ro, x)) return WATTN_ERR_ALIAS;
+  const size_t lse_bytes = (size_t)(elems / d) * sizeof(float);
+  if (lse != nullptr) {
+    if (dtype == WATTN_FP32) return WATTN_ERR_DTYPE;
+    const Range rl{reinterpret_cast<uintptr_t>(lse), reinterpret_cast<uintptr_t>(lse) + lse_bytes};
+    if (overlaps(rl, ro)) return WATTN_ERR_ALIAS;
+    for (const Range& x : ins)
+      if (x.hi > x.lo && overlaps(rl, x)) return WATTN_ERR_ALIAS;
+  }
 
   WattnPlan plan;
   WattnF32Plan fplan{};
   if (dtype != WATTN_FP32) {
-    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan)) return WATTN_ERR_SHAPE;
+    if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan, waves_for_window(M))) return WATTN_ERR_SHAPE;
   } else {
     fplan.B = B; fplan.H = H; fplan.Hg = Hgrid; fplan.Wg = Wgrid; fplan.M = M; fplan.s = shift;
     fplan.nwx = Wgrid / M;
@@ -193,14 +203,91 @@ extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* 
     st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
+  if (lse != nullptr && (st = pointer_ok(lse, lse_bytes)) != WATTN_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype != WATTN_FP32)
     e = wattn_launch_bf16(plan, r > 0 ? 3 : 2, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, theta,
-                          bias_u, bias_v, s);
+                          bias_u, bias_v, lse, s);
   else
     e = wattn_launch_f32(fplan, r, q, k, v, out, theta, bias_u, bias_v, s);
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Hgrid,
+                             int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
+                             const void* bias_v, int r, int dtype, void* stream) {
+  return forward_impl(q, k, v, out, nullptr, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype,
+                      stream);
+}
+
+extern "C" int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                                 int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
+                                 const void* bias_u, const void* bias_v, int r, int dtype, void* stream) {
+  if (lse == nullptr) return WATTN_ERR_NULL;
+  return forward_impl(q, k, v, out, lse, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype, stream);
+}
+
+extern "C" int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta, int B,
+                              int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
+                              const void* bias_u, const void* bias_v, int r, float* dbias_u, float* dbias_v,
+                              int dtype, void* stream) {
+  // ---- argument checks (no HIP call before this block ends)
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+      delta == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return WATTN_ERR_NULL;
+  if ((theta == nullptr) != (dtheta == nullptr)) return WATTN_ERR_NULL;
+  int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
+  if (st != WATTN_OK) return st;
+  if (d != 32) return WATTN_ERR_HEAD_DIM;
+  if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
+  // this version has no bias gradient
+  if (r != 0 || bias_u != nullptr || bias_v != nullptr || dbias_u != nullptr || dbias_v != nullptr)
+    return WATTN_ERR_RANK;
+  const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
+  if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
+  if ((int64_t)Hgrid * Wgrid * H * d >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  const size_t tbytes = (size_t)elems * 2;                                    // q, k, v
+  const size_t gbytes = (size_t)elems * (dtype == WATTN_BF16 ? 2 : 4);        // out, dout
+  const size_t fbytes = (size_t)elems * 4;                                    // dq, dk, dv
+  const size_t rbytes = (size_t)(elems / d) * 4;                              // lse, delta
+  const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
+  auto rng = [](const void* p, size_t n) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
+  };
+  const Range ins[7] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
+                        rng(lse, rbytes), rng(theta, th_bytes)};
+  const Range outs[5] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
+                         rng(dtheta, th_bytes)};
+  for (int i = 0; i < 5; ++i) {
+    if (outs[i].hi == outs[i].lo) continue;
+    for (const Range& x : ins)
+      if (x.hi > x.lo && overlaps(outs[i], x)) return WATTN_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (outs[j].hi > outs[j].lo && overlaps(outs[i], outs[j])) return WATTN_ERR_ALIAS;
+  }
+  WattnPlan plan;
+  if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan, std::min(waves_for_window(M), 4))) return WATTN_ERR_SHAPE;
+
+  // ---- device checks
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  const void* ptrs[12] = {q, k, v, out, dout, lse, delta, dq, dk, dv, theta, dtheta};
+  const size_t sizes[12] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes, fbytes,
+                            th_bytes, th_bytes};
+  for (int i = 0; i < 12; ++i) {
+    st = pointer_ok(ptrs[i], sizes[i]);
+    if (st != WATTN_OK) return st;
+  }
+  const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
+                                        lse, delta, dq, dk, dv, dtheta, theta, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 

@@ -77,6 +77,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = 32;          // head dimension of q, k, v
 constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
                                                               const float* __restrict__ theta,
                                                               const uint16_t* __restrict__ bu,
                                                               const uint16_t* __restrict__ bv,
+                                                              float* __restrict__ lse,
                                                               const WattnPlan P) {
   constexpr bool BIAS = (NKS == 3);
   constexpr int NTHR = 64 * NW;  // threads
@@ -612,6 +614,8 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       int li, lj;
       split_idx(X, (uint32_t)iq, li, lj);
       const int64_t off = X.img + X.regbase + li * rowstride + lj * colstride;
+      // natural-log log-sum-exp of the row: m and l are kept in base 2 (log2(e) folded into q)
+      if (lse != nullptr && g == 0) lse[off / D] = (m[a] + __log2f(lt)) * LN2;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const f32x4 o = O[db][a] * inv;
@@ -776,6 +780,541 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
   }
 }
 
+
+// ------------------------------------------------------------------------------------
+// Backward pass (flash-attention style: the scores are recomputed from the row log-sum-exp
+// of the forward pass, never stored).  For one window, head and region, with natural-log
+// logits s = (R q)(R k)^T / sqrt(d), P = exp(s - lse) and the output gradient dO:
+//   D  = rowsum(dO * O),  dP = dO V^T,  dS = P * (dP - D),
+//   dV = P^T dO,  d(Rq) = dS (Rk) / sqrt(d),  d(Rk) = dS^T (Rq) / sqrt(d),
+//   dq = R^T d(Rq),  dk = R^T d(Rk),
+//   dtheta[j] = sum over q and k tokens of pos_j * (g . J x) on rotation pair j, with g the
+//   gradient and x the input of the token (a rotation and the quarter turn J commute).
+// Kernel A owns query tiles and streams the region's K/V tiles (as the forward pass does):
+// it writes D, dq and the q part of dtheta.  Kernel B owns key tiles and streams the
+// region's rotated queries, dO and the per-query statistics: it writes dk, dv and the k
+// part of dtheta.  Both use the same 16x16x32 MFMAs and LDS layouts as the forward pass.
+// ------------------------------------------------------------------------------------
+
+// The backward kernels run 2 waves per workgroup for windows below 12 and 4 waves above, so
+// the 4-wave table serves every window side up to 128.
+__host__ __device__ constexpr int bwd_table_stride(int NW) { return NW == 2 ? 18 : 130; }
+
+// Region walk of one thread's row of a tile: region coordinates (ci, cj) and the element
+// offset of key / query idx + tile * KT, advanced by one tile at a time.
+struct Walker {
+  int ci, cj, off, last;
+};
+
+__device__ __forceinline__ void walker_init(Walker& w, const TaskCtx& Y, int idx, int col, int rowstride,
+                                            int colstride) {
+  split_idx(Y, (uint32_t)idx, w.ci, w.cj);
+  w.off = Y.regbase + w.ci * rowstride + w.cj * colstride + col;
+  int li, lj;
+  split_idx(Y, (uint32_t)(Y.n - 1), li, lj);
+  w.last = Y.regbase + li * rowstride + lj * colstride + col;
+}
+
+__device__ __forceinline__ void walker_advance(Walker& w, const TaskCtx& Y) {
+  w.ci += Y.step_i;
+  w.cj += Y.step_j;
+  w.off += Y.step_off;
+  if (w.cj >= Y.t.rw) {
+    w.cj -= Y.t.rw;
+    w.ci += 1;
+    w.off += Y.carry_off;
+  }
+}
+
+// window-local cos/sin table of head h (pair-major rows of TSTR entries), fp32 angles
+template <int NTHR, int TSTR>
+__device__ __forceinline__ void build_rope_table(float2* sTab, const float* __restrict__ theta, int h, int M,
+                                                 int tid) {
+  for (int i = tid; i < M * (D / 2); i += NTHR) {
+    const int pos = i >> 4, j = i & 15;
+    float sn, cs;
+    __sincosf((float)pos * theta[h * (D / 2) + j], &sn, &cs);
+    sTab[j * TSTR + pos] = make_float2(cs, sn);
+  }
+}
+
+// eight bf16 or fp32 values of a gradient-side tensor (out or dout) as fp32
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float x[8]) {
+  if (F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      x[2 * p] = bf_lo(w[p]);
+      x[2 * p + 1] = bf_hi(w[p]);
+    }
+  }
+}
+
+// un-rotate the gradient of four channels 4t' .. 4t'+3 (two rotation pairs j0, j0 + 1) at a
+// window position and add the pairs' angle-gradient terms pos * (g . J x) to sDth
+template <bool ROPE, int TSTR>
+__device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j0, int pos, const float2* sTab,
+                                             const uint16_t* __restrict__ xsrc, int64_t xoff, float* sDth,
+                                             float out[4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float a = acc[2 * t] * scale, b = acc[2 * t + 1] * scale;
+    if (ROPE) {
+      const float2 cs = sTab[(j0 + t) * TSTR + pos];
+      out[2 * t] = a * cs.x + b * cs.y;       // R^T: rotate back by -phi
+      out[2 * t + 1] = -a * cs.y + b * cs.x;
+    } else {
+      out[2 * t] = a;
+      out[2 * t + 1] = b;
+    }
+  }
+  if (ROPE) {
+    const u32x2 raw = *reinterpret_cast<const u32x2*>(xsrc + xoff);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float x0 = bf_lo(raw[t]), x1 = bf_hi(raw[t]);
+      atomicAdd(&sDth[j0 + t], (float)pos * (out[2 * t + 1] * x0 - out[2 * t] * x1));
+    }
+  }
+}
+
+// ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
+template <int NW, bool ROPE, bool OUTF32>
+__global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
+    const WattnPlan P) {
+  constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
+  constexpr int TSTR = bwd_table_stride(NW);
+  __shared__ __align__(16) uint16_t sK[2][KT * D];
+  __shared__ __align__(16) uint16_t sV[2][KT * D];
+  __shared__ float sDth[D / 2];
+  extern __shared__ float2 sTab[];
+
+  const int tid = threadIdx.x;
+  Task T0;
+  if (!decode_task(P, task_of_block(P, blockIdx.x), QT, T0)) return;
+  const TaskCtx X = make_ctx(P, T0, KT);
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int M = P.M, n = X.n;
+  const int colstride = P.H * D, rowstride = P.Wg * colstride;
+  if (tid < D / 2) sDth[tid] = 0.f;
+
+  // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
+  u32x4 qraw[2], dOf[2];
+  f32x4 CnL[2], CnD[2];
+  int qpos_r[2], qpos_c[2];
+  int64_t qoff[2];
+  bool qvalid[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int iq = X.t.q0 + wave * 32 + 16 * a + c;
+    qvalid[a] = iq < n;
+    int li = 0, lj = 0;
+    if (qvalid[a]) split_idx(X, (uint32_t)iq, li, lj);
+    qpos_r[a] = X.t.r0 + li;
+    qpos_c[a] = X.t.c0 + lj;
+    qoff[a] = X.img + X.regbase + li * rowstride + lj * colstride;
+    float go[8], o[8];
+    float Dp = 0.f, L2 = 0.f;
+    if (qvalid[a]) {
+      qraw[a] = *reinterpret_cast<const u32x4*>(q + qoff[a] + 8 * g);
+      load8<OUTF32>(dout, qoff[a] + 8 * g, go);
+      load8<OUTF32>(out, qoff[a] + 8 * g, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Dp += go[e] * o[e];
+      L2 = lse[qoff[a] / D] * LOG2E;
+    } else {
+      qraw[a] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) go[e] = 0.f;
+    }
+    const float Dn = xsum32(xsum16(Dp));  // the four lanes of query c hold 8 dims each
+    if (qvalid[a] && g == 0) delta[qoff[a] / D] = Dn;
+    CnL[a] = f32x4{-L2, -L2, -L2, -L2};
+    CnD[a] = f32x4{-Dn, -Dn, -Dn, -Dn};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[2 * p], go[2 * p + 1]);
+  }
+
+  // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V)
+  const int lk = tid >> 2, lch = tid & 3;
+  Walker W;
+  walker_init(W, X, lk, 8 * lch, rowstride, colstride);
+  u32x4 pk, pv;
+  int lpos = 0;
+  auto fetch = [&](int tile) {
+    const bool valid = tile * KT + lk < n;
+    const uint32_t off = (uint32_t)(valid ? W.off : W.last) * 2u;
+    pk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(k + X.img) + off);
+    pv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(v + X.img) + off);
+    lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
+  };
+  auto store = [&](int buf) {
+    u32x4 kr;
+    const int lp = min(lpos, M - 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf_lo(pk[p]), x1 = bf_hi(pk[p]);
+      if (ROPE) {
+        const float2 t = sTab[(4 * lch + p) * TSTR + lp];
+        kr[p] = pack_f16(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+      } else {
+        kr[p] = pack_f16(x0, x1);
+      }
+    }
+    *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
+    *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pv;
+  };
+
+  fetch(0);
+  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  __syncthreads();
+  // queries: rotate (fp32), scale by log2(e) / sqrt(d), round to fp16
+  u32x4 Qf[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const float qscale = LOG2E * 0.17677669529663687f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x0 = bf_lo(qraw[a][p]), x1 = bf_hi(qraw[a][p]);
+      if (ROPE) {
+        const int j = 4 * g + p;
+        const float2 t = sTab[j * TSTR + (j < D / 4 ? qpos_r[a] : qpos_c[a])];
+        const float r0 = x0 * t.x - x1 * t.y, r1 = x0 * t.y + x1 * t.x;
+        x0 = r0;
+        x1 = r1;
+      }
+      Qf[a][p] = pack_f16(x0 * qscale, x1 * qscale);
+    }
+  }
+  store(0);
+  walker_advance(W, X);
+  __syncthreads();
+
+  const int krow = 8 * (c >> 2) + (c & 3);
+  const int vrow = 8 * g + (c >> 2);
+  const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
+  f32x4 dQ[2][2];  // [channel block][query block]: channels 16 cb + 4 g + e of query 16 a + c
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) dQ[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bool wave_live = X.t.q0 + wave * 32 < n;
+
+  for (int tile = 0; tile < X.ntile; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < X.ntile;
+    if (more) fetch(tile + 1);
+    if (wave_live) {
+      const int nst = min(KT / 32, (n - tile * KT + 31) / 32);
+#pragma unroll
+      for (int st = 0; st < KT / 32; ++st) {
+        if (st < nst) {
+          const int kb = st * 32, kg = tile * KT + kb;
+          u32x4 Kf[2], Vr[2], KTf[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int key = kb + krow + 4 * b;
+            Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
+            Vr[b] = *reinterpret_cast<const u32x4*>(&sV[buf][key * D + ((g ^ vswz(key)) * 8)]);
+          }
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            u32x2 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = kb + vrow + 4 * hh;
+              h[hh] = lds_read_tr16(&sK[buf][row * D + (((2 * cb + vch) ^ kswz(row)) * 8) + vsub]);
+            }
+            KTf[cb] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+          }
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            f32x4 S[2], G[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              S[b] = mfma16_f16(Kf[b], Qf[a], CnL[a]);  // log2-domain score minus the row statistic
+              G[b] = mfma16_bf16(Vr[b], dOf[a], CnD[a]);  // dP - D
+            }
+            uint32_t dS16[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int b = t >> 1, e0 = 2 * (t & 1);
+              float s0 = S[b][e0], s1 = S[b][e0 + 1];
+              if (kg + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
+              if (kg + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
+              dS16[t] = pack_f16(__builtin_amdgcn_exp2f(s0) * G[b][e0], __builtin_amdgcn_exp2f(s1) * G[b][e0 + 1]);
+            }
+            const u32x4 dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) dQ[cb][a] = mfma16_f16(KTf[cb], dSa, dQ[cb][a]);
+          }
+        }
+      }
+    }
+    if (more) {
+      store(buf ^ 1);
+      walker_advance(W, X);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: dq = R^T (dS K) / sqrt(d), and the q part of dtheta
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (!qvalid[a]) continue;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float r4[4];
+      const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];  // channels 0..15 rotate with the row
+      finish_grad4<ROPE, TSTR>(dQ[cb][a], 0.17677669529663687f, 8 * cb + 2 * g, pos, sTab, q,
+                               qoff[a] + 16 * cb + 4 * g, sDth, r4);
+      *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+    }
+  }
+  if (ROPE) {
+    __syncthreads();
+    if (tid < D / 2) atomicAdd(&dtheta[X.t.h * (D / 2) + tid], sDth[tid]);
+  }
+}
+
+// ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
+template <int NW, bool ROPE, bool OUTF32>
+__global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const void* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
+    const WattnPlan P) {
+  constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
+  constexpr int TSTR = bwd_table_stride(NW);
+  __shared__ __align__(16) uint16_t sQ[2][QTT * D];
+  __shared__ __align__(16) uint16_t sO[2][QTT * D];
+  __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
+  __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
+  __shared__ float sDth[D / 2];
+  extern __shared__ float2 sTab[];
+
+  const int tid = threadIdx.x;
+  Task T0;
+  if (!decode_task(P, task_of_block(P, blockIdx.x), KTW, T0)) return;
+  const TaskCtx X = make_ctx(P, T0, QTT);
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int M = P.M, n = X.n;
+  const int colstride = P.H * D, rowstride = P.Wg * colstride;
+  if (tid < D / 2) sDth[tid] = 0.f;
+
+  // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands
+  u32x4 kraw[2], Vf[2];
+  int kpos_r[2], kpos_c[2];
+  int64_t koffs[2];
+  bool kvalid[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int ik = X.t.q0 + wave * 32 + 16 * a + c;  // the task's tile index counts keys here
+    kvalid[a] = ik < n;
+    int li = 0, lj = 0;
+    if (kvalid[a]) split_idx(X, (uint32_t)ik, li, lj);
+    kpos_r[a] = X.t.r0 + li;
+    kpos_c[a] = X.t.c0 + lj;
+    koffs[a] = X.img + X.regbase + li * rowstride + lj * colstride;
+    if (kvalid[a]) {
+      kraw[a] = *reinterpret_cast<const u32x4*>(k + koffs[a] + 8 * g);
+      Vf[a] = *reinterpret_cast<const u32x4*>(v + koffs[a] + 8 * g);
+    } else {
+      kraw[a] = u32x4{0u, 0u, 0u, 0u};
+      Vf[a] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // ---- query tile loader: thread t owns chunk t % 4 of query t / 4 in q and dO; threads
+  //      0 .. QTT - 1 also stage query t's statistics
+  const int lk = tid >> 2, lch = tid & 3;
+  Walker W, Ws;
+  walker_init(W, X, lk, 8 * lch, rowstride, colstride);
+  walker_init(Ws, X, tid < QTT ? tid : 0, 0, rowstride, colstride);
+  u32x4 pq, po;
+  float pl = 0.f, pd = 0.f;
+  int lpos = 0;
+  auto fetch = [&](int tile) {
+    const bool valid = tile * QTT + lk < n;
+    const int off = valid ? W.off : W.last;
+    pq = *reinterpret_cast<const u32x4*>(q + X.img + off);
+    float go[8];
+    load8<OUTF32>(dout, X.img + off, go);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) po[p] = pack_bf16(go[2 * p], go[2 * p + 1]);
+    lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
+    if (tid < QTT) {
+      const bool sv = tile * QTT + tid < n;
+      const int so = (sv ? Ws.off : Ws.last) / D;
+      pl = -lse[X.img / D + so] * LOG2E;
+      pd = -delta[X.img / D + so];
+    }
+  };
+  auto store = [&](int buf) {
+    u32x4 qr;
+    const int lp = min(lpos, M - 1);
+    const float qscale = LOG2E * 0.17677669529663687f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x0 = bf_lo(pq[p]), x1 = bf_hi(pq[p]);
+      if (ROPE) {
+        const float2 t = sTab[(4 * lch + p) * TSTR + lp];
+        const float r0 = x0 * t.x - x1 * t.y, r1 = x0 * t.y + x1 * t.x;
+        x0 = r0;
+        x1 = r1;
+      }
+      qr[p] = pack_f16(x0 * qscale, x1 * qscale);
+    }
+    *reinterpret_cast<u32x4*>(&sQ[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = qr;
+    *reinterpret_cast<u32x4*>(&sO[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = po;
+    if (tid < QTT) {
+      sL[buf][tid] = pl;
+      sDl[buf][tid] = pd;
+    }
+  };
+
+  fetch(0);
+  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  __syncthreads();
+  u32x4 Kf[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x0 = bf_lo(kraw[a][p]), x1 = bf_hi(kraw[a][p]);
+      if (ROPE) {
+        const int j = 4 * g + p;
+        const float2 t = sTab[j * TSTR + (j < D / 4 ? kpos_r[a] : kpos_c[a])];
+        const float r0 = x0 * t.x - x1 * t.y, r1 = x0 * t.y + x1 * t.x;
+        x0 = r0;
+        x1 = r1;
+      }
+      Kf[a][p] = pack_f16(x0, x1);
+    }
+  }
+  store(0);
+  walker_advance(W, X);
+  walker_advance(Ws, X);
+  __syncthreads();
+
+  const int krow = 8 * (c >> 2) + (c & 3);
+  const int vrow = 8 * g + (c >> 2);
+  const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
+  f32x4 dV[2][2], dK[2][2];  // [dim / channel block][key block]
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      dV[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dK[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  const bool wave_live = X.t.q0 + wave * 32 < n;
+
+  for (int tile = 0; tile < X.ntile; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < X.ntile;
+    if (more) fetch(tile + 1);
+    if (wave_live) {
+      const int nst = min(QTT / 32, (n - tile * QTT + 31) / 32);
+#pragma unroll
+      for (int st = 0; st < QTT / 32; ++st) {
+        if (st < nst) {
+          const int qb = st * 32, qg = tile * QTT + qb;
+          u32x4 Qr[2], Or[2], OT[2], QTf[2];
+          f32x4 CL[2], CD[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int row = qb + krow + 4 * b;
+            Qr[b] = *reinterpret_cast<const u32x4*>(&sQ[buf][row * D + ((g ^ kswz(row)) * 8)]);
+            Or[b] = *reinterpret_cast<const u32x4*>(&sO[buf][row * D + ((g ^ vswz(row)) * 8)]);
+            // statistics of the accumulator rows of this lane: queries qb + 8 g + 4 b + e
+            CL[b] = *reinterpret_cast<const f32x4*>(&sL[buf][qb + 8 * g + 4 * b]);
+            CD[b] = *reinterpret_cast<const f32x4*>(&sDl[buf][qb + 8 * g + 4 * b]);
+          }
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            u32x2 h[2], hq[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = qb + vrow + 4 * hh;
+              h[hh] = lds_read_tr16(&sO[buf][row * D + (((2 * x + vch) ^ vswz(row)) * 8) + vsub]);
+              hq[hh] = lds_read_tr16(&sQ[buf][row * D + (((2 * x + vch) ^ kswz(row)) * 8) + vsub]);
+            }
+            OT[x] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+            QTf[x] = u32x4{hq[0][0], hq[0][1], hq[1][0], hq[1][1]};
+          }
+#pragma unroll
+          for (int a = 0; a < 2; ++a) {
+            f32x4 S[2], G[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              S[b] = mfma16_f16(Qr[b], Kf[a], CL[b]);   // rows: queries, column: key 16 a + c
+              G[b] = mfma16_bf16(Or[b], Vf[a], CD[b]);  // dP - D
+            }
+            uint32_t Pb[4], dS16[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int b = t >> 1, e0 = 2 * (t & 1);
+              float s0 = S[b][e0], s1 = S[b][e0 + 1];
+              if (qg + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
+              if (qg + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
+              const float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+              Pb[t] = pack_bf16(p0, p1);
+              dS16[t] = pack_f16(p0 * G[b][e0], p1 * G[b][e0 + 1]);
+            }
+            const u32x4 Pa = {Pb[0], Pb[1], Pb[2], Pb[3]}, dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              dV[x][a] = mfma16_bf16(OT[x], Pa, dV[x][a]);
+              dK[x][a] = mfma16_f16(QTf[x], dSa, dK[x][a]);
+            }
+          }
+        }
+      }
+    }
+    if (more) {
+      store(buf ^ 1);
+      walker_advance(W, X);
+      walker_advance(Ws, X);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: dv, dk = R^T (dS^T Q~) ln 2, and the k part of dtheta
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if (!kvalid[a]) continue;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      *reinterpret_cast<float4*>(dv + koffs[a] + 16 * x + 4 * g) =
+          make_float4(dV[x][a][0], dV[x][a][1], dV[x][a][2], dV[x][a][3]);
+      float r4[4];
+      const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
+      finish_grad4<ROPE, TSTR>(dK[x][a], LN2, 8 * x + 2 * g, pos, sTab, k, koffs[a] + 16 * x + 4 * g, sDth, r4);
+      *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+    }
+  }
+  if (ROPE) {
+    __syncthreads();
+    if (tid < D / 2) atomicAdd(&dtheta[X.t.h * (D / 2) + tid], sDth[tid]);
+  }
+}
+
+__global__ void wattn_fill_zero_kernel(float* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------
@@ -784,40 +1323,41 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
 
 template <int NW, int NKS, bool ROPE, bool OUTF32>
 static hipError_t launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
-                                   const float* theta, const void* bu, const void* bv, hipStream_t stream) {
+                                   const float* theta, const void* bu, const void* bv, float* lse,
+                                   hipStream_t stream) {
   if (ROPE && plan.M > table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NW, NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, theta, static_cast<const uint16_t*>(bu),
-                     static_cast<const uint16_t*>(bv), plan);
+                     static_cast<const uint16_t*>(bv), lse, plan);
   return hipGetLastError();
 }
 
 template <int NW>
 static hipError_t launch_bf16_nw(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                                  const void* k, const void* v, void* out, const float* theta, const void* bu,
-                                 const void* bv, hipStream_t stream) {
+                                 const void* bv, float* lse, hipStream_t stream) {
   const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: return launch_bf16_inst<NW, 2, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 1: return launch_bf16_inst<NW, 2, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 2: return launch_bf16_inst<NW, 2, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 3: return launch_bf16_inst<NW, 2, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 4: return launch_bf16_inst<NW, 3, false, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 5: return launch_bf16_inst<NW, 3, false, true>(plan, q, k, v, out, theta, bu, bv, stream);
-    case 6: return launch_bf16_inst<NW, 3, true, false>(plan, q, k, v, out, theta, bu, bv, stream);
-    default: return launch_bf16_inst<NW, 3, true, true>(plan, q, k, v, out, theta, bu, bv, stream);
+    case 0: return launch_bf16_inst<NW, 2, false, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 1: return launch_bf16_inst<NW, 2, false, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 2: return launch_bf16_inst<NW, 2, true, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 3: return launch_bf16_inst<NW, 2, true, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 4: return launch_bf16_inst<NW, 3, false, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 5: return launch_bf16_inst<NW, 3, false, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 6: return launch_bf16_inst<NW, 3, true, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    default: return launch_bf16_inst<NW, 3, true, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
   }
 }
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
-                             const void* bv, hipStream_t stream) {
+                             const void* bv, float* lse, hipStream_t stream) {
   switch (plan.nw) {
-    case 2: return launch_bf16_nw<2>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
-    case 4: return launch_bf16_nw<4>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
-    case 8: return launch_bf16_nw<8>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, stream);
+    case 2: return launch_bf16_nw<2>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
+    case 4: return launch_bf16_nw<4>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
+    case 8: return launch_bf16_nw<8>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -836,4 +1376,53 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
   else
     hipLaunchKernelGGL((wattn_fwd_f32_kernel<0>), grid, block, 0, stream, Q, K, V, O, theta, U, W, plan);
   return hipGetLastError();
+}
+
+// ---- backward launchers
+template <int NW, bool ROPE, bool OUTF32>
+static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, const void* out,
+                                  const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
+                                  float* dtheta, const float* theta, hipStream_t stream) {
+  if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
+  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
+  auto Q = static_cast<const uint16_t*>(q);
+  auto K = static_cast<const uint16_t*>(k);
+  auto V = static_cast<const uint16_t*>(v);
+  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
+                     Q, K, V, out, dout, lse, delta, dq, dtheta, theta, plan);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
+                     stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta, plan);
+  return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
+                                const void* v, const void* out, const void* dout, const float* lse, float* delta,
+                                float* dq, float* dk, float* dv, float* dtheta, const float* theta,
+                                hipStream_t stream) {
+  const int sel = (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+  switch (sel) {
+    case 0: return launch_bwd_inst<NW, false, false>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    case 1: return launch_bwd_inst<NW, false, true>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    case 2: return launch_bwd_inst<NW, true, false>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    default: return launch_bwd_inst<NW, true, true>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+  }
+}
+
+hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
+                            const void* v, const void* out, const void* dout, const float* lse, float* delta,
+                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, hipStream_t stream) {
+  if (rope) {
+    const int nth = plan.H * (D / 2);
+    hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((nth + 255) / 256), dim3(256), 0, stream, dtheta, nth);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (plan.nw) {
+    case 2: return launch_bwd_nw<2>(plan, rope, out_f32, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    case 4: return launch_bwd_nw<4>(plan, rope, out_f32, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
