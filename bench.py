@@ -5,11 +5,13 @@ bias channels + QK^T + mask + online softmax + PV + normalise + scatter, all in 
 launch).  Inputs are resident in HBM before timing starts; several input sets are used in
 rotation so that consecutive steps do not find their inputs in the last-level cache.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--out-dtype fp32|bf16]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--out-dtype fp32|bf16] [--pass fwd|bwd]
 
 Prints one JSON line.  The default workload is the dense patch-2 grid at M = 32
 (16 images x 128 x 128 tokens, 3 heads x 32, shift 16), the configuration the headline
-metric is quoted on.
+metric is quoted on.  With --pass bwd a step is one wattn_backward call (dq, dk, dv and
+dtheta of the same workload, given the forward pass's output, its row log-sum-exp and an
+output gradient, all resident), timed the same way.
 """
 
 from __future__ import annotations
@@ -26,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "window-attn tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
+METRIC_BWD = "window-attn backward tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
 WARMUP_MIN_S = 0.5          # untimed back-to-back launches before timing (clock ramp)
 WARMUP_MAX_STEPS = 20000
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd: wattn_forward (the headline); bwd: wattn_backward")
     return ap.parse_args()
 
 
@@ -97,6 +102,33 @@ def pipe_bound(exps: float, mfma_flops: float, kernel_s: float):
         "kernel_vs_exp_plus_mfma": (t_exp + t_mfma) / (kernel_s * 1e6),
         "mfma_fma_split_vs_serial": rates["split_mfma_fma_ns_per_iteration"] / rates["serial_mfma_fma_ns_per_iteration"],
         "mfma_exp_interleaved_vs_serial": rates["interleaved_4mfma_16exp_ns"] / rates["serial_4mfma_16exp_ns"],
+    }
+
+
+def cpu_baseline_bwd(cfg, budget_s: float):
+    """Time the float64 oracle's backward pass on whole images of the same workload."""
+    import numpy as np
+
+    import oracle
+    from inputs import make_inputs
+
+    inp = make_inputs(cfg, batch=1)
+    dout = np.random.default_rng(0).normal(size=inp["q"].shape)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.window_attention_backward(inp["q"], inp["k"], inp["v"], dout, cfg.M, cfg.shift, inp["theta"])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": done * cfg.Hg * cfg.Wg / el,
+        "unit": "tokens/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{done} image(s) of {cfg.Hg}x{cfg.Wg} tokens x {cfg.H} heads, backward of every window, "
+                  f"{el:.1f} s, numpy float64 with materialised scores",
     }
 
 
@@ -155,6 +187,10 @@ def main():
 
     cfg = CONFIGS[args.workload]
     assert cfg.dtype == "bf16", "the benchmark covers the bf16 workloads"
+    if args.which == "bwd" and cfg.r:
+        print("the backward pass has no bias gradient in this version; pick a workload without bias",
+              file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = torch.bfloat16
@@ -179,6 +215,19 @@ def main():
         t = sets[i % len(sets)]
         wattn.forward(t["q"], t["k"], t["v"], M=cfg.M, shift=cfg.shift, theta=theta, bias_u=bu, bias_v=bv,
                       out=t["out"])
+
+    if args.which == "bwd":
+        # forward output, row statistic and a seeded output gradient per set, computed untimed
+        for i, t in enumerate(sets):
+            t["out"], t["lse"] = wattn.forward(t["q"], t["k"], t["v"], M=cfg.M, shift=cfg.shift, theta=theta,
+                                               out_dtype=odt, return_lse=True)
+            g = torch.Generator(device="cpu").manual_seed(100 + i)
+            t["dout"] = torch.randn(t["q"].shape, generator=g).to(odt).to(dev)
+
+        def step(i):  # noqa: F811 -- the backward pass replaces the forward step
+            t = sets[i % len(sets)]
+            wattn.backward(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"], M=cfg.M, shift=cfg.shift,
+                           theta=theta)
 
     # Untimed warm-up: W steps, continued until at least WARMUP_MIN_S seconds of back-to-back
     # launches have run, because the GPU's clocks only reach their sustained level after tens
@@ -213,13 +262,18 @@ def main():
     tokens = cfg.tokens
     value = tokens / (ms_per_step / 1e3)
     avg_kern_s = ev0.elapsed_time(ev1) / args.steps / 1e3
-    dense = cfg.dense_flops()
+    dense = cfg.dense_flops() * (2.5 if args.which == "bwd" else 1.0)  # backward: 5 products vs 2
     pairs = wattn.pair_count(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, cfg.shift)
     d_qk = cfg.d + cfg.r
     executed = 2.0 * pairs * (d_qk + cfg.d)
-    in_bytes = 3 * tokens * cfg.H * cfg.d * 2
-    out_bytes = tokens * cfg.H * cfg.d * (4 if args.out_dtype == "fp32" else 2)
-    alg_bytes = in_bytes + out_bytes
+    osz = 4 if args.out_dtype == "fp32" else 2
+    el = tokens * cfg.H * cfg.d
+    if args.which == "fwd":
+        alg_bytes = 3 * el * 2 + el * osz  # q, k, v read once, out written once
+    else:
+        executed *= 2.5
+        # q, k, v, out, dout and lse read once; dq, dk, dv and the row scratch written once
+        alg_bytes = 3 * el * 2 + 2 * el * osz + tokens * cfg.H * 4 + 3 * el * 4 + tokens * cfg.H * 4
     compute_bound = cfg.N / 2 >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3  # AI vs ridge (FLOP/B)
     if compute_bound:
         achieved = dense / avg_kern_s / 1e12
@@ -229,10 +283,11 @@ def main():
         achieved = alg_bytes / avg_kern_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
-    roof["traffic"] = traffic_from_profiles(args.workload, args.out_dtype)
+    roof["traffic"] = traffic_from_profiles(args.workload if args.which == "fwd" else args.workload + "_bwd",
+                                            args.out_dtype)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -260,9 +315,13 @@ def main():
         "peak_extra_device_bytes": int(peak_extra),
         "roofline": roof,
     }
-    rec["pipe_bound"] = pipe_bound(float(pairs), executed, avg_kern_s)
+    if args.which == "fwd":
+        rec["pipe_bound"] = pipe_bound(float(pairs), executed, avg_kern_s)
+    else:
+        rec["config"]["pass"] = "backward (dq, dk, dv, dtheta; three kernels per step)"
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        rec["cpu_baseline"] = (cpu_baseline(cfg, args.cpu_seconds) if args.which == "fwd"
+                               else cpu_baseline_bwd(cfg, args.cpu_seconds))
     print(json.dumps(rec), flush=True)
 
 
