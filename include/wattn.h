@@ -149,12 +149,16 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
  *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
  *   dtheta  : float32 [H][d/2] (zeroed, then accumulated with atomic adds, so its last bits
  *             depend on the order of the additions); required iff theta is not NULL.
- * bias_u, bias_v, r, dbias_u, dbias_v : must be NULL, NULL, 0, NULL, NULL in this version
- *             (WATTN_ERR_RANK otherwise): the bias gradient is not implemented.
+ *   dbias_u, dbias_v : float32 [H][M*M][r], the gradients of the bias factors (summed over
+ *             every window and image, which share them; zeroed, then accumulated with atomic
+ *             adds); required iff r == 16.
+ * bias_u, bias_v, r : the forward pass's bias factors (bfloat16 [H][M*M][r]) and rank: NULL,
+ *             NULL, 0 or both set with r == 16 (WATTN_ERR_RANK otherwise, also when the
+ *             dbias pointers do not match).
  * Sizes, shift and d follow wattn_forward.  No output may overlap an input or another
- * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: a fill kernel for dtheta and two
- * attention kernels (one per query tile: delta, dq, the q part of dtheta; one per key tile:
- * dk, dv, the k part of dtheta).
+ * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: fill kernels for the accumulated
+ * outputs and two attention kernels (one per query tile: delta, dq, the q part of dtheta,
+ * dbias_u; one per key tile: dk, dv, the k part of dtheta, dbias_v).
  *
  * Numerics: the scores are recomputed as in the forward pass (fp16 operands, P =
  * exp2(s log2(e) - lse log2(e)) in fp32); P is rounded to bf16 for dv, dS = P (dP - delta)

@@ -141,7 +141,9 @@ def _call_bwd(**kw):
         (dict(dk=None), 1), (dict(dv=None), 1), (dict(theta=TH), 1), (dict(dtheta=DT), 1),
         (dict(B=0), 2), (dict(Hg=20), 2), (dict(s=-1), 3), (dict(d=64), 4),
         (dict(dtype=1), 6), (dict(dtype=3), 6),
-        (dict(r=16, bu=BU, bv=BV), 5), (dict(dbu=0xE00000), 5),
+        (dict(r=16, bu=BU, bv=BV), 5), (dict(dbu=0xE00000), 5), (dict(r=8, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5),
+        (dict(r=16, bu=BU, bv=BV, dbu=0xE00000), 5), (dict(r=16, bu=BU, dbu=0xE00000, dbv=0xF00000), 5),
+        (dict(r=16, bu=BU, bv=BV, dbu=G1, dbv=0xF00000), 7), (dict(r=16, bu=BU, bv=BV, dbu=0xE00000, dbv=BV), 7),
         (dict(dq=P1), 7), (dict(dk=G1 + 64), 7), (dict(dv=LS), 7), (dict(delta=G3 + 4), 7),
         (dict(theta=TH, dtheta=TH), 7), (dict(theta=TH, dtheta=G1), 7),
     ],

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from inputs import qkv, round_bf16, theta_table
+from inputs import qkv, rib_factors, round_bf16, theta_table
 from parity_util import errors, note
 
 pytestmark = pytest.mark.gpu
@@ -23,17 +23,20 @@ GRAD_REL_L2 = 1e-2
 GRAD_MAX_REL = 2e-2
 
 
-def _setup(B, Hg, Wg, H, M, seed, rope=True, out_f32=True):
+def _setup(B, Hg, Wg, H, M, seed, rope=True, out_f32=True, r=0):
     q, k, v = qkv((B, Hg, Wg, H, 32), seed, "bf16")
     th = theta_table(H, 32, 0.1, seed + 1) if rope else None
     rng = np.random.default_rng(seed + 7)
     dout = rng.normal(size=(B, Hg, Wg, H, 32)).astype(np.float32)
     if not out_f32:
         dout = round_bf16(dout)
-    return q, k, v, th, dout
+    U = V = None
+    if r:
+        U, V = rib_factors(H, M, r, seed + 2, "bf16")
+    return q, k, v, th, dout, U, V
 
 
-def _gpu(q, k, v, th, dout, M, s, out_f32):
+def _gpu(q, k, v, th, dout, M, s, out_f32, U=None, V=None):
     import torch
 
     import vision_transformer_windowed_window_amd as wattn
@@ -43,12 +46,17 @@ def _gpu(q, k, v, th, dout, M, s, out_f32):
     odt = torch.float32 if out_f32 else torch.bfloat16
     tq, tk, tv = t(q), t(k), t(v)
     tth = None if th is None else t(th, torch.float32)
-    out, lse = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, out_dtype=odt, return_lse=True)
-    plain = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, out_dtype=odt)
-    dq, dk, dv, dth = wattn.backward(tq, tk, tv, out, t(dout, odt), lse, M=M, shift=s, theta=tth)
+    tu = None if U is None else t(U)
+    tvb = None if V is None else t(V)
+    out, lse = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, bias_u=tu, bias_v=tvb, out_dtype=odt,
+                             return_lse=True)
+    plain = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, bias_u=tu, bias_v=tvb, out_dtype=odt)
+    dq, dk, dv, dth, dbu, dbv = wattn.backward(tq, tk, tv, out, t(dout, odt), lse, M=M, shift=s, theta=tth,
+                                               bias_u=tu, bias_v=tvb)
     torch.cuda.synchronize()
     f = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
-    return dict(out=f(out), plain=f(plain), lse=f(lse), dq=f(dq), dk=f(dk), dv=f(dv), dtheta=f(dth))
+    return dict(out=f(out), plain=f(plain), lse=f(lse), dq=f(dq), dk=f(dk), dv=f(dv), dtheta=f(dth),
+                dbias_u=f(dbu), dbias_v=f(dbv))
 
 
 CASES = [
@@ -63,23 +71,28 @@ CASES = [
     ("m24_s10", 1, 48, 48, 1, 24, 10, True, True),
     ("m48_s13", 1, 96, 96, 1, 48, 13, True, True),
     ("m32_s16_bf16_out", 1, 64, 64, 1, 32, 16, True, False),
+    ("m8_s3_bias", 2, 16, 24, 2, 8, 3, True, True, 16),
+    ("m16_s8_bias_bf16_out", 1, 32, 32, 2, 16, 8, True, False, 16),
+    ("m24_s0_bias_norope", 2, 48, 48, 1, 24, 0, False, True, 16),
+    ("m40_s13_bias", 1, 40, 80, 1, 40, 13, True, True, 16),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_matches_oracle(case):
-    label, B, Hg, Wg, H, M, s, rope, out_f32 = case
-    note(f"backward {label}: B={B} grid={Hg}x{Wg} H={H} M={M} shift={s} rope={rope} fp32_out={out_f32}")
-    q, k, v, th, dout = _setup(B, Hg, Wg, H, M, 900 + M + s, rope, out_f32)
-    got = _gpu(q, k, v, th, dout, M, s, out_f32)
+    label, B, Hg, Wg, H, M, s, rope, out_f32 = case[:9]
+    r = case[9] if len(case) > 9 else 0
+    note(f"backward {label}: B={B} grid={Hg}x{Wg} H={H} M={M} shift={s} rope={rope} fp32_out={out_f32} r={r}")
+    q, k, v, th, dout, U, V = _setup(B, Hg, Wg, H, M, 900 + M + s, rope, out_f32, r)
+    got = _gpu(q, k, v, th, dout, M, s, out_f32, U, V)
     # the row-statistic forward pass writes the same output as the plain one, bit for bit
     assert np.array_equal(got["out"], got["plain"])
-    lse_ref = oracle.window_attention_lse(q, k, M, s, th)
+    lse_ref = oracle.window_attention_lse(q, k, M, s, th, U, V)
     lerr, _ = errors(got["lse"], lse_ref)
     note(f"  lse max|err| {lerr:.3e}")
     assert lerr <= LSE_MAX_ABS
-    ref = oracle.window_attention_backward(q, k, v, dout, M, s, th)
-    names = ["dq", "dk", "dv"] + (["dtheta"] if rope else [])
+    ref = oracle.window_attention_backward(q, k, v, dout, M, s, th, U, V)
+    names = ["dq", "dk", "dv"] + (["dtheta"] if rope else []) + (["dbias_u", "dbias_v"] if r else [])
     for name in names:
         mx, rel = errors(got[name], ref[name])
         scale = float(np.max(np.abs(ref[name])))
@@ -88,3 +101,5 @@ def test_backward_matches_oracle(case):
         assert mx <= GRAD_MAX_REL * scale, name
     if not rope:
         assert got["dtheta"] is None
+    if not r:
+        assert got["dbias_u"] is None and got["dbias_v"] is None

@@ -8,7 +8,7 @@ call raises.
 
     out = forward(q, k, v, M=32, shift=16, theta=theta)
     out, lse = forward(q, k, v, M=32, shift=16, theta=theta, return_lse=True)
-    dq, dk, dv, dtheta = backward(q, k, v, out, dout, lse, M=32, shift=16, theta=theta)
+    dq, dk, dv, dtheta, dbias_u, dbias_v = backward(q, k, v, out, dout, lse, M=32, shift=16, theta=theta)
 
 q, k, v: [B, Hgrid, Wgrid, H, 32] contiguous device tensors, bfloat16 or float32.
 theta:   [H, 16] float32 device tensor of rotation-pair frequencies, or None (no RoPE).
@@ -181,10 +181,12 @@ def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=
     return (out, lse) if return_lse else out
 
 
-def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, stream=None):
+def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=None,
+             stream=None):
     """Gradients of sum(dout * out) for the call ``out, lse = forward(q, k, v, ...,
-    return_lse=True)``; returns float32 ``(dq, dk, dv, dtheta)`` (dtheta is None without
-    theta).  q, k, v are bfloat16; out and dout are both bfloat16 or both float32."""
+    return_lse=True)``; returns float32 ``(dq, dk, dv, dtheta, dbias_u, dbias_v)`` (dtheta
+    is None without theta, the bias gradients None without a bias).  q, k, v and the bias
+    factors are bfloat16; out and dout are both bfloat16 or both float32."""
     import torch
 
     lib = load_library()
@@ -204,18 +206,28 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, str
     if theta is not None and (theta.dtype != torch.float32 or tuple(theta.shape) != (H, d // 2)
                               or not theta.is_contiguous()):
         raise ValueError(f"theta must be a contiguous float32 [{H}, {d // 2}] tensor")
+    r = 0
+    if (bias_u is None) != (bias_v is None):
+        raise ValueError("bias_u and bias_v go together")
+    if bias_u is not None:
+        r = bias_u.shape[-1]
+        for name, t in (("bias_u", bias_u), ("bias_v", bias_v)):
+            if tuple(t.shape) != (H, M * M, r) or t.dtype != q.dtype or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [H, M*M, r] bfloat16 device tensor")
     dtype = BF16 if out.dtype == torch.bfloat16 else BF16_OUT_FP32
     f32 = dict(dtype=torch.float32, device=q.device)
     dq, dk, dv = (torch.empty(q.shape, **f32) for _ in range(3))
     delta = torch.empty((B, Hg, Wg, H), **f32)
     dtheta = None if theta is None else torch.empty((H, d // 2), **f32)
+    dbu = None if bias_u is None else torch.empty(bias_u.shape, **f32)
+    dbv = None if bias_v is None else torch.empty(bias_v.shape, **f32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.wattn_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
-        _ptr(dtheta), B, H, Hg, Wg, M, shift, d, _ptr(theta), None, None, 0, None, None, dtype,
-        ctypes.c_void_p(stream),
+        _ptr(dtheta), B, H, Hg, Wg, M, shift, d, _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, _ptr(dbu), _ptr(dbv),
+        dtype, ctypes.c_void_p(stream),
     )
     if st != 0:
         raise WattnError(st, status_string(st))
-    return dq, dk, dv, dtheta
+    return dq, dk, dv, dtheta, dbu, dbv

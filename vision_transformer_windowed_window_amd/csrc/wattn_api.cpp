@@ -16,7 +16,8 @@ hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out
                              const void* bv, float* lse, hipStream_t stream);
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* delta,
-                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, hipStream_t stream);
+                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
+                            const void* bv, float* dbu, float* dbv, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -245,8 +246,10 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
   if (st != WATTN_OK) return st;
   if (d != 32) return WATTN_ERR_HEAD_DIM;
   if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
-  // this version has no bias gradient
-  if (r != 0 || bias_u != nullptr || bias_v != nullptr || dbias_u != nullptr || dbias_v != nullptr)
+  if (r != 0 && r != 16) return WATTN_ERR_RANK;
+  if (r == 0 && (bias_u != nullptr || bias_v != nullptr || dbias_u != nullptr || dbias_v != nullptr))
+    return WATTN_ERR_RANK;
+  if (r == 16 && (bias_u == nullptr || bias_v == nullptr || dbias_u == nullptr || dbias_v == nullptr))
     return WATTN_ERR_RANK;
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
   if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
@@ -256,14 +259,16 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
   const size_t fbytes = (size_t)elems * 4;                                    // dq, dk, dv
   const size_t rbytes = (size_t)(elems / d) * 4;                              // lse, delta
   const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
+  const size_t b_bytes = (size_t)H * M * M * r * 2;   // bias factors (bf16)
+  const size_t db_bytes = (size_t)H * M * M * r * 4;  // their gradients (float32)
   auto rng = [](const void* p, size_t n) {
     return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
   };
-  const Range ins[7] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
-                        rng(lse, rbytes), rng(theta, th_bytes)};
-  const Range outs[5] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
-                         rng(dtheta, th_bytes)};
-  for (int i = 0; i < 5; ++i) {
+  const Range ins[9] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
+                        rng(lse, rbytes), rng(theta, th_bytes), rng(bias_u, b_bytes), rng(bias_v, b_bytes)};
+  const Range outs[7] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
+                         rng(dtheta, th_bytes), rng(dbias_u, db_bytes), rng(dbias_v, db_bytes)};
+  for (int i = 0; i < 7; ++i) {
     if (outs[i].hi == outs[i].lo) continue;
     for (const Range& x : ins)
       if (x.hi > x.lo && overlaps(outs[i], x)) return WATTN_ERR_ALIAS;
@@ -279,15 +284,16 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
     (void)hipGetLastError();
     return WATTN_ERR_HIP;
   }
-  const void* ptrs[12] = {q, k, v, out, dout, lse, delta, dq, dk, dv, theta, dtheta};
-  const size_t sizes[12] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes, fbytes,
-                            th_bytes, th_bytes};
-  for (int i = 0; i < 12; ++i) {
+  const void* ptrs[16] = {q, k, v, out, dout, lse, delta, dq, dk, dv, theta, dtheta, bias_u, bias_v, dbias_u, dbias_v};
+  const size_t sizes[16] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes, fbytes,
+                            th_bytes, th_bytes, b_bytes, b_bytes, db_bytes, db_bytes};
+  for (int i = 0; i < 16; ++i) {
     st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
   const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
-                                        lse, delta, dq, dk, dv, dtheta, theta, static_cast<hipStream_t>(stream));
+                                        lse, delta, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v,
+                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 

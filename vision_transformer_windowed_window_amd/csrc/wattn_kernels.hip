@@ -884,16 +884,17 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 }
 
 // ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
-template <int NW, bool ROPE, bool OUTF32>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
+  __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];  // bias factor v of the keys (fp16)
   __shared__ float sDth[D / 2];
   extern __shared__ float2 sTab[];
 
@@ -907,8 +908,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   if (tid < D / 2) sDth[tid] = 0.f;
 
-  // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
-  u32x4 qraw[2], dOf[2];
+  // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic;
+  //      with a bias, u * log2(e) in channels 0..15 of a zero-padded k = 32 operand
+  u32x4 qraw[2], dOf[2], Qb[2];
   f32x4 CnL[2], CnD[2];
   int qpos_r[2], qpos_c[2];
   int64_t qoff[2];
@@ -938,17 +940,28 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     }
     const float Dn = xsum32(xsum16(Dp));  // the four lanes of query c hold 8 dims each
     if (qvalid[a] && g == 0) delta[qoff[a] / D] = Dn;
+    Qb[a] = u32x4{0u, 0u, 0u, 0u};
+    if (BIAS && qvalid[a] && g < 2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(
+          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 8 * g);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(raw[p]) * LOG2E, bf_hi(raw[p]) * LOG2E);
+    }
     CnL[a] = f32x4{-L2, -L2, -L2, -L2};
     CnD[a] = f32x4{-Dn, -Dn, -Dn, -Dn};
 #pragma unroll
     for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[2 * p], go[2 * p + 1]);
   }
 
-  // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V)
+  // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V; threads 0 .. 2 KT - 1
+  //      also the 16-byte half t % 2 of the bias factor v of key t / 2)
   const int lk = tid >> 2, lch = tid & 3;
-  Walker W;
+  const int bk = (tid % (2 * KT)) >> 1, bch = tid & 1;
+  const bool bthread = BIAS && tid < 2 * KT;
+  Walker W, Wb;
   walker_init(W, X, lk, 8 * lch, rowstride, colstride);
-  u32x4 pk, pv;
+  walker_init(Wb, X, bk, 0, rowstride, colstride);
+  u32x4 pk, pv, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
   auto fetch = [&](int tile) {
     const bool valid = tile * KT + lk < n;
@@ -956,6 +969,10 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     pk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(k + X.img) + off);
     pv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(v + X.img) + off);
     lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
+    if (bthread) {
+      const int key = (tile * KT + bk < n) ? (X.t.r0 + Wb.ci) * M + (X.t.c0 + Wb.cj) : 0;
+      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)X.t.h * M * M + key) * 16 + 8 * bch);
+    }
   };
   auto store = [&](int buf) {
     u32x4 kr;
@@ -972,6 +989,12 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     }
     *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
     *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pv;
+    if (bthread) {
+      u32x4 br;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
+      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = br;
+    }
   };
 
   fetch(0);
@@ -997,16 +1020,20 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
   }
   store(0);
   walker_advance(W, X);
+  walker_advance(Wb, X);
   __syncthreads();
 
   const int krow = 8 * (c >> 2) + (c & 3);
   const int vrow = 8 * g + (c >> 2);
   const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
   f32x4 dQ[2][2];  // [channel block][query block]: channels 16 cb + 4 g + e of query 16 a + c
+  f32x4 dU[2];     // [query block]: bias channels 4 g + e of query 16 a + c
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int a = 0; a < 2; ++a) dQ[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < 2; ++a) {
+    dQ[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dQ[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dU[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const bool wave_live = X.t.q0 + wave * 32 < n;
 
   for (int tile = 0; tile < X.ntile; ++tile) {
@@ -1019,12 +1046,22 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
       for (int st = 0; st < KT / 32; ++st) {
         if (st < nst) {
           const int kb = st * 32, kg = tile * KT + kb;
-          u32x4 Kf[2], Vr[2], KTf[2];
+          u32x4 Kf[2], Vr[2], KTf[2], Kb[2], VbT;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int key = kb + krow + 4 * b;
             Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
             Vr[b] = *reinterpret_cast<const u32x4*>(&sV[buf][key * D + ((g ^ vswz(key)) * 8)]);
+            if (BIAS) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+          }
+          if (BIAS) {  // bias factor v^T: channel c, keys kb + 8 g .. 8 g + 7
+            u32x2 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = kb + vrow + 4 * hh;
+              h[hh] = lds_read_tr16(&sKb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+            }
+            VbT = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
           }
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
@@ -1041,7 +1078,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
             f32x4 S[2], G[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-              S[b] = mfma16_f16(Kf[b], Qf[a], CnL[a]);  // log2-domain score minus the row statistic
+              // log2-domain score minus the row statistic (bias channels first, as in the forward pass)
+              S[b] = BIAS ? mfma16_f16(Kb[b], Qb[a], CnL[a]) : CnL[a];
+              S[b] = mfma16_f16(Kf[b], Qf[a], S[b]);
               G[b] = mfma16_bf16(Vr[b], dOf[a], CnD[a]);  // dP - D
             }
             uint32_t dS16[4];
@@ -1056,6 +1095,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
             const u32x4 dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) dQ[cb][a] = mfma16_f16(KTf[cb], dSa, dQ[cb][a]);
+            if (BIAS) dU[a] = mfma16_f16(VbT, dSa, dU[a]);
           }
         }
       }
@@ -1063,11 +1103,22 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     if (more) {
       store(buf ^ 1);
       walker_advance(W, X);
+      walker_advance(Wb, X);
     }
     __syncthreads();
   }
 
-  // ---- epilogue: dq = R^T (dS K) / sqrt(d), and the q part of dtheta
+  // ---- epilogue: the gradient of the bias factor u (shared by every window and image: added
+  //      into its window position with atomics), dq = R^T (dS K) / sqrt(d), the q part of dtheta
+  if (BIAS) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (!qvalid[a]) continue;
+      float* dst = dbu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dU[a][e]);
+    }
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (!qvalid[a]) continue;
@@ -1087,16 +1138,17 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
-template <int NW, bool ROPE, bool OUTF32>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sQ[2][QTT * D];
   __shared__ __align__(16) uint16_t sO[2][QTT * D];
+  __shared__ __align__(16) uint16_t sUb[BIAS ? 2 : 1][BIAS ? QTT * 16 : 8];  // u * log2(e) of the queries (fp16)
   __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
   __shared__ float sDth[D / 2];
@@ -1112,8 +1164,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   if (tid < D / 2) sDth[tid] = 0.f;
 
-  // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands
-  u32x4 kraw[2], Vf[2];
+  // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands; with a bias, the
+  //      factor v_b in channels 0..15 of a zero-padded k = 32 operand
+  u32x4 kraw[2], Vf[2], Vbf[2];
   int kpos_r[2], kpos_c[2];
   int64_t koffs[2];
   bool kvalid[2];
@@ -1133,15 +1186,25 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       kraw[a] = u32x4{0u, 0u, 0u, 0u};
       Vf[a] = u32x4{0u, 0u, 0u, 0u};
     }
+    Vbf[a] = u32x4{0u, 0u, 0u, 0u};
+    if (BIAS && kvalid[a] && g < 2) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(
+          bv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * 16 + 8 * g);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Vbf[a][p] = pack_f16(bf_lo(raw[p]), bf_hi(raw[p]));
+    }
   }
 
   // ---- query tile loader: thread t owns chunk t % 4 of query t / 4 in q and dO; threads
   //      0 .. QTT - 1 also stage query t's statistics
   const int lk = tid >> 2, lch = tid & 3;
-  Walker W, Ws;
+  const int bk = (tid % (2 * QTT)) >> 1, bch = tid & 1;
+  const bool bthread = BIAS && tid < 2 * QTT;
+  Walker W, Ws, Wb;
   walker_init(W, X, lk, 8 * lch, rowstride, colstride);
   walker_init(Ws, X, tid < QTT ? tid : 0, 0, rowstride, colstride);
-  u32x4 pq, po;
+  walker_init(Wb, X, bk, 0, rowstride, colstride);
+  u32x4 pq, po, pu = {0u, 0u, 0u, 0u};
   float pl = 0.f, pd = 0.f;
   int lpos = 0;
   auto fetch = [&](int tile) {
@@ -1158,6 +1221,10 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       const int so = (sv ? Ws.off : Ws.last) / D;
       pl = -lse[X.img / D + so] * LOG2E;
       pd = -delta[X.img / D + so];
+    }
+    if (bthread) {
+      const int qn = (tile * QTT + bk < n) ? (X.t.r0 + Wb.ci) * M + (X.t.c0 + Wb.cj) : 0;
+      pu = *reinterpret_cast<const u32x4*>(bu + ((int64_t)X.t.h * M * M + qn) * 16 + 8 * bch);
     }
   };
   auto store = [&](int buf) {
@@ -1180,6 +1247,12 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     if (tid < QTT) {
       sL[buf][tid] = pl;
       sDl[buf][tid] = pd;
+    }
+    if (bthread) {
+      u32x4 ur;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ur[p] = pack_f16(bf_lo(pu[p]) * LOG2E, bf_hi(pu[p]) * LOG2E);
+      *reinterpret_cast<u32x4*>(&sUb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = ur;
     }
   };
 
@@ -1205,19 +1278,23 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   store(0);
   walker_advance(W, X);
   walker_advance(Ws, X);
+  walker_advance(Wb, X);
   __syncthreads();
 
   const int krow = 8 * (c >> 2) + (c & 3);
   const int vrow = 8 * g + (c >> 2);
   const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
   f32x4 dV[2][2], dK[2][2];  // [dim / channel block][key block]
+  f32x4 dVb[2];              // [key block]: bias channels 4 g + e of key 16 a + c (times log2(e))
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int a = 0; a < 2; ++a) {
+    dVb[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int x = 0; x < 2; ++x) {
       dV[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
       dK[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  }
   const bool wave_live = X.t.q0 + wave * 32 < n;
 
   for (int tile = 0; tile < X.ntile; ++tile) {
@@ -1230,13 +1307,23 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       for (int st = 0; st < QTT / 32; ++st) {
         if (st < nst) {
           const int qb = st * 32, qg = tile * QTT + qb;
-          u32x4 Qr[2], Or[2], OT[2], QTf[2];
+          u32x4 Qr[2], Or[2], OT[2], QTf[2], Ur[2], UT;
           f32x4 CL[2], CD[2];
+          if (BIAS) {  // bias factor (u log2 e)^T: channel c, queries qb + 8 g .. 8 g + 7
+            u32x2 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = qb + vrow + 4 * hh;
+              h[hh] = lds_read_tr16(&sUb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+            }
+            UT = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+          }
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int row = qb + krow + 4 * b;
             Qr[b] = *reinterpret_cast<const u32x4*>(&sQ[buf][row * D + ((g ^ kswz(row)) * 8)]);
             Or[b] = *reinterpret_cast<const u32x4*>(&sO[buf][row * D + ((g ^ vswz(row)) * 8)]);
+            if (BIAS) Ur[b] = *reinterpret_cast<const u32x4*>(&sUb[buf][row * 16 + 8 * ((g & 1) ^ bswz(row))]);
             // statistics of the accumulator rows of this lane: queries qb + 8 g + 4 b + e
             CL[b] = *reinterpret_cast<const f32x4*>(&sL[buf][qb + 8 * g + 4 * b]);
             CD[b] = *reinterpret_cast<const f32x4*>(&sDl[buf][qb + 8 * g + 4 * b]);
@@ -1258,7 +1345,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
             f32x4 S[2], G[2];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-              S[b] = mfma16_f16(Qr[b], Kf[a], CL[b]);   // rows: queries, column: key 16 a + c
+              // rows: queries, column: key 16 a + c (bias channels first, as in the forward pass)
+              S[b] = BIAS ? mfma16_f16(Ur[b], Vbf[a], CL[b]) : CL[b];
+              S[b] = mfma16_f16(Qr[b], Kf[a], S[b]);
               G[b] = mfma16_bf16(Or[b], Vf[a], CD[b]);  // dP - D
             }
             uint32_t Pb[4], dS16[4];
@@ -1278,6 +1367,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
               dV[x][a] = mfma16_bf16(OT[x], Pa, dV[x][a]);
               dK[x][a] = mfma16_f16(QTf[x], dSa, dK[x][a]);
             }
+            if (BIAS) dVb[a] = mfma16_f16(UT, dSa, dVb[a]);
           }
         }
       }
@@ -1286,8 +1376,21 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       store(buf ^ 1);
       walker_advance(W, X);
       walker_advance(Ws, X);
+      walker_advance(Wb, X);
     }
     __syncthreads();
+  }
+
+  // ---- the gradient of the bias factor v_b (shared by every window and image: added into its
+  //      window position with atomics; the u tile carried log2(e))
+  if (BIAS) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (!kvalid[a]) continue;
+      float* dst = dbv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * 16 + 4 * g;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dVb[a][e] * LN2);
+    }
   }
 
   // ---- epilogue: dv, dk = R^T (dS^T Q~) ln 2, and the k part of dtheta
@@ -1379,50 +1482,69 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
 }
 
 // ---- backward launchers
-template <int NW, bool ROPE, bool OUTF32>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS>
 static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, const void* out,
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
-                                  float* dtheta, const float* theta, hipStream_t stream) {
+                                  float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
+                                  float* dbv, hipStream_t stream) {
   if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
   auto K = static_cast<const uint16_t*>(k);
   auto V = static_cast<const uint16_t*>(v);
-  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
-                     Q, K, V, out, dout, lse, delta, dq, dtheta, theta, plan);
+  auto BU = static_cast<const uint16_t*>(bu);
+  auto BV = static_cast<const uint16_t*>(bv);
+  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes,
+                     stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
-                     stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta, plan);
+  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes,
+                     stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv,
+                     plan);
   return hipGetLastError();
 }
 
 template <int NW>
-static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
-                                const void* v, const void* out, const void* dout, const float* lse, float* delta,
-                                float* dq, float* dk, float* dv, float* dtheta, const float* theta,
-                                hipStream_t stream) {
-  const int sel = (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, bool bias, const void* q,
+                                const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                                float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
+                                const void* bu, const void* bv, float* dbu, float* dbv, hipStream_t stream) {
+#define WATTN_BWD_ARGS plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, stream
+  const int sel = (bias ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: return launch_bwd_inst<NW, false, false>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
-    case 1: return launch_bwd_inst<NW, false, true>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
-    case 2: return launch_bwd_inst<NW, true, false>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
-    default: return launch_bwd_inst<NW, true, true>(plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    case 0: return launch_bwd_inst<NW, false, false, false>(WATTN_BWD_ARGS);
+    case 1: return launch_bwd_inst<NW, false, true, false>(WATTN_BWD_ARGS);
+    case 2: return launch_bwd_inst<NW, true, false, false>(WATTN_BWD_ARGS);
+    case 3: return launch_bwd_inst<NW, true, true, false>(WATTN_BWD_ARGS);
+    case 4: return launch_bwd_inst<NW, false, false, true>(WATTN_BWD_ARGS);
+    case 5: return launch_bwd_inst<NW, false, true, true>(WATTN_BWD_ARGS);
+    case 6: return launch_bwd_inst<NW, true, false, true>(WATTN_BWD_ARGS);
+    default: return launch_bwd_inst<NW, true, true, true>(WATTN_BWD_ARGS);
   }
+#undef WATTN_BWD_ARGS
 }
 
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* delta,
-                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, hipStream_t stream) {
-  if (rope) {
-    const int nth = plan.H * (D / 2);
-    hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((nth + 255) / 256), dim3(256), 0, stream, dtheta, nth);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                            float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
+                            const void* bv, float* dbu, float* dbv, hipStream_t stream) {
+  const bool bias = bu != nullptr;
+  auto fill = [&](float* p, int64_t cnt) {
+    hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, p,
+                       (int)cnt);
+    return hipGetLastError();
+  };
+  hipError_t e = hipSuccess;
+  if (rope && (e = fill(dtheta, (int64_t)plan.H * (D / 2))) != hipSuccess) return e;
+  if (bias) {
+    const int64_t cnt = (int64_t)plan.H * plan.M * plan.M * 16;
+    if ((e = fill(dbu, cnt)) != hipSuccess || (e = fill(dbv, cnt)) != hipSuccess) return e;
   }
   switch (plan.nw) {
-    case 2: return launch_bwd_nw<2>(plan, rope, out_f32, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
-    case 4: return launch_bwd_nw<4>(plan, rope, out_f32, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, stream);
+    case 2: return launch_bwd_nw<2>(plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta,
+                                    theta, bu, bv, dbu, dbv, stream);
+    case 4: return launch_bwd_nw<4>(plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta,
+                                    theta, bu, bv, dbu, dbv, stream);
     default: return hipErrorInvalidValue;
   }
 }
