@@ -59,6 +59,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 
 #include "wattn_plan.h"
 
@@ -885,7 +887,7 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 
 // ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
 template <int NW, bool ROPE, bool OUTF32, bool BIAS>
-__global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
@@ -1041,11 +1043,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
     const bool more = tile + 1 < X.ntile;
     if (more) fetch(tile + 1);
     if (wave_live) {
-      const int nst = min(KT / 32, (n - tile * KT + 31) / 32);
-#pragma unroll
-      for (int st = 0; st < KT / 32; ++st) {
-        if (st < nst) {
-          const int kb = st * 32, kg = tile * KT + kb;
+      // one 32-key block; MASK: the region's last, partial block, whose padded keys get -inf
+      auto kblock = [&](int kb, int kg, auto mask_tag) {
+          constexpr bool MASK = decltype(mask_tag)::value;
           u32x4 Kf[2], Vr[2], KTf[2], Kb[2], VbT;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
@@ -1088,8 +1088,10 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
             for (int t = 0; t < 4; ++t) {
               const int b = t >> 1, e0 = 2 * (t & 1);
               float s0 = S[b][e0], s1 = S[b][e0 + 1];
-              if (kg + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
-              if (kg + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
+              if (MASK) {
+                if (kg + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
+                if (kg + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
+              }
               dS16[t] = pack_f16(__builtin_amdgcn_exp2f(s0) * G[b][e0], __builtin_amdgcn_exp2f(s1) * G[b][e0 + 1]);
             }
             const u32x4 dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
@@ -1097,7 +1099,14 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dq_kernel(
             for (int cb = 0; cb < 2; ++cb) dQ[cb][a] = mfma16_f16(KTf[cb], dSa, dQ[cb][a]);
             if (BIAS) dU[a] = mfma16_f16(VbT, dSa, dU[a]);
           }
-        }
+      };
+#pragma unroll
+      for (int st = 0; st < KT / 32; ++st) {
+        const int kb = st * 32, kg = tile * KT + kb;
+        if (kg + 32 <= n)
+          kblock(kb, kg, std::false_type{});
+        else if (kg < n)
+          kblock(kb, kg, std::true_type{});
       }
     }
     if (more) {
@@ -1219,7 +1228,8 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     if (tid < QTT) {
       const bool sv = tile * QTT + tid < n;
       const int so = (sv ? Ws.off : Ws.last) / D;
-      pl = -lse[X.img / D + so] * LOG2E;
+      // a padded query gets the statistic +inf: its scores become -inf, so P = dS = 0
+      pl = sv ? -lse[X.img / D + so] * LOG2E : -INFINITY;
       pd = -delta[X.img / D + so];
     }
     if (bthread) {
@@ -1306,7 +1316,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
 #pragma unroll
       for (int st = 0; st < QTT / 32; ++st) {
         if (st < nst) {
-          const int qb = st * 32, qg = tile * QTT + qb;
+          const int qb = st * 32;
           u32x4 Qr[2], Or[2], OT[2], QTf[2], Ur[2], UT;
           f32x4 CL[2], CD[2];
           if (BIAS) {  // bias factor (u log2 e)^T: channel c, queries qb + 8 g .. 8 g + 7
@@ -1354,10 +1364,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const int b = t >> 1, e0 = 2 * (t & 1);
-              float s0 = S[b][e0], s1 = S[b][e0 + 1];
-              if (qg + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
-              if (qg + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
-              const float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+              const float p0 = __builtin_amdgcn_exp2f(S[b][e0]), p1 = __builtin_amdgcn_exp2f(S[b][e0 + 1]);
               Pb[t] = pack_bf16(p0, p1);
               dS16[t] = pack_f16(p0 * G[b][e0], p1 * G[b][e0 + 1]);
             }
