@@ -14,4 +14,8 @@ from .generate import (  # noqa: F401
     theta_table,
     rib_factors,
     make_inputs,
+    GatedConfig,
+    GATED_CONFIGS,
+    block_gate,
+    make_gated_inputs,
 )

@@ -21,6 +21,10 @@ Learned-parameter inputs:
 * ``rib_factors``: the rank-r bias factors U, V of the RIB page (section 2.1): window-local
   token coordinates -> Fourier features -> small seeded MLP -> (U, V).  This is an input
   generator, not part of what the operator computes.
+* ``block_gate``: per-block gate values in [0, 1] for the gated local path (HSMLA page,
+  section 2: a learned gate per spatial block, about 30% of the blocks above the threshold).
+  The gate network itself is a learned model part; the synthetic gates are i.i.d. uniform,
+  so a threshold tau selects a fraction 1 - tau of the blocks in expectation.
 """
 
 from __future__ import annotations
@@ -179,6 +183,52 @@ def rib_factors(H: int, M: int, r: int, seed: int, dtype: str = "bf16", n_freq: 
     if dtype == "bf16":
         U, V = round_bf16(U), round_bf16(V)
     return U, V
+
+
+@dataclasses.dataclass(frozen=True)
+class GatedConfig:
+    """A workload of the gated local path: the token grid, heads, window w, threshold tau
+    and the denominator guard eps of the linear attention."""
+    name: str
+    B: int
+    Hg: int
+    Wg: int
+    H: int
+    d: int
+    w: int
+    tau: float
+    eps: float
+    seed: int           # q/k/v use seed, the gate seed+3000, the base output seed+4000
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.Hg * self.Wg
+
+    @property
+    def blocks(self) -> int:
+        return self.B * (self.Hg // self.w) * (self.Wg // self.w)
+
+
+# The dense patch-2 grid with 8x8 and 16x16 local windows, 30% of the blocks selected.
+GATED_CONFIGS = {
+    "gated_p2_w8": GatedConfig("gated_p2_w8", 16, 128, 128, 3, 32, 8, 0.7, 1e-6, 1006),
+    "gated_p2_w16": GatedConfig("gated_p2_w16", 16, 128, 128, 3, 32, 16, 0.7, 1e-6, 1006),
+}
+
+
+def block_gate(B: int, nWy: int, nWx: int, seed: int) -> np.ndarray:
+    """Gate values in [0, 1) per block, [B][nWy][nWx] float32, i.i.d. uniform."""
+    return _rng(seed).random(size=(B, nWy, nWx), dtype=np.float32)
+
+
+def make_gated_inputs(cfg: GatedConfig, batch: int | None = None):
+    """q, k, v (bf16-exact float32), the block gate and a base output ~ N(0, 1) (float32)."""
+    B = cfg.B if batch is None else batch
+    shape = (B, cfg.Hg, cfg.Wg, cfg.H, cfg.d)
+    q, k, v = qkv(shape, cfg.seed, "bf16")
+    gate = block_gate(B, cfg.Hg // cfg.w, cfg.Wg // cfg.w, cfg.seed + 3000)
+    base = _rng(cfg.seed + 4000).standard_normal(size=shape, dtype=np.float32)
+    return dict(q=q, k=k, v=v, gate=gate, base=base)
 
 
 def make_inputs(cfg: WorkloadConfig, batch: int | None = None, shared_theta: bool = True):

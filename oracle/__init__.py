@@ -20,3 +20,13 @@ from .wattn_oracle import (  # noqa: F401
     window_attention_lse,
     window_attention_backward,
 )
+from .hsmla_oracle import (  # noqa: F401
+    select_blocks,
+    block_origin,
+    relu_linear_attention,
+    softmax_attention,
+    local_residual_window,
+    local_residual,
+    gated_local_path,
+    global_linear_attention,
+)
