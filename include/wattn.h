@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define WATTN_ABI_VERSION 2
+#define WATTN_ABI_VERSION 3
 
 /* Element types.  The bf16 modes run QK^T and PV on bf16 matrix cores with fp32 RoPE,
  * fp32 softmax and fp32 accumulation; they differ only in the type of `out`.  A bf16
@@ -68,10 +68,12 @@ typedef enum {
   WATTN_ERR_DTYPE = 6,    /* unknown dtype enum */
   WATTN_ERR_ALIAS = 7,    /* out overlaps an input buffer */
   WATTN_ERR_HIP = 8,      /* HIP runtime error (no device, launch failure, ...) */
-  WATTN_ERR_POINTER = 9   /* a buffer is not device-accessible memory */
+  WATTN_ERR_POINTER = 9,  /* a buffer is not device-accessible memory */
+  WATTN_ERR_VALUE = 10    /* a scalar parameter out of range (eps of the gated local path) */
 } wattn_status_t;
 
 #define WATTN_MAX_M 128
+#define WATTN_MAX_BLOCKS (1 << 22) /* blocks of one gated-local-path call */
 
 /*
  * wattn_forward -- out = shifted-window attention of (q, k, v); see the header comment.
@@ -169,6 +171,62 @@ int wattn_backward(const void* q, const void* k, const void* v, const void* out,
                    int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
                    const float* theta, const void* bias_u, const void* bias_v, int r,
                    float* dbias_u, float* dbias_v, int dtype, void* stream);
+
+/*
+ * Gated local path of hybrid linear/softmax attention (HSMLA: Hierarchical Softmax
+ * Multi-scale Linear Attention for Efficient Vision Transformers, technical summary section 2).
+ * The global path is ReLU linear attention over all tokens; a learned gate shared by the heads
+ * scores every spatial block, and only the blocks whose gate exceeds a threshold tau are routed
+ * to a local softmax path inside a small w x w window, whose output becomes the global output
+ * plus the residual R = O_local - O_lin-local.  Blocks are the w x w windows of the unshifted
+ * grid, numbered blk = b * (Hgrid/w) * (Wgrid/w) + wy * (Wgrid/w) + wx.
+ */
+
+/*
+ * wattn_select_blocks -- routing: list the blocks whose gate value exceeds tau.
+ *
+ * gate   : float32 device pointer, [nblocks] gate values (the gate network's M_b per block,
+ *          in block order); read only.  A NaN gate is never selected; the comparison is
+ *          strict (gate == tau is not selected).
+ * nblocks: 1 .. WATTN_MAX_BLOCKS (WATTN_ERR_SHAPE otherwise).
+ * list   : int32 device pointer, capacity nblocks; receives the selected block indices in
+ *          ascending order in list[0 .. *count).  Entries past the count are left as they were.
+ * count  : int32 device pointer to one element; receives the number selected.
+ * None of gate, list and count may overlap (WATTN_ERR_ALIAS).  One workgroup launched on
+ * `stream`; nothing is allocated.
+ */
+int wattn_select_blocks(const float* gate, int nblocks, float tau, int* list, int* count, void* stream);
+
+/*
+ * wattn_local_residual -- the residual correction of the listed blocks, in place:
+ *
+ *   out[t][h] += O_local[t][h] - O_lin-local[t][h]   for every token t of every listed block
+ *
+ * with, over the keys j of the token's w x w block (scale d^-1/2, no shift, no mask, no RoPE):
+ *   O_local     = sum_j softmax_j(q_t . k_j / sqrt(d)) v_j
+ *   O_lin-local = sum_j (relu(q_t) . relu(k_j)) v_j / (sum_j relu(q_t) . relu(k_j) + eps)
+ * Tokens of unlisted blocks are not touched: `out` is expected to hold the global path's
+ * output on entry.
+ *
+ * q, k, v : bfloat16 device pointers, [B][Hgrid][Wgrid][H][d]; read only.
+ * out     : device pointer of the same shape, bfloat16 (dtype WATTN_BF16) or float32
+ *           (WATTN_BF16_OUT_FP32); read and written.  Must not overlap q, k, v, list or count.
+ * list, count : the block list and its length on the device (as written by
+ *           wattn_select_blocks, capacity B * (Hgrid/w) * (Wgrid/w)).  The count is clamped to
+ *           [0, number of blocks] and list entries outside the grid are skipped.
+ * w       : block side, one of 4, 8, 12, 16; Hgrid and Wgrid multiples of w.
+ * d       : 32.   eps : finite, >= 0 (WATTN_ERR_VALUE otherwise).
+ * One workgroup per (block, head) is launched for every block of the grid; those past the
+ * device-side count return at once, so the call needs no host synchronisation.
+ *
+ * Numerics: scores from exact bf16 products accumulated in fp32; softmax in fp32 with the
+ * exact row max; P (<= 1) and v rounded to fp16 for the value product (v entries must stay
+ * below 65504 in magnitude); relu(k)^T v and the key sums accumulated in fp32 and applied
+ * through a bf16 high + low split; the residual added in fp32 and rounded once to out's type.
+ */
+int wattn_local_residual(const void* q, const void* k, const void* v, void* out, const int* list,
+                         const int* count, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps,
+                         int dtype, void* stream);
 
 /*
  * wattn_pair_count -- number of (query, key) pairs with a finite logit in a call with

@@ -26,6 +26,7 @@ from .hsmla_oracle import (  # noqa: F401
     relu_linear_attention,
     softmax_attention,
     local_residual_window,
+    window_tokens,
     local_residual,
     gated_local_path,
     global_linear_attention,

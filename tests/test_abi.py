@@ -34,8 +34,8 @@ def _call(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, thet
 def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
-    assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_pair_count",
-                     "wattn_status_string", "wattn_abi_version"}
+    assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_select_blocks",
+                     "wattn_local_residual", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -150,3 +150,59 @@ def _call_bwd(**kw):
 )
 def test_backward_rejects_invalid_arguments(kw, status):
     assert _call_bwd(**kw) == status
+
+
+# ---- the gated local path: host-side rejections
+GT, LST, CNT = 0x1000000, 0x1100000, 0x1200000
+
+
+def _call_select(gate=GT, n=64, tau=0.5, lst=LST, cnt=CNT):
+    vp = ctypes.c_void_p
+    return _lib().wattn_select_blocks(vp(gate), n, ctypes.c_float(tau), vp(lst), vp(cnt), vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(gate=None), 1), (dict(lst=None), 1), (dict(cnt=None), 1),
+        (dict(n=0), 2), (dict(n=-3), 2), (dict(n=(1 << 22) + 1), 2),
+        (dict(lst=GT + 4), 7), (dict(cnt=GT + 252), 7), (dict(cnt=LST + 8), 7),
+    ],
+)
+def test_select_blocks_rejects_invalid_arguments(kw, status):
+    assert _call_select(**kw) == status
+
+
+def test_select_blocks_valid_arguments_reach_the_device_check():
+    assert _call_select() in (8, 9)  # no GPU here: WATTN_ERR_HIP (or a pointer error on a GPU host)
+
+
+def _call_local(**kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, lst=LST, cnt=CNT, B=1, H=2, Hg=16, Wg=16, w=8, d=32, eps=1e-6, dtype=2)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_local_residual(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(a["lst"]),
+                                       vp(a["cnt"]), a["B"], a["H"], a["Hg"], a["Wg"], a["w"], a["d"],
+                                       ctypes.c_float(a["eps"]), a["dtype"], vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(out=None), 1), (dict(lst=None), 1),
+        (dict(cnt=None), 1),
+        (dict(B=0), 2), (dict(H=-1), 2), (dict(Hg=12), 2), (dict(Wg=20), 2), (dict(w=6, Hg=12, Wg=12), 2),
+        (dict(w=32, Hg=32, Wg=32), 2), (dict(w=0), 2), (dict(Hg=70000, Wg=8), 2),
+        (dict(d=64), 4),
+        (dict(eps=-1e-6), 10), (dict(eps=float("nan")), 10), (dict(eps=float("inf")), 10),
+        (dict(dtype=1), 6), (dict(dtype=3), 6),
+        (dict(out=P1), 7), (dict(out=P3 + 64), 7), (dict(out=LST - 64), 7), (dict(out=CNT - 32), 7),
+    ],
+)
+def test_local_residual_rejects_invalid_arguments(kw, status):
+    assert _call_local(**kw) == status
+
+
+def test_local_residual_valid_arguments_reach_the_device_check():
+    assert _call_local() in (8, 9)
+    assert _call_local(w=4, eps=0.0, dtype=0) in (8, 9)

@@ -9,6 +9,8 @@ call raises.
     out = forward(q, k, v, M=32, shift=16, theta=theta)
     out, lse = forward(q, k, v, M=32, shift=16, theta=theta, return_lse=True)
     dq, dk, dv, dtheta, dbias_u, dbias_v = backward(q, k, v, out, dout, lse, M=32, shift=16, theta=theta)
+    blocks, count = select_blocks(gate, tau)                      # gated local path: routing
+    local_residual(q, k, v, out, blocks, count, w=8, eps=1e-6)    # out += O_local - O_lin-local
 
 q, k, v: [B, Hgrid, Wgrid, H, 32] contiguous device tensors, bfloat16 or float32.
 theta:   [H, 16] float32 device tensor of rotation-pair frequencies, or None (no RoPE).
@@ -23,6 +25,9 @@ import os
 __all__ = [
     "forward",
     "backward",
+    "select_blocks",
+    "local_residual",
+    "gated_local_path",
     "pair_count",
     "abi_version",
     "status_string",
@@ -49,6 +54,7 @@ STATUS = {
     7: "WATTN_ERR_ALIAS",
     8: "WATTN_ERR_HIP",
     9: "WATTN_ERR_POINTER",
+    10: "WATTN_ERR_VALUE",
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +90,10 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_forward_lse.restype = ci
     lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
     lib.wattn_backward.restype = ci
+    lib.wattn_select_blocks.argtypes = [vp, ci, ctypes.c_float, vp, vp, vp]
+    lib.wattn_select_blocks.restype = ci
+    lib.wattn_local_residual.argtypes = [vp] * 6 + [ci] * 6 + [ctypes.c_float, ci, vp]
+    lib.wattn_local_residual.restype = ci
     lib.wattn_pair_count.argtypes = [ci] * 6
     lib.wattn_pair_count.restype = ctypes.c_int64
     lib.wattn_status_string.argtypes = [ci]
@@ -231,3 +241,73 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bia
     if st != 0:
         raise WattnError(st, status_string(st))
     return dq, dk, dv, dtheta, dbu, dbv
+
+
+def select_blocks(gate, tau: float, *, blocks=None, count=None, stream=None):
+    """Routing of the gated local path: the ascending indices of the blocks whose gate value
+    exceeds ``tau``.  ``gate`` is a float32 device tensor of the per-block gate values
+    ([B, Hg/w, Wg/w] or flat); returns ``(blocks, count)``: an int32 device tensor with room
+    for every block, of which the first ``count[0]`` entries are valid, and the one-element
+    int32 device count.  Nothing is synchronised."""
+    import torch
+
+    lib = load_library()
+    if gate.dtype != torch.float32 or not gate.is_cuda or not gate.is_contiguous():
+        raise ValueError("gate must be a contiguous float32 device tensor")
+    n = gate.numel()
+    if blocks is None:
+        blocks = torch.empty(n, dtype=torch.int32, device=gate.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=gate.device)
+    if blocks.dtype != torch.int32 or blocks.numel() < n or count.dtype != torch.int32 or count.numel() < 1:
+        raise ValueError("blocks must be int32 with room for every block, count int32 with one element")
+    if stream is None:
+        stream = torch.cuda.current_stream(gate.device).cuda_stream
+    st = lib.wattn_select_blocks(_ptr(gate), n, ctypes.c_float(tau), _ptr(blocks), _ptr(count),
+                                 ctypes.c_void_p(stream))
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return blocks, count
+
+
+def local_residual(q, k, v, out, blocks, count, *, w: int, eps: float = 1e-6, stream=None):
+    """out += O_local - O_lin-local on the tokens of the listed blocks (in place; ``out``
+    holds the global path's output).  q, k, v: bfloat16 [B, Hg, Wg, H, 32]; out: bfloat16 or
+    float32 of that shape; blocks, count: as returned by ``select_blocks``.  Returns out."""
+    import torch
+
+    lib = load_library()
+    if q.dtype != torch.bfloat16 or q.dim() != 5:
+        raise TypeError("q, k, v must be bfloat16 [B, Hgrid, Wgrid, H, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.shape != q.shape or not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor shaped like q")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must be bfloat16")
+    if out.dtype == torch.bfloat16:
+        dtype = BF16
+    elif out.dtype == torch.float32:
+        dtype = BF16_OUT_FP32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    if blocks.dtype != torch.int32 or count.dtype != torch.int32 or not blocks.is_cuda or not count.is_cuda:
+        raise ValueError("blocks and count must be int32 device tensors")
+    B, Hg, Wg, H, d = q.shape
+    if blocks.numel() < B * (Hg // w) * (Wg // w):
+        raise ValueError("blocks must have room for every block of the grid")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.wattn_local_residual(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(blocks), _ptr(count),
+                                  B, H, Hg, Wg, w, d, ctypes.c_float(eps), dtype, ctypes.c_void_p(stream))
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return out
+
+
+def gated_local_path(q, k, v, out, gate, tau: float, *, w: int, eps: float = 1e-6, stream=None):
+    """Routing followed by the residual correction, both on the same stream: the blocks with
+    gate > tau get out += O_local - O_lin-local.  Returns ``(out, blocks, count)``."""
+    blocks, count = select_blocks(gate, tau, stream=stream)
+    local_residual(q, k, v, out, blocks, count, w=w, eps=eps, stream=stream)
+    return out, blocks, count

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "wattn.h"
 #include "wattn_plan.h"
@@ -18,6 +19,9 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
                             const void* v, const void* out, const void* dout, const float* lse, float* delta,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
                             const void* bv, float* dbu, float* dbv, hipStream_t stream);
+hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, int* count, hipStream_t stream);
+hipError_t wattn_launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
+                              void* out, const int* list, const int* count, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -297,6 +301,76 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 
+extern "C" int wattn_select_blocks(const float* gate, int nblocks, float tau, int* list, int* count, void* stream) {
+  if (gate == nullptr || list == nullptr || count == nullptr) return WATTN_ERR_NULL;
+  if (nblocks <= 0 || nblocks > WATTN_MAX_BLOCKS) return WATTN_ERR_SHAPE;
+  const size_t gbytes = (size_t)nblocks * sizeof(float), lbytes = (size_t)nblocks * sizeof(int);
+  auto rng = [](const void* p, size_t n) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+  };
+  const Range rg = rng(gate, gbytes), rl = rng(list, lbytes), rc = rng(count, sizeof(int));
+  if (overlaps(rl, rg) || overlaps(rc, rg) || overlaps(rc, rl)) return WATTN_ERR_ALIAS;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  int st;
+  if ((st = pointer_ok(gate, gbytes)) != WATTN_OK || (st = pointer_ok(list, lbytes)) != WATTN_OK ||
+      (st = pointer_ok(count, sizeof(int))) != WATTN_OK)
+    return st;
+  const hipError_t e = wattn_launch_select(gate, nblocks, tau, list, count, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+extern "C" int wattn_local_residual(const void* q, const void* k, const void* v, void* out, const int* list,
+                                    const int* count, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps,
+                                    int dtype, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || list == nullptr || count == nullptr)
+    return WATTN_ERR_NULL;
+  if (B <= 0 || H <= 0 || Hgrid <= 0 || Wgrid <= 0 || Hgrid > 65535 || Wgrid > 65535) return WATTN_ERR_SHAPE;
+  if (w != 4 && w != 8 && w != 12 && w != 16) return WATTN_ERR_SHAPE;
+  if (Hgrid % w != 0 || Wgrid % w != 0) return WATTN_ERR_SHAPE;
+  if (d != 32) return WATTN_ERR_HEAD_DIM;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return WATTN_ERR_VALUE;
+  if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
+  const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
+  if (elems >= kMaxElems || (int64_t)Hgrid * Wgrid * H * d >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  const int64_t nblocks = (int64_t)B * (Hgrid / w) * (Wgrid / w);
+  if (nblocks > WATTN_MAX_BLOCKS || nblocks * H > 0x7fffffffLL) return WATTN_ERR_SHAPE;
+  const size_t tbytes = (size_t)elems * 2, obytes = (size_t)elems * (dtype == WATTN_BF16 ? 2 : 4);
+  const size_t lbytes = (size_t)nblocks * sizeof(int);
+  auto rng = [](const void* p, size_t n) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+  };
+  const Range ro = rng(out, obytes);
+  const Range ins[5] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(list, lbytes), rng(count, sizeof(int))};
+  for (const Range& x : ins)
+    if (overlaps(ro, x)) return WATTN_ERR_ALIAS;
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  const void* ptrs[6] = {q, k, v, out, list, count};
+  const size_t sizes[6] = {tbytes, tbytes, tbytes, obytes, lbytes, sizeof(int)};
+  for (int i = 0; i < 6; ++i) {
+    const int st = pointer_ok(ptrs[i], sizes[i]);
+    if (st != WATTN_OK) return st;
+  }
+  LocalPlan P;
+  P.B = B; P.H = H; P.Hg = Hgrid; P.Wg = Wgrid; P.w = w;
+  P.nWx = Wgrid / w;
+  P.nW = (Hgrid / w) * P.nWx;
+  P.nblocks = (int)nblocks;
+  P.img_stride = (int64_t)Hgrid * Wgrid * H * d;
+  P.eps = eps;
+  const hipError_t e = wattn_launch_local(P, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, list, count,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
 extern "C" int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift) {
   if (check_shape(B, H, Hgrid, Wgrid, M, shift) != WATTN_OK) return -1;
   const AxisSplit ay = split_axis(Hgrid, M, shift), ax = split_axis(Wgrid, M, shift);
@@ -321,6 +395,7 @@ extern "C" const char* wattn_status_string(int status) {
     case WATTN_ERR_ALIAS: return "out overlaps an input buffer";
     case WATTN_ERR_HIP: return "HIP runtime error (no device or launch failure)";
     case WATTN_ERR_POINTER: return "buffer is not device-accessible memory of the required size";
+    case WATTN_ERR_VALUE: return "scalar parameter out of range (eps must be finite and >= 0)";
     default: return "unknown status";
   }
 }

@@ -51,3 +51,12 @@ struct WattnF32Plan {
   int nwx, nw, nqt;
   int grid;
 };
+
+// Launch description of the gated local path: the w x w block grid of the token grid.
+// Block index = b * nW + wy * nWx + wx (nW = nWy * nWx blocks per image).
+struct LocalPlan {
+  int B, H, Hg, Wg, w;
+  int nWx, nW, nblocks;
+  int64_t img_stride;  // elements of one image: Hg * Wg * H * d
+  float eps;           // denominator guard of the linear attention
+};
