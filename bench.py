@@ -5,13 +5,17 @@ bias channels + QK^T + mask + online softmax + PV + normalise + scatter, all in 
 launch).  Inputs are resident in HBM before timing starts; several input sets are used in
 rotation so that consecutive steps do not find their inputs in the last-level cache.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--out-dtype fp32|bf16] [--pass fwd|bwd]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--out-dtype fp32|bf16] [--pass fwd|bwd|gated]
 
 Prints one JSON line.  The default workload is the dense patch-2 grid at M = 32
 (16 images x 128 x 128 tokens, 3 heads x 32, shift 16), the configuration the headline
 metric is quoted on.  With --pass bwd a step is one wattn_backward call (dq, dk, dv and
 dtheta of the same workload, given the forward pass's output, its row log-sum-exp and an
-output gradient, all resident), timed the same way.
+output gradient, all resident), timed the same way.  With --pass gated a step is the gated
+local path of hybrid linear/softmax attention on the dense grid with 8 x 8 (or 16 x 16)
+blocks: one wattn_gated_local call (the ~30% of blocks whose gate exceeds tau get
+out += O_local - O_lin-local, in place); the list form (wattn_select_blocks followed by
+wattn_local_residual) is timed beside it.
 """
 
 from __future__ import annotations
@@ -29,11 +33,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "window-attn tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
 METRIC_BWD = "window-attn backward tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
+METRIC_GATED = "gated local path tokens/s (routing + local softmax residual), % of HBM peak, p=2 grid"
 WARMUP_MIN_S = 0.5          # untimed back-to-back launches before timing (clock ramp)
 WARMUP_MAX_STEPS = 20000
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SRC = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "csrc", "wattn_kernels.hip")
+CSRC = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "csrc")
+# the sources each profiled kernel is compiled from (their hash tags the traffic records)
+KERNEL_SRCS = {
+    "attention": [os.path.join(CSRC, f) for f in ("wattn_kernels.hip", "wattn_device.h", "wattn_plan.h")],
+    "gated": [os.path.join(CSRC, f) for f in ("wattn_gated.hip", "wattn_device.h", "wattn_plan.h")],
+}
 PIPE_RATES = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "pipe_rates")
 MFMA_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 / _f16
 
@@ -48,25 +58,28 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
-                    help="fwd: wattn_forward (the headline); bwd: wattn_backward")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated"],
+                    help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path")
     return ap.parse_args()
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_sha(which: str = "attention") -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS[which]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, out_dtype: str):
+def traffic_from_profiles(workload: str, out_dtype: str, which: str = "attention"):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were taken on
-    the current kernel source; otherwise None."""
+    the current kernel sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{out_dtype}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha") != kernel_sha():
+    if rec.get("kernel_sha") != kernel_sha(which):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -172,6 +185,142 @@ def cpu_baseline(cfg, budget_s: float):
     }
 
 
+def cpu_baseline_gated(cfg, budget_s: float):
+    """Time the float64 oracle's residual on random selected blocks of the gated workload."""
+    import numpy as np
+
+    import oracle
+    from inputs import make_gated_inputs
+
+    inp = make_gated_inputs(cfg, batch=1)
+    sel = oracle.select_blocks(inp["gate"], cfg.tau)
+    frac = sel.size / (inp["gate"].size)
+    rng = np.random.default_rng(0)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.local_residual_window(inp["q"], inp["k"], inp["v"], int(rng.choice(sel)), cfg.w, cfg.eps)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    # one selected block per (w*w / frac) layer tokens
+    return {
+        "value": done * cfg.w * cfg.w / frac / el,
+        "unit": "tokens/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"{done} random selected {cfg.w}x{cfg.w} blocks of one image (all {cfg.H} heads, {el:.1f} s, "
+                  f"numpy float64 with materialised weights), scaled by the selected fraction {frac:.3f} to "
+                  "tokens of the layer",
+    }
+
+
+def main_gated(args):
+    """--pass gated: routing + residual correction of the gated local path."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from inputs import GATED_CONFIGS, make_gated_inputs
+
+    name = args.workload if args.workload in GATED_CONFIGS else "gated_p2_w8"
+    cfg = GATED_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    odt = torch.float32 if args.out_dtype == "fp32" else torch.bfloat16
+    base = make_gated_inputs(cfg)
+    nsel = int(np.count_nonzero(base["gate"] > cfg.tau))
+    sets = []
+    for i in range(args.input_sets):
+        g = torch.Generator(device="cpu").manual_seed(i)
+        perm = torch.randperm(cfg.B, generator=g) if i else torch.arange(cfg.B)
+        t = {key: torch.from_numpy(np.ascontiguousarray(base[key])).to(torch.bfloat16)[perm].contiguous().to(dev)
+             for key in ("q", "k", "v")}
+        t["out"] = torch.from_numpy(base["base"])[perm].contiguous().to(odt).to(dev)
+        t["gate"] = torch.from_numpy(base["gate"])[perm].contiguous().to(dev)
+        t["blocks"] = torch.empty(cfg.blocks, dtype=torch.int32, device=dev)
+        t["count"] = torch.empty(1, dtype=torch.int32, device=dev)
+        sets.append(t)
+    del base
+
+    def step(i):  # routing and residual in one launch
+        t = sets[i % len(sets)]
+        wattn.gated_local_path(t["q"], t["k"], t["v"], t["out"], t["gate"], cfg.tau, w=cfg.w, eps=cfg.eps)
+
+    def step_list(i):  # the list form: wattn_select_blocks, then wattn_local_residual
+        t = sets[i % len(sets)]
+        wattn.select_blocks(t["gate"], cfg.tau, blocks=t["blocks"], count=t["count"])
+        wattn.local_residual(t["q"], t["k"], t["v"], t["out"], t["blocks"], t["count"], w=cfg.w, eps=cfg.eps)
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or (time.perf_counter() - t_w < WARMUP_MIN_S and i < WARMUP_MAX_STEPS):
+        step(i)
+        step_list(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    avg_s = ev[0].elapsed_time(ev[1]) / args.steps / 1e3
+    ev[2].record(stream)
+    for i in range(args.steps):
+        step_list(i)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    list_s = ev[2].elapsed_time(ev[3]) / args.steps / 1e3
+    osz = 4 if args.out_dtype == "fp32" else 2
+    T = cfg.w * cfg.w
+    kp = (T + 31) // 32 * 32
+    unit_heads = nsel * cfg.H
+    # q, k, v read and out read + written on the selected tokens, every block's gate read
+    alg_bytes = unit_heads * T * (3 * cfg.d * 2 + 2 * cfg.d * osz) + cfg.blocks * 4
+    # matrix-core flops per (block, head): scores and PV over the padded keys, relu(K)^T V and
+    # the key sums, the linear apply (high + low parts)
+    flops = unit_heads * (4.0 * T * kp * cfg.d + 2.0 * kp * cfg.d * (cfg.d + 32) + 4.0 * T * cfg.d * cfg.d)
+    achieved = alg_bytes / avg_s / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic_from_profiles(cfg.name, args.out_dtype, "gated")}
+    rec = {
+        "metric": METRIC_GATED,
+        "value": cfg.tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v rounded to bf16; i.i.d. uniform block gates; N(0,1) base output)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hgrid": cfg.Hg, "Wgrid": cfg.Wg, "H": cfg.H, "d": cfg.d,
+                   "w": cfg.w, "tau": cfg.tau, "eps": cfg.eps, "blocks": cfg.blocks, "selected_blocks": nsel,
+                   "out_dtype": args.out_dtype, "global_batch": cfg.B, "tokens_per_step": cfg.tokens,
+                   "input_sets": args.input_sets,
+                   "pass": "gated local path (routing + residual in one launch, wattn_gated_local)"},
+        "kernel_ms_avg": avg_s * 1e3,
+        "list_form_ms_avg": list_s * 1e3,
+        "algorithmic_gbs_kernel": achieved,
+        "tflops_executed_kernel": flops / avg_s / 1e12,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_gated(cfg, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -179,6 +328,9 @@ def main():
               "(the operator needs no collective: batch and window sharding are communication-free)",
               file=sys.stderr)
         sys.exit(2)
+    if args.which == "gated":
+        main_gated(args)
+        return
 
     import numpy as np
     import torch

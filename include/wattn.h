@@ -229,6 +229,19 @@ int wattn_local_residual(const void* q, const void* k, const void* v, void* out,
                          int dtype, void* stream);
 
 /*
+ * wattn_gated_local -- routing and residual correction in one launch: the blocks whose gate
+ * exceeds tau (strictly; a NaN gate never) get out += O_local - O_lin-local exactly as in
+ * wattn_local_residual; no list is produced.  Every (block, head) has a workgroup that reads
+ * its block's gate and leaves at once unless the block is selected.
+ *
+ * gate : float32 device pointer, [B * (Hgrid/w) * (Wgrid/w)] gate values in block order;
+ *        read only; must not overlap out.
+ * All other arguments, checks and numerics are those of wattn_local_residual.
+ */
+int wattn_gated_local(const void* q, const void* k, const void* v, void* out, const float* gate, float tau,
+                      int B, int H, int Hgrid, int Wgrid, int w, int d, float eps, int dtype, void* stream);
+
+/*
  * wattn_pair_count -- number of (query, key) pairs with a finite logit in a call with
  * these sizes (the masked pairs of wrapped windows excluded).  Pure host arithmetic:
  * no HIP call, no side effect.  Returns -1 for sizes wattn_forward would reject with

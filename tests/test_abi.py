@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
     assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_select_blocks",
-                     "wattn_local_residual", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
+                     "wattn_local_residual", "wattn_gated_local", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -206,3 +206,30 @@ def test_local_residual_rejects_invalid_arguments(kw, status):
 def test_local_residual_valid_arguments_reach_the_device_check():
     assert _call_local() in (8, 9)
     assert _call_local(w=4, eps=0.0, dtype=0) in (8, 9)
+
+
+def _call_gated(**kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, gate=GT, tau=0.5, B=1, H=2, Hg=16, Wg=16, w=8, d=32, eps=1e-6, dtype=2)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_gated_local(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(a["gate"]),
+                                    ctypes.c_float(a["tau"]), a["B"], a["H"], a["Hg"], a["Wg"], a["w"], a["d"],
+                                    ctypes.c_float(a["eps"]), a["dtype"], vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=None), 1), (dict(out=None), 1), (dict(gate=None), 1),
+        (dict(B=0), 2), (dict(Wg=20), 2), (dict(w=5, Hg=10, Wg=10), 2), (dict(d=16), 4),
+        (dict(eps=-1.0), 10), (dict(dtype=1), 6),
+        (dict(out=GT - 64), 7), (dict(out=P2 + 32), 7),
+    ],
+)
+def test_gated_local_rejects_invalid_arguments(kw, status):
+    assert _call_gated(**kw) == status
+
+
+def test_gated_local_valid_arguments_reach_the_device_check():
+    assert _call_gated() in (8, 9)
+    assert _call_gated(tau=float("nan"), w=16, dtype=0) in (8, 9)

@@ -1,6 +1,7 @@
 """GPU parity of the gated local path: block routing (bit-exact list and count) and the
 residual correction out += O_local - O_lin-local (through the C ABI) against the float64
-oracle on the same seeded inputs.
+oracle on the same seeded inputs.  The one-launch form (each block's workgroups route
+themselves by its gate) must give the list form's output bit for bit.
 
 Bounds on the residual R = out - base: max|err| <= 1e-2 and relative L2 <= 5e-3 (the
 bf16 bounds of the attention kernel; the expected relative L2 is about 3e-4: the scores are
@@ -19,6 +20,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _gpu(q, k, v, base, gate, tau, w, eps, out_f32=True, blocks=None, count=None):
+    """Both forms of the path on the same inputs: the list form (wattn_select_blocks +
+    wattn_local_residual, or a caller-made list) and, given a gate, the one-launch form
+    (wattn_gated_local).  Returns (out of the list form, list, count, out of the one-launch form)."""
     import torch
 
     import vision_transformer_windowed_window_amd as wattn
@@ -26,15 +30,20 @@ def _gpu(q, k, v, base, gate, tau, w, eps, out_f32=True, blocks=None, count=None
     dev = torch.device("cuda:0")
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
     tq, tk, tv = (t(a, torch.bfloat16) for a in (q, k, v))
-    out = t(base, torch.float32 if out_f32 else torch.bfloat16)
+    odt = torch.float32 if out_f32 else torch.bfloat16
+    out = t(base, odt)
+    fused = None
     if blocks is None:
-        out, blocks, count = wattn.gated_local_path(tq, tk, tv, out, t(gate, torch.float32), tau, w=w, eps=eps)
+        tg = t(gate, torch.float32)
+        blocks, count = wattn.select_blocks(tg, tau)
+        fused = wattn.gated_local_path(tq, tk, tv, t(base, odt), tg, tau, w=w, eps=eps)
     else:
         blocks, count = t(blocks, torch.int32), t(count, torch.int32)
-        wattn.local_residual(tq, tk, tv, out, blocks, count, w=w, eps=eps)
+    wattn.local_residual(tq, tk, tv, out, blocks, count, w=w, eps=eps)
     torch.cuda.synchronize()
     n = int(count[0].item())
-    return out.float().cpu().numpy().astype(np.float64), blocks[:n].cpu().numpy(), n
+    f64 = lambda x: None if x is None else x.float().cpu().numpy().astype(np.float64)
+    return f64(out), blocks[:n].cpu().numpy(), n, f64(fused)
 
 
 def _check_residual(got, base, ref, label):
@@ -64,7 +73,8 @@ def test_gated_local_path_matches_oracle(case):
     q, k, v = qkv((B, Hg, Wg, H, 32), seed, "bf16")
     base = np.random.default_rng(seed + 1).standard_normal(size=q.shape).astype(np.float32)
     gate = block_gate(B, Hg // w, Wg // w, seed + 2)
-    got, blocks, n = _gpu(q, k, v, base, gate, tau, w, eps, out_f32)
+    got, blocks, n, fused = _gpu(q, k, v, base, gate, tau, w, eps, out_f32)
+    assert np.array_equal(fused, got), "the one-launch form differs from the list form"
     sel = oracle.select_blocks(gate, tau)
     assert n == sel.size and np.array_equal(blocks, sel), "block list"
     ref = oracle.local_residual(q, k, v, base, sel, w, eps)
@@ -79,7 +89,8 @@ def test_bf16_output():
     q, k, v = qkv((B, Hg, Wg, H, 32), 811, "bf16")
     gate = block_gate(B, Hg // w, Wg // w, 812)
     base = np.zeros(q.shape, np.float32)
-    got, blocks, n = _gpu(q, k, v, base, gate, 0.5, w, 1e-6, out_f32=False)
+    got, blocks, n, fused = _gpu(q, k, v, base, gate, 0.5, w, 1e-6, out_f32=False)
+    assert np.array_equal(fused, got)
     sel = oracle.select_blocks(gate, 0.5)
     assert np.array_equal(blocks, sel)
     ref = oracle.local_residual(q, k, v, base, sel, w, 1e-6)
@@ -94,8 +105,8 @@ def test_nothing_selected_leaves_out_unchanged():
     q, k, v = qkv((B, Hg, Wg, H, 32), 821, "bf16")
     base = np.random.default_rng(822).standard_normal(size=q.shape).astype(np.float32)
     gate = block_gate(B, Hg // w, Wg // w, 823)
-    got, _, n = _gpu(q, k, v, base, gate, 1.0, w, 1e-6)
-    assert n == 0 and np.array_equal(got, base.astype(np.float64))
+    got, _, n, fused = _gpu(q, k, v, base, gate, 1.0, w, 1e-6)
+    assert n == 0 and np.array_equal(got, base.astype(np.float64)) and np.array_equal(fused, got)
 
 
 def test_gate_ties_and_nan_route_like_the_oracle():
@@ -105,20 +116,20 @@ def test_gate_ties_and_nan_route_like_the_oracle():
     gate.reshape(-1)[::7] = 0.5                # ties with tau are not selected
     gate.reshape(-1)[3::11] = np.nan           # NaN never selected
     base = np.zeros(q.shape, np.float32)
-    got, blocks, n = _gpu(q, k, v, base, gate, 0.5, w, 1e-6)
+    got, blocks, n, fused = _gpu(q, k, v, base, gate, 0.5, w, 1e-6)
     sel = oracle.select_blocks(gate, 0.5)
-    assert n == sel.size and np.array_equal(blocks, sel)
+    assert n == sel.size and np.array_equal(blocks, sel) and np.array_equal(fused, got)
     _check_residual(got, base, oracle.local_residual(q, k, v, base, sel, w, 1e-6), "ties_nan")
 
 
 def test_caller_list_with_entries_outside_the_grid():
-    """A caller-made list: entries outside the grid are skipped, a count above the number of
-    blocks is clamped, and repeated entries are applied once per appearance."""
+    """A caller-made list: entries outside the grid are skipped and a count above the number
+    of blocks is clamped."""
     B, Hg, Wg, H, w = 1, 16, 16, 2, 8      # 4 blocks
     q, k, v = qkv((B, Hg, Wg, H, 32), 841, "bf16")
     base = np.random.default_rng(842).standard_normal(size=q.shape).astype(np.float32)
     lst = np.array([2, 1 << 20, -3, 0], np.int32)
-    got, _, _ = _gpu(q, k, v, base, None, None, w, 1e-6, blocks=lst, count=np.array([9], np.int32))
+    got, _, _, _ = _gpu(q, k, v, base, None, None, w, 1e-6, blocks=lst, count=np.array([9], np.int32))
     ref = oracle.local_residual(q, k, v, base, [2, 0], w, 1e-6)
     _check_residual(got, base, ref, "caller_list")
 
@@ -130,9 +141,9 @@ def test_full_size_sampled(name):
     cfg = GATED_CONFIGS[name]
     inp = make_gated_inputs(cfg)
     note(f"full size {name}: {cfg.B}x{cfg.Hg}x{cfg.Wg} H={cfg.H} w={cfg.w} tau={cfg.tau}")
-    got, blocks, n = _gpu(inp["q"], inp["k"], inp["v"], inp["base"], inp["gate"], cfg.tau, cfg.w, cfg.eps)
+    got, blocks, n, fused = _gpu(inp["q"], inp["k"], inp["v"], inp["base"], inp["gate"], cfg.tau, cfg.w, cfg.eps)
     sel = oracle.select_blocks(inp["gate"], cfg.tau)
-    assert n == sel.size and np.array_equal(blocks, sel)
+    assert n == sel.size and np.array_equal(blocks, sel) and np.array_equal(fused, got)
     note(f"  {n} of {cfg.blocks} blocks selected")
     untouched = ~np.repeat(np.repeat(inp["gate"] > cfg.tau, cfg.w, axis=1), cfg.w, axis=2)
     assert np.array_equal(got[untouched], inp["base"][untouched].astype(np.float64))

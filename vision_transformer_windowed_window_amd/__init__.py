@@ -11,6 +11,7 @@ call raises.
     dq, dk, dv, dtheta, dbias_u, dbias_v = backward(q, k, v, out, dout, lse, M=32, shift=16, theta=theta)
     blocks, count = select_blocks(gate, tau)                      # gated local path: routing
     local_residual(q, k, v, out, blocks, count, w=8, eps=1e-6)    # out += O_local - O_lin-local
+    gated_local_path(q, k, v, out, gate, tau, w=8, eps=1e-6)      # both in one launch, no list
 
 q, k, v: [B, Hgrid, Wgrid, H, 32] contiguous device tensors, bfloat16 or float32.
 theta:   [H, 16] float32 device tensor of rotation-pair frequencies, or None (no RoPE).
@@ -94,6 +95,8 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_select_blocks.restype = ci
     lib.wattn_local_residual.argtypes = [vp] * 6 + [ci] * 6 + [ctypes.c_float, ci, vp]
     lib.wattn_local_residual.restype = ci
+    lib.wattn_gated_local.argtypes = [vp] * 5 + [ctypes.c_float] + [ci] * 6 + [ctypes.c_float, ci, vp]
+    lib.wattn_gated_local.restype = ci
     lib.wattn_pair_count.argtypes = [ci] * 6
     lib.wattn_pair_count.restype = ctypes.c_int64
     lib.wattn_status_string.argtypes = [ci]
@@ -306,8 +309,34 @@ def local_residual(q, k, v, out, blocks, count, *, w: int, eps: float = 1e-6, st
 
 
 def gated_local_path(q, k, v, out, gate, tau: float, *, w: int, eps: float = 1e-6, stream=None):
-    """Routing followed by the residual correction, both on the same stream: the blocks with
-    gate > tau get out += O_local - O_lin-local.  Returns ``(out, blocks, count)``."""
-    blocks, count = select_blocks(gate, tau, stream=stream)
-    local_residual(q, k, v, out, blocks, count, w=w, eps=eps, stream=stream)
-    return out, blocks, count
+    """Routing and residual correction in one launch: the blocks whose gate value exceeds
+    ``tau`` get out += O_local - O_lin-local (in place).  ``gate``: float32 device tensor of
+    the B * (Hg/w) * (Wg/w) block gates in block order.  Returns out."""
+    import torch
+
+    lib = load_library()
+    if q.dtype != torch.bfloat16 or q.dim() != 5:
+        raise TypeError("q, k, v must be bfloat16 [B, Hgrid, Wgrid, H, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.shape != q.shape or not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous device tensor shaped like q")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must be bfloat16")
+    if out.dtype == torch.bfloat16:
+        dtype = BF16
+    elif out.dtype == torch.float32:
+        dtype = BF16_OUT_FP32
+    else:
+        raise TypeError("out must be bfloat16 or float32")
+    B, Hg, Wg, H, d = q.shape
+    if (gate.dtype != torch.float32 or not gate.is_cuda or not gate.is_contiguous()
+            or gate.numel() != B * (Hg // w) * (Wg // w)):
+        raise ValueError("gate must be a contiguous float32 device tensor with one value per block")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.wattn_gated_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(gate), ctypes.c_float(tau),
+                               B, H, Hg, Wg, w, d, ctypes.c_float(eps), dtype, ctypes.c_void_p(stream))
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return out

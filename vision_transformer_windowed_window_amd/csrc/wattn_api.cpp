@@ -22,6 +22,8 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
 hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, int* count, hipStream_t stream);
 hipError_t wattn_launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
                               void* out, const int* list, const int* count, hipStream_t stream);
+hipError_t wattn_launch_gated(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
+                              void* out, const float* gate, float tau, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -323,11 +325,15 @@ extern "C" int wattn_select_blocks(const float* gate, int nblocks, float tau, in
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 
-extern "C" int wattn_local_residual(const void* q, const void* k, const void* v, void* out, const int* list,
-                                    const int* count, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps,
-                                    int dtype, void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || list == nullptr || count == nullptr)
-    return WATTN_ERR_NULL;
+namespace {
+
+// Checks and launch shared by the two forms of the residual correction: LISTED takes the block
+// list of wattn_select_blocks, otherwise every block's workgroups route themselves by its gate.
+int local_impl(const void* q, const void* k, const void* v, void* out, const int* list, const int* count,
+               const float* gate, float tau, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps, int dtype,
+               void* stream, bool listed) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return WATTN_ERR_NULL;
+  if (listed ? (list == nullptr || count == nullptr) : gate == nullptr) return WATTN_ERR_NULL;
   if (B <= 0 || H <= 0 || Hgrid <= 0 || Wgrid <= 0 || Hgrid > 65535 || Wgrid > 65535) return WATTN_ERR_SHAPE;
   if (w != 4 && w != 8 && w != 12 && w != 16) return WATTN_ERR_SHAPE;
   if (Hgrid % w != 0 || Wgrid % w != 0) return WATTN_ERR_SHAPE;
@@ -337,25 +343,26 @@ extern "C" int wattn_local_residual(const void* q, const void* k, const void* v,
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
   if (elems >= kMaxElems || (int64_t)Hgrid * Wgrid * H * d >= (1LL << 31)) return WATTN_ERR_SHAPE;
   const int64_t nblocks = (int64_t)B * (Hgrid / w) * (Wgrid / w);
-  if (nblocks > WATTN_MAX_BLOCKS || nblocks * H > 0x7fffffffLL) return WATTN_ERR_SHAPE;
+  if (nblocks > WATTN_MAX_BLOCKS || 8 * H * ((nblocks + 7) / 8) > 0x7fffffffLL) return WATTN_ERR_SHAPE;
   const size_t tbytes = (size_t)elems * 2, obytes = (size_t)elems * (dtype == WATTN_BF16 ? 2 : 4);
-  const size_t lbytes = (size_t)nblocks * sizeof(int);
+  const size_t lbytes = (size_t)nblocks * sizeof(int), gbytes = (size_t)nblocks * sizeof(float);
   auto rng = [](const void* p, size_t n) {
-    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
   };
   const Range ro = rng(out, obytes);
-  const Range ins[5] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(list, lbytes), rng(count, sizeof(int))};
+  const Range ins[6] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(list, lbytes), rng(count, sizeof(int)),
+                        rng(gate, gbytes)};
   for (const Range& x : ins)
-    if (overlaps(ro, x)) return WATTN_ERR_ALIAS;
+    if (x.hi > x.lo && overlaps(ro, x)) return WATTN_ERR_ALIAS;
 
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
     (void)hipGetLastError();
     return WATTN_ERR_HIP;
   }
-  const void* ptrs[6] = {q, k, v, out, list, count};
-  const size_t sizes[6] = {tbytes, tbytes, tbytes, obytes, lbytes, sizeof(int)};
-  for (int i = 0; i < 6; ++i) {
+  const void* ptrs[7] = {q, k, v, out, list, count, gate};
+  const size_t sizes[7] = {tbytes, tbytes, tbytes, obytes, lbytes, sizeof(int), gbytes};
+  for (int i = 0; i < 7; ++i) {
     const int st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
@@ -366,9 +373,25 @@ extern "C" int wattn_local_residual(const void* q, const void* k, const void* v,
   P.nblocks = (int)nblocks;
   P.img_stride = (int64_t)Hgrid * Wgrid * H * d;
   P.eps = eps;
-  const hipError_t e = wattn_launch_local(P, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, list, count,
-                                          static_cast<hipStream_t>(stream));
+  const bool f32 = dtype == WATTN_BF16_OUT_FP32;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = listed ? wattn_launch_local(P, f32, q, k, v, out, list, count, s)
+                              : wattn_launch_gated(P, f32, q, k, v, out, gate, tau, s);
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int wattn_local_residual(const void* q, const void* k, const void* v, void* out, const int* list,
+                                    const int* count, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps,
+                                    int dtype, void* stream) {
+  return local_impl(q, k, v, out, list, count, nullptr, 0.f, B, H, Hgrid, Wgrid, w, d, eps, dtype, stream, true);
+}
+
+extern "C" int wattn_gated_local(const void* q, const void* k, const void* v, void* out, const float* gate,
+                                 float tau, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps, int dtype,
+                                 void* stream) {
+  return local_impl(q, k, v, out, nullptr, nullptr, gate, tau, B, H, Hgrid, Wgrid, w, d, eps, dtype, stream, false);
 }
 
 extern "C" int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift) {

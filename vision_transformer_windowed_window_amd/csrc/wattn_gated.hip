@@ -11,7 +11,9 @@
 //   wattn_select_blocks_kernel : one workgroup compacts the indices of the blocks with
 //       gate > tau into an ascending list (wave ballots and a prefix over the waves).
 //   wattn_local_residual_kernel : one workgroup per (listed block, head), the grid sized for
-//       every block and the workgroups past the device-side count leaving at once.  The
+//       every block and the workgroups past the device-side count leaving at once; or, in
+//       the one-launch form, one workgroup per (block, head) of the grid that leaves unless
+//       the block's gate exceeds tau.  The
 //       block's K and V (at most 16 x 16 tokens) are staged whole in LDS; each wave owns 16
 //       queries and computes
 //         O_local      exact softmax over the block's keys: S^T = K Q^T on bf16 MFMA (bf16
@@ -76,10 +78,14 @@ __global__ __launch_bounds__(1024) void wattn_select_blocks_kernel(const float* 
   if (tid == 0) *count = base;
 }
 
-template <int W, bool OUTF32>
+// LISTED: the blocks come from a list and its device-side count (wattn_select_blocks);
+// otherwise every block of the grid has a workgroup per head that routes itself by reading
+// the block's gate (one launch, no list).
+template <int W, bool OUTF32, bool LISTED>
 __global__ __launch_bounds__(64 * ((W * W + 15) / 16)) void wattn_local_residual_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    void* __restrict__ out, const int* __restrict__ list, const int* __restrict__ count, const LocalPlan P) {
+    void* __restrict__ out, const int* __restrict__ list, const int* __restrict__ count,
+    const float* __restrict__ gate, float tau, const LocalPlan P) {
   constexpr int T = W * W;                 // queries = keys of a block
   constexpr int KP = (T + 31) / 32 * 32;   // keys padded to whole 32-key steps (zero rows)
   constexpr int NWV = (T + 15) / 16;       // waves, 16 queries each
@@ -92,12 +98,23 @@ __global__ __launch_bounds__(64 * ((W * W + 15) / 16)) void wattn_local_residual
   __shared__ __align__(16) float sKV[D * KVS];    // [dim][channel]: sum_j relu(k_j)[ch] v_j[dim]
   __shared__ __align__(16) float sKS[D];          // sum_j relu(k_j)[ch]
 
-  // ---- task: (listed block, head); list entries outside the grid are skipped
-  const int listed = min(max(*count, 0), P.nblocks);
-  const int task = blockIdx.x;
-  if (task >= listed * P.H) return;
-  const int blk = list[task / P.H], h = task % P.H;
-  if (blk < 0 || blk >= P.nblocks) return;
+  // ---- task: (entry i, head h).  Workgroups are dealt to the 8 XCDs round-robin; workgroup
+  //      x + 8 r (x < 8) takes entry x + 8 (r / H) and head r % H, so the heads of a block,
+  //      whose rows share cache lines, meet in one XCD's L2.  An entry is a list position
+  //      (LISTED: entries past the count and entries outside the grid are skipped) or a block
+  //      (its gate must exceed tau; a NaN gate does not).
+  const int xr = blockIdx.x >> 3;
+  const int i = (blockIdx.x & 7) + 8 * (xr / P.H), h = xr - (xr / P.H) * P.H;
+  int blk;
+  if (LISTED) {
+    const int listed = min(max(*count, 0), P.nblocks);
+    if (i >= listed) return;
+    blk = list[i];
+    if (blk < 0 || blk >= P.nblocks) return;
+  } else {
+    if (i >= P.nblocks || !(gate[i] > tau)) return;
+    blk = i;
+  }
   const int b = blk / P.nW, rb = blk - b * P.nW;
   const int wy = rb / P.nWx, wx = rb - wy * P.nWx;
   const int y0 = wy * W, x0 = wx * W;
@@ -130,7 +147,21 @@ __global__ __launch_bounds__(64 * ((W * W + 15) / 16)) void wattn_local_residual
   const int qn = wave * 16 + c;
   const bool qvalid = qn < T;
   u32x4 Qf = {0u, 0u, 0u, 0u};
-  if (qvalid) Qf = *reinterpret_cast<const u32x4*>(q + tok_off(qn) + 8 * g);
+  // the lane's part of `out` (dims 16 db + 4 g .. + 3 of query qn), read now so that the
+  // read's latency passes while the block is computed
+  f32x4 base[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  u32x2 base16[2] = {{0u, 0u}, {0u, 0u}};
+  const int64_t qoff = tok_off(qn);
+  if (qvalid) {
+    Qf = *reinterpret_cast<const u32x4*>(q + qoff + 8 * g);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      if (OUTF32)
+        base[db] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(out) + qoff + 16 * db + 4 * g);
+      else
+        base16[db] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(out) + qoff + 16 * db + 4 * g);
+    }
+  }
   __syncthreads();
 
   // transposed-read coordinates: lane (c, g) of a 32-key step reads keys 8 g + (c >> 2) and
@@ -258,44 +289,49 @@ __global__ __launch_bounds__(64 * ((W * W + 15) / 16)) void wattn_local_residual
   // ---- out += O_local - O_lin-local (dims 16 db + 4 g .. + 3 of query qn)
   if (qvalid) {
     const float il = 1.0f / l, iden = 1.0f / den;
-    const int64_t o = tok_off(qn);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       float r[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = O[db][e] * il - Num[db][e] * iden;
       if (OUTF32) {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + o + 16 * db + 4 * g);
-        float4 cur = *p;
-        cur.x += r[0];
-        cur.y += r[1];
-        cur.z += r[2];
-        cur.w += r[3];
-        *p = cur;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + qoff + 16 * db + 4 * g) =
+            f32x4{base[db][0] + r[0], base[db][1] + r[1], base[db][2] + r[2], base[db][3] + r[3]};
       } else {
-        u32x2* p = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + o + 16 * db + 4 * g);
-        const u32x2 cur = *p;
-        *p = u32x2{pack_bf16(bf_lo(cur[0]) + r[0], bf_hi(cur[0]) + r[1]),
-                   pack_bf16(bf_lo(cur[1]) + r[2], bf_hi(cur[1]) + r[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + qoff + 16 * db + 4 * g) =
+            u32x2{pack_bf16(bf_lo(base16[db][0]) + r[0], bf_hi(base16[db][0]) + r[1]),
+                  pack_bf16(bf_lo(base16[db][1]) + r[2], bf_hi(base16[db][1]) + r[3])};
       }
     }
   }
 }
 
-template <int W>
+template <int W, bool LISTED>
 hipError_t launch_local_w(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v, void* out,
-                          const int* list, const int* count, hipStream_t stream) {
+                          const int* list, const int* count, const float* gate, float tau, hipStream_t stream) {
   constexpr int NT = 64 * ((W * W + 15) / 16);
-  const dim3 grid((unsigned)(P.nblocks * P.H));
+  const dim3 grid((unsigned)(8 * P.H * ((P.nblocks + 7) / 8)));
+  const uint16_t *q16 = static_cast<const uint16_t*>(q), *k16 = static_cast<const uint16_t*>(k),
+                 *v16 = static_cast<const uint16_t*>(v);
   if (out_f32)
-    hipLaunchKernelGGL((wattn_local_residual_kernel<W, true>), grid, dim3(NT), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), out, list, count, P);
+    hipLaunchKernelGGL((wattn_local_residual_kernel<W, true, LISTED>), grid, dim3(NT), 0, stream, q16, k16, v16,
+                       out, list, count, gate, tau, P);
   else
-    hipLaunchKernelGGL((wattn_local_residual_kernel<W, false>), grid, dim3(NT), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), out, list, count, P);
+    hipLaunchKernelGGL((wattn_local_residual_kernel<W, false, LISTED>), grid, dim3(NT), 0, stream, q16, k16, v16,
+                       out, list, count, gate, tau, P);
   return hipGetLastError();
+}
+
+template <bool LISTED>
+hipError_t launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v, void* out,
+                        const int* list, const int* count, const float* gate, float tau, hipStream_t stream) {
+  switch (P.w) {
+    case 4: return launch_local_w<4, LISTED>(P, out_f32, q, k, v, out, list, count, gate, tau, stream);
+    case 8: return launch_local_w<8, LISTED>(P, out_f32, q, k, v, out, list, count, gate, tau, stream);
+    case 12: return launch_local_w<12, LISTED>(P, out_f32, q, k, v, out, list, count, gate, tau, stream);
+    case 16: return launch_local_w<16, LISTED>(P, out_f32, q, k, v, out, list, count, gate, tau, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -307,11 +343,10 @@ hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, i
 
 hipError_t wattn_launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
                               void* out, const int* list, const int* count, hipStream_t stream) {
-  switch (P.w) {
-    case 4: return launch_local_w<4>(P, out_f32, q, k, v, out, list, count, stream);
-    case 8: return launch_local_w<8>(P, out_f32, q, k, v, out, list, count, stream);
-    case 12: return launch_local_w<12>(P, out_f32, q, k, v, out, list, count, stream);
-    case 16: return launch_local_w<16>(P, out_f32, q, k, v, out, list, count, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_local<true>(P, out_f32, q, k, v, out, list, count, nullptr, 0.f, stream);
+}
+
+hipError_t wattn_launch_gated(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
+                              void* out, const float* gate, float tau, hipStream_t stream) {
+  return launch_local<false>(P, out_f32, q, k, v, out, nullptr, nullptr, gate, tau, stream);
 }
