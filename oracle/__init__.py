@@ -31,3 +31,12 @@ from .hsmla_oracle import (  # noqa: F401
     gated_local_path,
     global_linear_attention,
 )
+from .cla_oracle import (  # noqa: F401
+    sigmoid,
+    depthwise3x3,
+    pointwise,
+    cla_gate_logits,
+    gated_window_attention,
+    gated_window_attention_backward,
+    cyclic_schedule,
+)
