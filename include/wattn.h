@@ -173,6 +173,63 @@ int wattn_backward(const void* q, const void* k, const void* v, const void* out,
                    float* dbias_u, float* dbias_v, int dtype, void* stream);
 
 /*
+ * Convolutional gate on the attention output (Rank-Factorized Implicit Neural Bias: Scaling
+ * Super-Resolution Transformer with FlashAttention, section 2.2): a 3x3 depth-wise and a 1x1
+ * point-wise convolution of the layer input give gate logits z, a sigmoid turns them into a
+ * gating map, and the map multiplies the attention output channel by channel:
+ *
+ *   out[b][y][x][h][j] = sigmoid(z[b][y][x][h][j]) * attention[b][y][x][h][j]
+ *
+ * wattn_forward_gated -- wattn_forward_lse (lse may be NULL here) with that product fused into
+ * the epilogue.
+ *   gate_z : device pointer, [B][Hgrid][Wgrid][H][d] in q's element type (the gate logits, e.g.
+ *            from wattn_cla_logits); read only; must not overlap out.  NULL: WATTN_ERR_NULL.
+ *   lse    : the attention's row statistic (before the gate), as in wattn_forward_lse, or NULL.
+ * dtype must be WATTN_BF16 or WATTN_BF16_OUT_FP32 (WATTN_ERR_DTYPE otherwise).  The sigmoid is
+ * 1 / (1 + 2^(-z log2 e)) in fp32 with the hardware exp2 and reciprocal.  Other arguments,
+ * checks and numerics are those of wattn_forward.
+ */
+int wattn_forward_gated(const void* q, const void* k, const void* v, void* out, float* lse, const void* gate_z,
+                        int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                        const float* theta, const void* bias_u, const void* bias_v, int r,
+                        int dtype, void* stream);
+
+/*
+ * wattn_backward_gated -- wattn_backward for out = sigmoid(z) * attention (out as written by
+ * wattn_forward_gated, lse from the same call), plus the gradient of the gate logits:
+ *   the attention's output gradient is dout * sigmoid(z), rowsum(dout * out) equals the
+ *   attention's rowsum(d_attention * attention), and
+ *   dgate_z = dout * out * (1 - sigmoid(z))   (float32 [B][Hgrid][Wgrid][H][d], written).
+ * gate_z, dgate_z : both required (WATTN_ERR_NULL); dgate_z must not overlap any other buffer.
+ * All other arguments, checks and numerics are those of wattn_backward.
+ */
+int wattn_backward_gated(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                         const float* lse, const void* gate_z, float* delta, float* dq, float* dk, float* dv,
+                         float* dtheta, float* dgate_z, int B, int H, int Hgrid, int Wgrid, int M, int shift,
+                         int d, const float* theta, const void* bias_u, const void* bias_v, int r,
+                         float* dbias_u, float* dbias_v, int dtype, void* stream);
+
+/*
+ * wattn_cla_logits -- the gate logits z = PW(DW3x3(x)) of the same section:
+ *   y[b][i][j][c] = b_dw[c] + sum_{di,dj in -1..1} w_dw[c][di+1][dj+1] x[b][i+di][j+dj][c]
+ *                   (x = 0 outside the grid: stride 1, zero padding 1, output the input's size)
+ *   z[b][i][j][o] = b_pw[o] + sum_c w_pw[o][c] y[b][i][j][c]
+ * with no activation between the two.
+ *
+ * x     : bfloat16 device pointer, [B][Hgrid][Wgrid][C] (channels last; with C = H * d this is
+ *         the attention's [B][Hgrid][Wgrid][H][d] layout, channel c = h * d + j); read only.
+ * w_dw  : float32 [C][3][3]; b_dw : float32 [C] or NULL (zero); w_pw : float32 [C][C] (output
+ *         channel major); b_pw : float32 [C] or NULL.  Device pointers, read only.
+ * z     : bfloat16 device pointer, [B][Hgrid][Wgrid][C], written; must not overlap an input.
+ * C     : 32 .. 256, a multiple of 32 (WATTN_ERR_HEAD_DIM otherwise).  dtype : WATTN_BF16.
+ * Numerics: the depth-wise sums in fp32, rounded to fp16 for the point-wise product (fp16
+ * matrix cores, fp32 accumulation; w_pw rounded to fp16), z rounded once to bf16.  Depth-wise
+ * outputs and w_pw entries must stay below 65504 in magnitude.
+ */
+int wattn_cla_logits(const void* x, const float* w_dw, const float* b_dw, const float* w_pw, const float* b_pw,
+                     void* z, int B, int Hgrid, int Wgrid, int C, int dtype, void* stream);
+
+/*
  * Gated local path of hybrid linear/softmax attention (HSMLA: Hierarchical Softmax
  * Multi-scale Linear Attention for Efficient Vision Transformers, technical summary section 2).
  * The global path is ReLU linear attention over all tokens; a learned gate shared by the heads

@@ -18,4 +18,5 @@ from .generate import (  # noqa: F401
     GATED_CONFIGS,
     block_gate,
     make_gated_inputs,
+    cla_params,
 )

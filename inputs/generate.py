@@ -25,6 +25,9 @@ Learned-parameter inputs:
   section 2: a learned gate per spatial block, about 30% of the blocks above the threshold).
   The gate network itself is a learned model part; the synthetic gates are i.i.d. uniform,
   so a threshold tau selects a fraction 1 - tau of the blocks in expectation.
+* ``cla_params``: seeded weights of the convolutional gate (RIB/SST page, section 2.2): a
+  3x3 depth-wise kernel per channel ~ N(0, 1/9), a C x C point-wise matrix ~ N(0, 1/C), and
+  biases ~ N(0, 0.1^2), so the gate logits of an N(0, 1) input are O(1).
 """
 
 from __future__ import annotations
@@ -229,6 +232,16 @@ def make_gated_inputs(cfg: GatedConfig, batch: int | None = None):
     gate = block_gate(B, cfg.Hg // cfg.w, cfg.Wg // cfg.w, cfg.seed + 3000)
     base = _rng(cfg.seed + 4000).standard_normal(size=shape, dtype=np.float32)
     return dict(q=q, k=k, v=v, gate=gate, base=base)
+
+
+def cla_params(C: int, seed: int):
+    """(w_dw [C][3][3], b_dw [C], w_pw [C][C], b_pw [C]) as float32."""
+    rng = _rng(seed)
+    w_dw = rng.normal(0.0, 1.0 / 3.0, size=(C, 3, 3)).astype(np.float32)
+    b_dw = rng.normal(0.0, 0.1, size=C).astype(np.float32)
+    w_pw = rng.normal(0.0, 1.0 / math.sqrt(C), size=(C, C)).astype(np.float32)
+    b_pw = rng.normal(0.0, 0.1, size=C).astype(np.float32)
+    return w_dw, b_dw, w_pw, b_pw
 
 
 def make_inputs(cfg: WorkloadConfig, batch: int | None = None, shared_theta: bool = True):

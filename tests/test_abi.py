@@ -35,7 +35,8 @@ def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
     assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_select_blocks",
-                     "wattn_local_residual", "wattn_gated_local", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
+                     "wattn_local_residual", "wattn_gated_local", "wattn_forward_gated", "wattn_backward_gated",
+                     "wattn_cla_logits", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -233,3 +234,83 @@ def test_gated_local_rejects_invalid_arguments(kw, status):
 def test_gated_local_valid_arguments_reach_the_device_check():
     assert _call_gated() in (8, 9)
     assert _call_gated(tau=float("nan"), w=16, dtype=0) in (8, 9)
+
+
+# ---- the convolutional gate: host-side rejections
+ZG, DZ, WD, WP, BD, BP = 0x1300000, 0x1400000, 0x1500000, 0x1600000, 0x1700000, 0x1800000
+
+
+def _call_fwd_gated(lse=None, gz=ZG, dtype=2, **kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, theta=None, bu=None, bv=None, r=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_forward_gated(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(lse), vp(gz), a["B"],
+                                      a["H"], a["Hg"], a["Wg"], a["M"], a["s"], a["d"], vp(a["theta"]), vp(a["bu"]),
+                                      vp(a["bv"]), a["r"], dtype, vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(gz=None), 1), (dict(q=None), 1), (dict(dtype=1), 6), (dict(M=0), 2), (dict(s=8), 3),
+        (dict(gz=P4 + 64), 7), (dict(lse=ZG), 7), (dict(d=16), 4),
+    ],
+)
+def test_forward_gated_rejects_invalid_arguments(kw, status):
+    assert _call_fwd_gated(**kw) == status
+
+
+def test_forward_gated_valid_arguments_reach_the_device_check():
+    assert _call_fwd_gated() in (8, 9)
+    assert _call_fwd_gated(lse=LS, dtype=0) in (8, 9)
+
+
+def _call_bwd_gated(**kw):
+    a = dict(q=P1, k=P2, v=P3, out=P4, dout=0x480000, lse=LS, gz=ZG, delta=DL, dq=G1, dk=G2, dv=G3, dtheta=None,
+             dz=DZ, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, theta=None, bu=None, bv=None, r=0, dbu=None, dbv=None,
+             dtype=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return _lib().wattn_backward_gated(vp(a["q"]), vp(a["k"]), vp(a["v"]), vp(a["out"]), vp(a["dout"]),
+                                       vp(a["lse"]), vp(a["gz"]), vp(a["delta"]), vp(a["dq"]), vp(a["dk"]),
+                                       vp(a["dv"]), vp(a["dtheta"]), vp(a["dz"]), a["B"], a["H"], a["Hg"], a["Wg"],
+                                       a["M"], a["s"], a["d"], vp(a["theta"]), vp(a["bu"]), vp(a["bv"]), a["r"],
+                                       vp(a["dbu"]), vp(a["dbv"]), a["dtype"], vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(gz=None), 1), (dict(dz=None), 1), (dict(dq=None), 1), (dict(dtype=1), 6), (dict(B=0), 2),
+        (dict(dz=ZG + 8), 7), (dict(dz=G1 + 4), 7), (dict(dq=ZG), 7), (dict(dz=P2), 7),
+    ],
+)
+def test_backward_gated_rejects_invalid_arguments(kw, status):
+    assert _call_bwd_gated(**kw) == status
+
+
+def test_backward_gated_valid_arguments_reach_the_device_check():
+    assert _call_bwd_gated() in (8, 9)
+
+
+def _call_cla(x=P1, wd=WD, bd=BD, wp=WP, bp=BP, z=P2, B=1, Hg=8, Wg=8, C=96, dtype=0):
+    vp = ctypes.c_void_p
+    return _lib().wattn_cla_logits(vp(x), vp(wd), vp(bd), vp(wp), vp(bp), vp(z), B, Hg, Wg, C, dtype, vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(x=None), 1), (dict(wd=None), 1), (dict(wp=None), 1), (dict(z=None), 1),
+        (dict(B=0), 2), (dict(Hg=-1), 2), (dict(Wg=70000), 2),
+        (dict(C=0), 4), (dict(C=48), 4), (dict(C=288), 4), (dict(dtype=1), 6), (dict(dtype=2), 6),
+        (dict(z=P1 + 32), 7), (dict(z=WP - 64), 7), (dict(z=BD), 7),
+    ],
+)
+def test_cla_logits_rejects_invalid_arguments(kw, status):
+    assert _call_cla(**kw) == status
+
+
+def test_cla_logits_valid_arguments_reach_the_device_check():
+    assert _call_cla() in (8, 9)
+    assert _call_cla(bd=None, bp=None, C=256) in (8, 9)

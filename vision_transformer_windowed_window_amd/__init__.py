@@ -26,6 +26,7 @@ import os
 __all__ = [
     "forward",
     "backward",
+    "cla_logits",
     "select_blocks",
     "local_residual",
     "gated_local_path",
@@ -91,6 +92,12 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_forward_lse.restype = ci
     lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
     lib.wattn_backward.restype = ci
+    lib.wattn_cla_logits.argtypes = [vp] * 6 + [ci] * 5 + [vp]
+    lib.wattn_cla_logits.restype = ci
+    lib.wattn_forward_gated.argtypes = [vp] * 6 + [ci] * 7 + [vp, vp, vp, ci, ci, vp]
+    lib.wattn_forward_gated.restype = ci
+    lib.wattn_backward_gated.argtypes = [vp] * 13 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
+    lib.wattn_backward_gated.restype = ci
     lib.wattn_select_blocks.argtypes = [vp, ci, ctypes.c_float, vp, vp, vp]
     lib.wattn_select_blocks.restype = ci
     lib.wattn_local_residual.argtypes = [vp] * 6 + [ci] * 6 + [ctypes.c_float, ci, vp]
@@ -125,14 +132,15 @@ def _ptr(t):
 
 
 def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=None, out=None,
-            out_dtype=None, stream=None, return_lse: bool = False):
+            out_dtype=None, stream=None, return_lse: bool = False, gate_z=None):
     """Shifted-window attention of (q, k, v) on the GPU; returns ``out`` ([B, Hg, Wg, H, d]).
 
     ``out_dtype`` (or the dtype of a given ``out``) may be torch.float32 for bfloat16
     inputs; by default the output has the input dtype.  The call is asynchronous on
     ``stream`` (default: torch's current stream).  With ``return_lse`` (bfloat16 inputs)
     it returns ``(out, lse)``, lse being the float32 [B, Hg, Wg, H] natural-log log-sum-exp
-    of every query row that ``backward`` needs.
+    of every query row that ``backward`` needs.  With ``gate_z`` (gate logits shaped and typed
+    like q, bfloat16 inputs only) the output is sigmoid(gate_z) * attention.
     """
     import torch
 
@@ -178,8 +186,15 @@ def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=
         raise ValueError("out must be a contiguous device tensor shaped like q")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    if return_lse:
-        lse = torch.empty((B, Hg, Wg, H), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hg, Wg, H), dtype=torch.float32, device=q.device) if return_lse else None
+    if gate_z is not None:
+        if gate_z.shape != q.shape or gate_z.dtype != q.dtype or not gate_z.is_cuda or not gate_z.is_contiguous():
+            raise ValueError("gate_z must be a contiguous device tensor shaped and typed like q")
+        st = lib.wattn_forward_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(gate_z), B, H, Hg, Wg, M, shift, d,
+            _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
+        )
+    elif return_lse:
         st = lib.wattn_forward_lse(
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hg, Wg, M, shift, d,
             _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, dtype, ctypes.c_void_p(stream),
@@ -195,11 +210,12 @@ def forward(q, k, v, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=
 
 
 def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bias_u=None, bias_v=None,
-             stream=None):
+             stream=None, gate_z=None):
     """Gradients of sum(dout * out) for the call ``out, lse = forward(q, k, v, ...,
     return_lse=True)``; returns float32 ``(dq, dk, dv, dtheta, dbias_u, dbias_v)`` (dtheta
     is None without theta, the bias gradients None without a bias).  q, k, v and the bias
-    factors are bfloat16; out and dout are both bfloat16 or both float32."""
+    factors are bfloat16; out and dout are both bfloat16 or both float32.  With ``gate_z`` (the
+    forward call's gate logits) it returns the float32 gradient of gate_z as a seventh value."""
     import torch
 
     lib = load_library()
@@ -236,6 +252,18 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bia
     dbv = None if bias_v is None else torch.empty(bias_v.shape, **f32)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    if gate_z is not None:
+        if gate_z.shape != q.shape or gate_z.dtype != q.dtype or not gate_z.is_cuda or not gate_z.is_contiguous():
+            raise ValueError("gate_z must be a contiguous device tensor shaped and typed like q")
+        dz = torch.empty(q.shape, **f32)
+        st = lib.wattn_backward_gated(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(gate_z), _ptr(delta), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dz), B, H, Hg, Wg, M, shift, d, _ptr(theta), _ptr(bias_u),
+            _ptr(bias_v), r, _ptr(dbu), _ptr(dbv), dtype, ctypes.c_void_p(stream),
+        )
+        if st != 0:
+            raise WattnError(st, status_string(st))
+        return dq, dk, dv, dtheta, dbu, dbv, dz
     st = lib.wattn_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(dtheta), B, H, Hg, Wg, M, shift, d, _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, _ptr(dbu), _ptr(dbv),
@@ -337,6 +365,34 @@ def gated_local_path(q, k, v, out, gate, tau: float, *, w: int, eps: float = 1e-
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.wattn_gated_local(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(gate), ctypes.c_float(tau),
                                B, H, Hg, Wg, w, d, ctypes.c_float(eps), dtype, ctypes.c_void_p(stream))
+    if st != 0:
+        raise WattnError(st, status_string(st))
+    return out
+
+
+def cla_logits(x, w_dw, w_pw, b_dw=None, b_pw=None, *, out=None, stream=None):
+    """Gate logits z = PW(DW3x3(x)) of the convolutional gate (zero padding, no activation
+    between).  x: bfloat16 [B, Hg, Wg, C] (or [B, Hg, Wg, H, d] with C = H * d); w_dw: float32
+    [C, 3, 3]; w_pw: float32 [C, C]; biases float32 [C] or None.  Returns z shaped like x."""
+    import torch
+
+    lib = load_library()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() < 4:
+        raise ValueError("x must be a contiguous bfloat16 device tensor [B, Hg, Wg, C] or [B, Hg, Wg, H, d]")
+    B, Hg, Wg = x.shape[:3]
+    C = x[0, 0, 0].numel()
+    for name, t, shape in (("w_dw", w_dw, (C, 3, 3)), ("w_pw", w_pw, (C, C)), ("b_dw", b_dw, (C,)),
+                           ("b_pw", b_pw, (C,))):
+        if t is None and name.startswith("b"):
+            continue
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 device tensor of shape {shape}")
+    if out is None:
+        out = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib.wattn_cla_logits(_ptr(x), _ptr(w_dw), _ptr(b_dw), _ptr(w_pw), _ptr(b_pw), _ptr(out), B, Hg, Wg, C,
+                              BF16, ctypes.c_void_p(stream))
     if st != 0:
         raise WattnError(st, status_string(st))
     return out

@@ -14,16 +14,18 @@
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
-                             const void* bv, float* lse, hipStream_t stream);
+                             const void* bv, float* lse, const void* gz, hipStream_t stream);
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* delta,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
-                            const void* bv, float* dbu, float* dbv, hipStream_t stream);
+                            const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream);
 hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, int* count, hipStream_t stream);
 hipError_t wattn_launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
                               void* out, const int* list, const int* count, hipStream_t stream);
 hipError_t wattn_launch_gated(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
                               void* out, const float* gate, float tau, hipStream_t stream);
+hipError_t wattn_launch_cla(const ClaPlan& P, const void* x, const float* w_dw, const float* b_dw, const float* w_pw,
+                            const float* b_pw, void* z, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -142,10 +144,11 @@ int pointer_ok(const void* p, size_t bytes) {
   return WATTN_OK;
 }
 
-// Forward pass shared by wattn_forward and wattn_forward_lse (lse may be NULL).
-int forward_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Hgrid,
-                 int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u, const void* bias_v,
-                 int r, int dtype, void* stream) {
+// Forward pass shared by wattn_forward, wattn_forward_lse and wattn_forward_gated (lse and the
+// gate logits gz may be NULL).
+int forward_impl(const void* q, const void* k, const void* v, void* out, float* lse, const void* gz, int B, int H,
+                 int Hgrid, int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
+                 const void* bias_v, int r, int dtype, void* stream) {
   // ---- argument checks (no HIP call before this block ends)
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return WATTN_ERR_NULL;
   int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
@@ -165,14 +168,16 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
   const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
   const size_t b_bytes = (size_t)H * M * M * r * esz;
   const Range ro{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + obytes};
-  const Range ins[6] = {
+  const Range ins[7] = {
       {reinterpret_cast<uintptr_t>(q), reinterpret_cast<uintptr_t>(q) + tbytes},
       {reinterpret_cast<uintptr_t>(k), reinterpret_cast<uintptr_t>(k) + tbytes},
       {reinterpret_cast<uintptr_t>(v), reinterpret_cast<uintptr_t>(v) + tbytes},
       {reinterpret_cast<uintptr_t>(theta), reinterpret_cast<uintptr_t>(theta) + (theta ? th_bytes : 0)},
       {reinterpret_cast<uintptr_t>(bias_u), reinterpret_cast<uintptr_t>(bias_u) + (bias_u ? b_bytes : 0)},
       {reinterpret_cast<uintptr_t>(bias_v), reinterpret_cast<uintptr_t>(bias_v) + (bias_v ? b_bytes : 0)},
+      {reinterpret_cast<uintptr_t>(gz), reinterpret_cast<uintptr_t>(gz) + (gz ? tbytes : 0)},
   };
+  if (gz != nullptr && dtype == WATTN_FP32) return WATTN_ERR_DTYPE;
   for (const Range& x : ins)
     if (x.hi > x.lo && overlaps(ro, x)) return WATTN_ERR_ALIAS;
   const size_t lse_bytes = (size_t)(elems / d) * sizeof(float);
@@ -204,9 +209,9 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
     (void)hipGetLastError();
     return WATTN_ERR_HIP;
   }
-  const void* ptrs[7] = {q, k, v, out, theta, bias_u, bias_v};
-  const size_t sizes[7] = {tbytes, tbytes, tbytes, obytes, th_bytes, b_bytes, b_bytes};
-  for (int i = 0; i < 7; ++i) {
+  const void* ptrs[8] = {q, k, v, out, theta, bias_u, bias_v, gz};
+  const size_t sizes[8] = {tbytes, tbytes, tbytes, obytes, th_bytes, b_bytes, b_bytes, tbytes};
+  for (int i = 0; i < 8; ++i) {
     st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
@@ -216,7 +221,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
   hipError_t e;
   if (dtype != WATTN_FP32)
     e = wattn_launch_bf16(plan, r > 0 ? 3 : 2, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, theta,
-                          bias_u, bias_v, lse, s);
+                          bias_u, bias_v, lse, gz, s);
   else
     e = wattn_launch_f32(fplan, r, q, k, v, out, theta, bias_u, bias_v, s);
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
@@ -227,27 +232,40 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
 extern "C" int wattn_forward(const void* q, const void* k, const void* v, void* out, int B, int H, int Hgrid,
                              int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
                              const void* bias_v, int r, int dtype, void* stream) {
-  return forward_impl(q, k, v, out, nullptr, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype,
-                      stream);
+  return forward_impl(q, k, v, out, nullptr, nullptr, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r,
+                      dtype, stream);
 }
 
 extern "C" int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
                                  int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
                                  const void* bias_u, const void* bias_v, int r, int dtype, void* stream) {
   if (lse == nullptr) return WATTN_ERR_NULL;
-  return forward_impl(q, k, v, out, lse, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype, stream);
+  return forward_impl(q, k, v, out, lse, nullptr, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype,
+                      stream);
 }
 
-extern "C" int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                              const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta, int B,
-                              int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
-                              const void* bias_u, const void* bias_v, int r, float* dbias_u, float* dbias_v,
-                              int dtype, void* stream) {
+extern "C" int wattn_forward_gated(const void* q, const void* k, const void* v, void* out, float* lse,
+                                   const void* gate_z, int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                                   const float* theta, const void* bias_u, const void* bias_v, int r, int dtype,
+                                   void* stream) {
+  if (gate_z == nullptr) return WATTN_ERR_NULL;
+  return forward_impl(q, k, v, out, lse, gate_z, B, H, Hgrid, Wgrid, M, shift, d, theta, bias_u, bias_v, r, dtype,
+                      stream);
+}
+
+namespace {
+
+// Backward pass shared by wattn_backward and wattn_backward_gated (gz and dz both NULL or both set).
+int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                  const void* gz, float* delta, float* dq, float* dk, float* dv, float* dtheta, float* dz, int B,
+                  int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
+                  const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype, void* stream) {
   // ---- argument checks (no HIP call before this block ends)
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
       delta == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return WATTN_ERR_NULL;
   if ((theta == nullptr) != (dtheta == nullptr)) return WATTN_ERR_NULL;
+  if ((gz == nullptr) != (dz == nullptr)) return WATTN_ERR_NULL;
   int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
   if (st != WATTN_OK) return st;
   if (d != 32) return WATTN_ERR_HEAD_DIM;
@@ -270,11 +288,12 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
   auto rng = [](const void* p, size_t n) {
     return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
   };
-  const Range ins[9] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
-                        rng(lse, rbytes), rng(theta, th_bytes), rng(bias_u, b_bytes), rng(bias_v, b_bytes)};
-  const Range outs[7] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
-                         rng(dtheta, th_bytes), rng(dbias_u, db_bytes), rng(dbias_v, db_bytes)};
-  for (int i = 0; i < 7; ++i) {
+  const Range ins[10] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
+                         rng(lse, rbytes), rng(theta, th_bytes), rng(bias_u, b_bytes), rng(bias_v, b_bytes),
+                         rng(gz, tbytes)};
+  const Range outs[8] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
+                         rng(dtheta, th_bytes), rng(dbias_u, db_bytes), rng(dbias_v, db_bytes), rng(dz, fbytes)};
+  for (int i = 0; i < 8; ++i) {
     if (outs[i].hi == outs[i].lo) continue;
     for (const Range& x : ins)
       if (x.hi > x.lo && overlaps(outs[i], x)) return WATTN_ERR_ALIAS;
@@ -290,17 +309,40 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
     (void)hipGetLastError();
     return WATTN_ERR_HIP;
   }
-  const void* ptrs[16] = {q, k, v, out, dout, lse, delta, dq, dk, dv, theta, dtheta, bias_u, bias_v, dbias_u, dbias_v};
-  const size_t sizes[16] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes, fbytes,
-                            th_bytes, th_bytes, b_bytes, b_bytes, db_bytes, db_bytes};
-  for (int i = 0; i < 16; ++i) {
+  const void* ptrs[18] = {q,     k,  v,      out,    dout,   lse,     delta,   dq, dk,
+                          dv,    theta, dtheta, bias_u, bias_v, dbias_u, dbias_v, gz, dz};
+  const size_t sizes[18] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes,
+                            fbytes, th_bytes, th_bytes, b_bytes, b_bytes, db_bytes, db_bytes, tbytes, fbytes};
+  for (int i = 0; i < 18; ++i) {
     st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
   const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
-                                        lse, delta, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v,
-                                        static_cast<hipStream_t>(stream));
+                                        lse, delta, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v, gz,
+                                        dz, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta, int B,
+                              int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
+                              const void* bias_u, const void* bias_v, int r, float* dbias_u, float* dbias_v,
+                              int dtype, void* stream) {
+  return backward_impl(q, k, v, out, dout, lse, nullptr, delta, dq, dk, dv, dtheta, nullptr, B, H, Hgrid, Wgrid, M,
+                       shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream);
+}
+
+extern "C" int wattn_backward_gated(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                    const float* lse, const void* gate_z, float* delta, float* dq, float* dk,
+                                    float* dv, float* dtheta, float* dgate_z, int B, int H, int Hgrid, int Wgrid,
+                                    int M, int shift, int d, const float* theta, const void* bias_u,
+                                    const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype,
+                                    void* stream) {
+  if (gate_z == nullptr || dgate_z == nullptr) return WATTN_ERR_NULL;
+  return backward_impl(q, k, v, out, dout, lse, gate_z, delta, dq, dk, dv, dtheta, dgate_z, B, H, Hgrid, Wgrid, M,
+                       shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream);
 }
 
 extern "C" int wattn_select_blocks(const float* gate, int nblocks, float tau, int* list, int* count, void* stream) {
@@ -392,6 +434,44 @@ extern "C" int wattn_gated_local(const void* q, const void* k, const void* v, vo
                                  float tau, int B, int H, int Hgrid, int Wgrid, int w, int d, float eps, int dtype,
                                  void* stream) {
   return local_impl(q, k, v, out, nullptr, nullptr, gate, tau, B, H, Hgrid, Wgrid, w, d, eps, dtype, stream, false);
+}
+
+extern "C" int wattn_cla_logits(const void* x, const float* w_dw, const float* b_dw, const float* w_pw,
+                                const float* b_pw, void* z, int B, int Hgrid, int Wgrid, int C, int dtype,
+                                void* stream) {
+  if (x == nullptr || w_dw == nullptr || w_pw == nullptr || z == nullptr) return WATTN_ERR_NULL;
+  if (B <= 0 || Hgrid <= 0 || Wgrid <= 0 || Hgrid > 65535 || Wgrid > 65535) return WATTN_ERR_SHAPE;
+  if (C < 32 || C > 256 || C % 32 != 0) return WATTN_ERR_HEAD_DIM;
+  if (dtype != WATTN_BF16) return WATTN_ERR_DTYPE;
+  const int64_t elems = (int64_t)B * Hgrid * Wgrid * C;
+  if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
+  const size_t tbytes = (size_t)elems * 2, dw_bytes = (size_t)C * 9 * 4, pw_bytes = (size_t)C * C * 4,
+               b_bytes = (size_t)C * 4;
+  auto rng = [](const void* p, size_t n) {
+    return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
+  };
+  const Range rz = rng(z, tbytes);
+  const Range ins[5] = {rng(x, tbytes), rng(w_dw, dw_bytes), rng(b_dw, b_bytes), rng(w_pw, pw_bytes),
+                        rng(b_pw, b_bytes)};
+  for (const Range& r : ins)
+    if (r.hi > r.lo && overlaps(rz, r)) return WATTN_ERR_ALIAS;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  const void* ptrs[6] = {x, w_dw, b_dw, w_pw, b_pw, z};
+  const size_t sizes[6] = {tbytes, dw_bytes, b_bytes, pw_bytes, b_bytes, tbytes};
+  for (int i = 0; i < 6; ++i) {
+    const int st = pointer_ok(ptrs[i], sizes[i]);
+    if (st != WATTN_OK) return st;
+  }
+  ClaPlan P;
+  P.B = B; P.Hg = Hgrid; P.Wg = Wgrid; P.C = C;
+  const int64_t tiles = (elems / C + 63) / 64;
+  P.grid = (int)std::min<int64_t>(tiles, 2048);
+  const hipError_t e = wattn_launch_cla(P, x, w_dw, b_dw, w_pw, b_pw, z, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 
 extern "C" int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift) {

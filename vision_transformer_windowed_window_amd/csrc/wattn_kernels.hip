@@ -68,6 +68,12 @@ namespace {
 #include "wattn_device.h"
 
 constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
+
+// 1 / (1 + e^-z) with the hardware exp2 and reciprocal (fp32, about 1 ulp each); z = -inf
+// gives 0, z = +inf gives 1, NaN stays NaN.
+__device__ __forceinline__ float sigmoidf_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * LOG2E));
+}
 constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
 
 struct Task {
@@ -175,7 +181,7 @@ __device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt,
 __host__ __device__ constexpr int table_stride(int NW) { return NW == 2 ? 18 : (NW == 4 ? 26 : 130); }
 
 // NW waves per workgroup (2, 4 or 8): 32 NW queries, key tiles of 16 NW keys.
-template <int NW, int NKS, bool ROPE, bool OUTF32>
+template <int NW, int NKS, bool ROPE, bool OUTF32, bool GATE>
 __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
@@ -184,6 +190,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
                                                               const uint16_t* __restrict__ bu,
                                                               const uint16_t* __restrict__ bv,
                                                               float* __restrict__ lse,
+                                                              const uint16_t* __restrict__ gz,
                                                               const WattnPlan P) {
   constexpr bool BIAS = (NKS == 3);
   constexpr int NTHR = 64 * NW;  // threads
@@ -536,7 +543,13 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       if (lse != nullptr && g == 0) lse[off / D] = (m[a] + __log2f(lt)) * LN2;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const f32x4 o = O[db][a] * inv;
+        f32x4 o = O[db][a] * inv;
+        if (GATE) {  // out = sigmoid(z) * attention, z in q's type at the output position
+          const u32x2 zr = *reinterpret_cast<const u32x2*>(gz + off + 16 * db + 4 * g);
+          const float z[4] = {bf_lo(zr[0]), bf_hi(zr[0]), bf_lo(zr[1]), bf_hi(zr[1])};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] *= sigmoidf_fast(z[e]);
+        }
         if (OUTF32) {
           *reinterpret_cast<float4*>(static_cast<float*>(out) + off + 16 * db + 4 * g) =
               make_float4(o[0], o[1], o[2], o[3]);
@@ -802,12 +815,13 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 }
 
 // ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
-template <int NW, bool ROPE, bool OUTF32, bool BIAS>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
 __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu, const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu,
+    const uint16_t* __restrict__ gz, float* __restrict__ dz, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sK[2][KT * D];
@@ -851,6 +865,23 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) Dp += go[e] * o[e];
       L2 = lse[qoff[a] / D] * LOG2E;
+      if (GATE) {
+        // out is sigmoid(z) * attention: the attention's output gradient is dout * sigmoid(z),
+        // dz = dout * out * (1 - sigmoid(z)), and D = rowsum(dout * out) is unchanged
+        const u32x4 zr = *reinterpret_cast<const u32x4*>(gz + qoff[a] + 8 * g);
+        float gzv[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float s0 = sigmoidf_fast(bf_lo(zr[p])), s1 = sigmoidf_fast(bf_hi(zr[p]));
+          gzv[2 * p] = go[2 * p] * o[2 * p] * (1.0f - s0);
+          gzv[2 * p + 1] = go[2 * p + 1] * o[2 * p + 1] * (1.0f - s1);
+          go[2 * p] *= s0;
+          go[2 * p + 1] *= s1;
+        }
+        float* dst = dz + qoff[a] + 8 * g;
+        *reinterpret_cast<float4*>(dst) = make_float4(gzv[0], gzv[1], gzv[2], gzv[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(gzv[4], gzv[5], gzv[6], gzv[7]);
+      }
     } else {
       qraw[a] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1063,12 +1094,13 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
-template <int NW, bool ROPE, bool OUTF32, bool BIAS>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv, const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
+    const uint16_t* __restrict__ gz, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sQ[2][QTT * D];
@@ -1138,6 +1170,14 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     pq = *reinterpret_cast<const u32x4*>(q + X.img + off);
     float go[8];
     load8<OUTF32>(dout, X.img + off, go);
+    if (GATE) {  // the attention's output gradient: dout * sigmoid(z)
+      const u32x4 zr = *reinterpret_cast<const u32x4*>(gz + X.img + off);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        go[2 * p] *= sigmoidf_fast(bf_lo(zr[p]));
+        go[2 * p + 1] *= sigmoidf_fast(bf_hi(zr[p]));
+      }
+    }
 #pragma unroll
     for (int p = 0; p < 4; ++p) po[p] = pack_bf16(go[2 * p], go[2 * p + 1]);
     lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
@@ -1347,45 +1387,55 @@ __global__ void wattn_fill_zero_kernel(float* __restrict__ p, int n) {
 // Launchers (C++ linkage, internal to the library)
 // ------------------------------------------------------------------------------------
 
-template <int NW, int NKS, bool ROPE, bool OUTF32>
+template <int NW, int NKS, bool ROPE, bool OUTF32, bool GATE>
 static hipError_t launch_bf16_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, void* out,
-                                   const float* theta, const void* bu, const void* bv, float* lse,
+                                   const float* theta, const void* bu, const void* bv, float* lse, const void* gz,
                                    hipStream_t stream) {
   if (ROPE && plan.M > table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)table_stride(NW) * (D / 2) * sizeof(float2) : 0;
-  hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NW, NKS, ROPE, OUTF32>), dim3(plan.grid), dim3(64 * NW), table_bytes,
-                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  hipLaunchKernelGGL((wattn_fwd_bf16_kernel<NW, NKS, ROPE, OUTF32, GATE>), dim3(plan.grid), dim3(64 * NW),
+                     table_bytes, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, theta, static_cast<const uint16_t*>(bu),
-                     static_cast<const uint16_t*>(bv), lse, plan);
+                     static_cast<const uint16_t*>(bv), lse, static_cast<const uint16_t*>(gz), plan);
   return hipGetLastError();
 }
 
-template <int NW>
+template <int NW, bool GATE>
 static hipError_t launch_bf16_nw(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                                  const void* k, const void* v, void* out, const float* theta, const void* bu,
-                                 const void* bv, float* lse, hipStream_t stream) {
+                                 const void* bv, float* lse, const void* gz, hipStream_t stream) {
+#define WATTN_FWD_ARGS plan, q, k, v, out, theta, bu, bv, lse, gz, stream
   const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: return launch_bf16_inst<NW, 2, false, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 1: return launch_bf16_inst<NW, 2, false, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 2: return launch_bf16_inst<NW, 2, true, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 3: return launch_bf16_inst<NW, 2, true, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 4: return launch_bf16_inst<NW, 3, false, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 5: return launch_bf16_inst<NW, 3, false, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    case 6: return launch_bf16_inst<NW, 3, true, false>(plan, q, k, v, out, theta, bu, bv, lse, stream);
-    default: return launch_bf16_inst<NW, 3, true, true>(plan, q, k, v, out, theta, bu, bv, lse, stream);
+    case 0: return launch_bf16_inst<NW, 2, false, false, GATE>(WATTN_FWD_ARGS);
+    case 1: return launch_bf16_inst<NW, 2, false, true, GATE>(WATTN_FWD_ARGS);
+    case 2: return launch_bf16_inst<NW, 2, true, false, GATE>(WATTN_FWD_ARGS);
+    case 3: return launch_bf16_inst<NW, 2, true, true, GATE>(WATTN_FWD_ARGS);
+    case 4: return launch_bf16_inst<NW, 3, false, false, GATE>(WATTN_FWD_ARGS);
+    case 5: return launch_bf16_inst<NW, 3, false, true, GATE>(WATTN_FWD_ARGS);
+    case 6: return launch_bf16_inst<NW, 3, true, false, GATE>(WATTN_FWD_ARGS);
+    default: return launch_bf16_inst<NW, 3, true, true, GATE>(WATTN_FWD_ARGS);
+  }
+#undef WATTN_FWD_ARGS
+}
+
+template <bool GATE>
+static hipError_t launch_bf16_gate(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
+                                   const void* k, const void* v, void* out, const float* theta, const void* bu,
+                                   const void* bv, float* lse, const void* gz, hipStream_t stream) {
+  switch (plan.nw) {
+    case 2: return launch_bf16_nw<2, GATE>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, gz, stream);
+    case 4: return launch_bf16_nw<4, GATE>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, gz, stream);
+    case 8: return launch_bf16_nw<8, GATE>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, gz, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
-                             const void* bv, float* lse, hipStream_t stream) {
-  switch (plan.nw) {
-    case 2: return launch_bf16_nw<2>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
-    case 4: return launch_bf16_nw<4>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
-    case 8: return launch_bf16_nw<8>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, stream);
-    default: return hipErrorInvalidValue;
-  }
+                             const void* bv, float* lse, const void* gz, hipStream_t stream) {
+  return gz != nullptr ? launch_bf16_gate<true>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, gz, stream)
+                       : launch_bf16_gate<false>(plan, nks, rope, out_f32, q, k, v, out, theta, bu, bv, lse, gz, stream);
 }
 
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
@@ -1405,11 +1455,11 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
 }
 
 // ---- backward launchers
-template <int NW, bool ROPE, bool OUTF32, bool BIAS>
+template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
 static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, const void* out,
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
-                                  float* dbv, hipStream_t stream) {
+                                  float* dbv, const void* gz, float* dz, hipStream_t stream) {
   if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
@@ -1417,32 +1467,35 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   auto V = static_cast<const uint16_t*>(v);
   auto BU = static_cast<const uint16_t*>(bu);
   auto BV = static_cast<const uint16_t*>(bv);
-  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes,
-                     stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, plan);
+  auto GZ = static_cast<const uint16_t*>(gz);
+  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
+                     table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz,
+                     plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes,
-                     stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv,
-                     plan);
+  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
+                     table_bytes, stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta,
+                     BU, BV, dbv, GZ, plan);
   return hipGetLastError();
 }
 
-template <int NW>
+template <int NW, bool GATE>
 static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, bool bias, const void* q,
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
                                 float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
-                                const void* bu, const void* bv, float* dbu, float* dbv, hipStream_t stream) {
-#define WATTN_BWD_ARGS plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, stream
+                                const void* bu, const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
+                                hipStream_t stream) {
+#define WATTN_BWD_ARGS plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, stream
   const int sel = (bias ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: return launch_bwd_inst<NW, false, false, false>(WATTN_BWD_ARGS);
-    case 1: return launch_bwd_inst<NW, false, true, false>(WATTN_BWD_ARGS);
-    case 2: return launch_bwd_inst<NW, true, false, false>(WATTN_BWD_ARGS);
-    case 3: return launch_bwd_inst<NW, true, true, false>(WATTN_BWD_ARGS);
-    case 4: return launch_bwd_inst<NW, false, false, true>(WATTN_BWD_ARGS);
-    case 5: return launch_bwd_inst<NW, false, true, true>(WATTN_BWD_ARGS);
-    case 6: return launch_bwd_inst<NW, true, false, true>(WATTN_BWD_ARGS);
-    default: return launch_bwd_inst<NW, true, true, true>(WATTN_BWD_ARGS);
+    case 0: return launch_bwd_inst<NW, false, false, false, GATE>(WATTN_BWD_ARGS);
+    case 1: return launch_bwd_inst<NW, false, true, false, GATE>(WATTN_BWD_ARGS);
+    case 2: return launch_bwd_inst<NW, true, false, false, GATE>(WATTN_BWD_ARGS);
+    case 3: return launch_bwd_inst<NW, true, true, false, GATE>(WATTN_BWD_ARGS);
+    case 4: return launch_bwd_inst<NW, false, false, true, GATE>(WATTN_BWD_ARGS);
+    case 5: return launch_bwd_inst<NW, false, true, true, GATE>(WATTN_BWD_ARGS);
+    case 6: return launch_bwd_inst<NW, true, false, true, GATE>(WATTN_BWD_ARGS);
+    default: return launch_bwd_inst<NW, true, true, true, GATE>(WATTN_BWD_ARGS);
   }
 #undef WATTN_BWD_ARGS
 }
@@ -1450,7 +1503,7 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* delta,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
-                            const void* bv, float* dbu, float* dbv, hipStream_t stream) {
+                            const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream) {
   const bool bias = bu != nullptr;
   auto fill = [&](float* p, int64_t cnt) {
     hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, p,
@@ -1463,11 +1516,13 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
     const int64_t cnt = (int64_t)plan.H * plan.M * plan.M * 16;
     if ((e = fill(dbu, cnt)) != hipSuccess || (e = fill(dbv, cnt)) != hipSuccess) return e;
   }
+#define WATTN_BWD_ARGS plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
+                       dbu, dbv, gz, dz, stream
+  const bool gate = gz != nullptr;
   switch (plan.nw) {
-    case 2: return launch_bwd_nw<2>(plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta,
-                                    theta, bu, bv, dbu, dbv, stream);
-    case 4: return launch_bwd_nw<4>(plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta,
-                                    theta, bu, bv, dbu, dbv, stream);
+    case 2: return gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS);
+    case 4: return gate ? launch_bwd_nw<4, true>(WATTN_BWD_ARGS) : launch_bwd_nw<4, false>(WATTN_BWD_ARGS);
     default: return hipErrorInvalidValue;
   }
+#undef WATTN_BWD_ARGS
 }

@@ -60,3 +60,10 @@ struct LocalPlan {
   int64_t img_stride;  // elements of one image: Hg * Wg * H * d
   float eps;           // denominator guard of the linear attention
 };
+
+// Launch description of the gate-logit convolutions: the token grid, the channel count and the
+// number of workgroups (each loops over tiles of 64 tokens).
+struct ClaPlan {
+  int B, Hg, Wg, C;
+  int grid;
+};
