@@ -15,7 +15,10 @@ output gradient, all resident), timed the same way.  With --pass gated a step is
 local path of hybrid linear/softmax attention on the dense grid with 8 x 8 (or 16 x 16)
 blocks: one wattn_gated_local call (the ~30% of blocks whose gate exceeds tau get
 out += O_local - O_lin-local, in place); the list form (wattn_select_blocks followed by
-wattn_local_residual) is timed beside it.
+wattn_local_residual) is timed beside it.  With --pass stack a step runs six window-attention
+layers over the SR-style grid (8 x 192 x 192 tokens, 6 heads x 32) whose windows cycle 16, 32,
+64 (shifted on every second layer), each with a rank-16 bias and the convolutional gate: per
+layer wattn_cla_logits on the layer input, then wattn_forward_gated.
 """
 
 from __future__ import annotations
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "window-attn tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
 METRIC_BWD = "window-attn backward tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
+METRIC_STACK = "window-attn stack tokens/s (cyclic windows 16/32/64, rank-16 bias, convolutional gate), SR grid"
 METRIC_GATED = "gated local path tokens/s (routing + local softmax residual), % of HBM peak, p=2 grid"
 WARMUP_MIN_S = 0.5          # untimed back-to-back launches before timing (clock ramp)
 WARMUP_MAX_STEPS = 20000
@@ -58,8 +62,9 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated"],
-                    help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack"],
+                    help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path; "
+                         "stack: six layers with cyclic windows and the convolutional gate")
     return ap.parse_args()
 
 
@@ -321,6 +326,162 @@ def main_gated(args):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_baseline_stack(cfg, budget_s: float):
+    """Time the float64 oracle on random window-heads of every layer of the stack (gate logits
+    of the window's tokens included), scaled to tokens through the whole stack."""
+    import numpy as np
+
+    import oracle
+    from inputs import make_stack_layer
+
+    rng = np.random.default_rng(0)
+    per_layer = budget_s / len(cfg.layers)
+    s_per_token = 0.0
+    parts = []
+    for l, (M, shift) in enumerate(cfg.layers):
+        inp = make_stack_layer(cfg, l, batch=1)
+        z = oracle.cla_gate_logits(inp["x"], inp["w_dw"], inp["b_dw"], inp["w_pw"], inp["b_pw"]).reshape(
+            inp["q"].shape)
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            wy, wx, h = int(rng.integers(cfg.Hg // M)), int(rng.integers(cfg.Wg // M)), int(rng.integers(cfg.H))
+            o, ys, xs = oracle.window_head_output(inp["q"], inp["k"], inp["v"], M, shift, 0, wy, wx, h, None,
+                                                  inp["bias_u"], inp["bias_v"])
+            _ = o * oracle.sigmoid(z[0, ys, xs, h])
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= per_layer:
+                break
+        t_conv = time.perf_counter()
+        oracle.cla_gate_logits(inp["x"][:, :16], inp["w_dw"], inp["b_dw"], inp["w_pw"], inp["b_pw"])
+        conv_per_token = (time.perf_counter() - t_conv) / (16 * cfg.Wg)
+        s_per_token += el / (done * M * M / cfg.H) + conv_per_token
+        parts.append(f"M={M}: {done} window-heads")
+    return {
+        "value": 1.0 / s_per_token,
+        "unit": "tokens/s",
+        "cores": os.cpu_count(),
+        "kind": "oracle",
+        "sample": "random window-heads of each layer (" + ", ".join(parts) + f", {budget_s:.0f} s in all) and "
+                  "the gate logits of a 16-row strip per layer, numpy float64 with materialised scores, "
+                  "scaled to tokens through all six layers",
+    }
+
+
+def main_stack(args):
+    """--pass stack: the cyclic-window stack with the convolutional gate."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from inputs import STACK_CONFIGS, make_stack_layer
+
+    cfg = STACK_CONFIGS["sst_cycle_sr"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf, f32 = torch.bfloat16, torch.float32
+    layers = []
+    for l in range(len(cfg.layers)):
+        inp = make_stack_layer(cfg, l)
+        t = {key: torch.from_numpy(inp[key]).to(bf).to(dev) for key in ("q", "k", "v", "x", "bias_u", "bias_v")}
+        t.update({key: torch.from_numpy(inp[key]).to(dev) for key in ("w_dw", "b_dw", "w_pw", "b_pw")})
+        t["z"] = torch.empty_like(t["x"])
+        t["out"] = torch.empty_like(t["q"])
+        layers.append(t)
+        del inp
+
+    def conv(l):
+        t = layers[l]
+        wattn.cla_logits(t["x"], t["w_dw"], t["w_pw"], t["b_dw"], t["b_pw"], out=t["z"])
+
+    def attn(l):
+        t = layers[l]
+        M, shift = cfg.layers[l]
+        wattn.forward(t["q"], t["k"], t["v"], M=M, shift=shift, bias_u=t["bias_u"], bias_v=t["bias_v"],
+                      out=t["out"], gate_z=t["z"].view(t["q"].shape))
+
+    def step(i):
+        for l in range(len(layers)):
+            conv(l)
+            attn(l)
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or (time.perf_counter() - t_w < WARMUP_MIN_S and i < WARMUP_MAX_STEPS):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_s = ev0.elapsed_time(ev1) / args.steps / 1e3
+
+    # per-kernel averages, each kernel launched back to back on its own
+    def timed(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    reps = max(3, args.steps // 5)
+    per_layer = []
+    dense_total = 0.0
+    for l, (M, shift) in enumerate(cfg.layers):
+        t_conv = timed(lambda: conv(l), reps)
+        t_attn = timed(lambda: attn(l), reps)
+        dense = 4.0 * cfg.tokens * M * M * cfg.d * cfg.H
+        pairs = wattn.pair_count(cfg.B, cfg.H, cfg.Hg, cfg.Wg, M, shift)
+        executed = 2.0 * pairs * (cfg.d + cfg.r + cfg.d)
+        dense_total += dense
+        per_layer.append({"M": M, "shift": shift, "cla_logits_ms": t_conv * 1e3, "attention_ms": t_attn * 1e3,
+                          "attention_tflops_dense": dense / t_attn / 1e12,
+                          "attention_tflops_executed": executed / t_attn / 1e12,
+                          "cla_logits_gbs": 4.0 * cfg.tokens * cfg.C / t_conv / 1e9})
+    # the dominant kernel: the gated attention of the slowest layer
+    dom = max(range(len(per_layer)), key=lambda l: per_layer[l]["attention_ms"])
+    achieved = per_layer[dom]["attention_tflops_dense"]
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": f"wattn_forward_gated, layer {dom} (M={cfg.layers[dom][0]}, shift={cfg.layers[dom][1]})"}
+    rec = {
+        "metric": METRIC_STACK,
+        "value": cfg.tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v and layer inputs rounded to bf16; seeded RIB-MLP bias factors "
+                "and gate convolution weights per layer)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hgrid": cfg.Hg, "Wgrid": cfg.Wg, "H": cfg.H, "d": cfg.d,
+                   "r": cfg.r, "layers": [list(x) for x in cfg.layers], "out_dtype": "bf16",
+                   "global_batch": cfg.B, "tokens_per_step": cfg.tokens,
+                   "pass": "per layer: wattn_cla_logits + wattn_forward_gated"},
+        "kernel_ms_avg": step_s * 1e3,
+        "tflops_dense_stack": dense_total / step_s / 1e12,
+        "per_layer": per_layer,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_stack(cfg, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -330,6 +491,9 @@ def main():
         sys.exit(2)
     if args.which == "gated":
         main_gated(args)
+        return
+    if args.which == "stack":
+        main_stack(args)
         return
 
     import numpy as np

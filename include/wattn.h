@@ -222,6 +222,7 @@ int wattn_backward_gated(const void* q, const void* k, const void* v, const void
  *         channel major); b_pw : float32 [C] or NULL.  Device pointers, read only.
  * z     : bfloat16 device pointer, [B][Hgrid][Wgrid][C], written; must not overlap an input.
  * C     : 32 .. 256, a multiple of 32 (WATTN_ERR_HEAD_DIM otherwise).  dtype : WATTN_BF16.
+ * B * Hgrid * Wgrid must stay below 2^31 tokens (WATTN_ERR_SHAPE).
  * Numerics: the depth-wise sums in fp32, rounded to fp16 for the point-wise product (fp16
  * matrix cores, fp32 accumulation; w_pw rounded to fp16), z rounded once to bf16.  Depth-wise
  * outputs and w_pw entries must stay below 65504 in magnitude.

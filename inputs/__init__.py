@@ -19,4 +19,7 @@ from .generate import (  # noqa: F401
     block_gate,
     make_gated_inputs,
     cla_params,
+    StackConfig,
+    STACK_CONFIGS,
+    make_stack_layer,
 )

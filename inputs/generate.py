@@ -93,16 +93,17 @@ CONFIGS = {
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32.
 
-    NaN stays NaN; values beyond the bf16 range round to +-inf as IEEE rounding does.
+    NaN stays NaN; values beyond the bf16 range round to +-inf as IEEE rounding does.  The
+    32-bit sum cannot wrap for a non-NaN input (the largest pattern, -inf = 0xFF800000, plus
+    0x8000 stays below 2^32).
     """
     a = np.ascontiguousarray(x, dtype=np.float32)
-    bits = a.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
-    out = (rounded & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    bits = a.view(np.uint32)
+    rounded = bits + (np.uint32(0x7FFF) + ((bits >> 16) & np.uint32(1)))
+    rounded &= np.uint32(0xFFFF0000)
+    out = rounded.view(np.float32)
     nan = np.isnan(a)
     if nan.any():
-        out = out.copy()
         out[nan] = np.nan
     return out.reshape(a.shape)
 
@@ -232,6 +233,51 @@ def make_gated_inputs(cfg: GatedConfig, batch: int | None = None):
     gate = block_gate(B, cfg.Hg // cfg.w, cfg.Wg // cfg.w, cfg.seed + 3000)
     base = _rng(cfg.seed + 4000).standard_normal(size=shape, dtype=np.float32)
     return dict(q=q, k=k, v=v, gate=gate, base=base)
+
+
+@dataclasses.dataclass(frozen=True)
+class StackConfig:
+    """A stack of window-attention layers with a per-layer window schedule (RIB/SST page,
+    section 2.3), the convolutional gate on every layer's output (section 2.2) and a rank-r
+    bias per layer (section 2.1).  ``layers`` lists (M, shift) per layer."""
+    name: str
+    B: int
+    Hg: int
+    Wg: int
+    H: int
+    d: int
+    layers: tuple
+    r: int
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.Hg * self.Wg
+
+    @property
+    def C(self) -> int:
+        return self.H * self.d
+
+
+# The SR-style grid (8 x 192 x 192 tokens, 6 heads x 32) through six layers whose windows
+# cycle 16, 32, 64, shifted on every second layer, each with a rank-16 bias and the gate.
+STACK_CONFIGS = {
+    "sst_cycle_sr": StackConfig("sst_cycle_sr", 8, 192, 192, 6, 32,
+                                ((16, 0), (32, 16), (64, 0), (16, 8), (32, 0), (64, 32)), 16, 1007),
+}
+
+
+def make_stack_layer(cfg: StackConfig, layer: int, batch: int | None = None):
+    """Inputs of one layer of a stack: q, k, v and the layer input x (bf16-exact float32), the
+    gate's convolution weights, and the bias factors for the layer's window side."""
+    B = cfg.B if batch is None else batch
+    M = cfg.layers[layer][0]
+    seed = cfg.seed + 10 * layer
+    q, k, v = qkv((B, cfg.Hg, cfg.Wg, cfg.H, cfg.d), seed, "bf16")
+    x = round_bf16(_rng(seed + 4).standard_normal(size=(B, cfg.Hg, cfg.Wg, cfg.C), dtype=np.float32))
+    w_dw, b_dw, w_pw, b_pw = cla_params(cfg.C, seed + 5)
+    U, V = rib_factors(cfg.H, M, cfg.r, seed + 7, "bf16") if cfg.r else (None, None)
+    return dict(q=q, k=k, v=v, x=x, w_dw=w_dw, b_dw=b_dw, w_pw=w_pw, b_pw=b_pw, bias_u=U, bias_v=V)
 
 
 def cla_params(C: int, seed: int):

@@ -131,3 +131,30 @@ def test_logits_feed_the_gated_forward_pass():
     z_ref = round_bf16(oracle.cla_gate_logits(x, w_dw, b_dw, w_pw, b_pw).astype(np.float32)).reshape(q.shape)
     ref = oracle.gated_window_attention(q, k, v, z_ref, M, s, th)
     check(out.cpu().numpy().astype(np.float64), ref, "bf16", "logits -> gated forward")
+
+
+def test_cyclic_stack_layers_match_oracle():
+    """A reduced stack (one image of 64 x 64 tokens, 2 heads): every layer of the cyclic schedule
+    16, 32, 64 with its rank-16 bias and gate, computed as bench.py's stack pass does."""
+    import dataclasses
+
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from inputs import STACK_CONFIGS, make_stack_layer
+
+    cfg = dataclasses.replace(STACK_CONFIGS["sst_cycle_sr"], B=1, Hg=64, Wg=64, H=2,
+                              layers=tuple(oracle.cyclic_schedule(6)))
+    for l, (M, shift) in enumerate(cfg.layers):
+        inp = make_stack_layer(cfg, l)
+        d = {key: _dev(inp[key], torch.bfloat16) for key in ("q", "k", "v", "x", "bias_u", "bias_v")}
+        d.update({key: _dev(inp[key], torch.float32) for key in ("w_dw", "b_dw", "w_pw", "b_pw")})
+        z = wattn.cla_logits(d["x"], d["w_dw"], d["w_pw"], d["b_dw"], d["b_pw"])
+        out = wattn.forward(d["q"], d["k"], d["v"], M=M, shift=shift, bias_u=d["bias_u"], bias_v=d["bias_v"],
+                            out_dtype=torch.float32, gate_z=z.view(d["q"].shape))
+        torch.cuda.synchronize()
+        z_ref = round_bf16(oracle.cla_gate_logits(inp["x"], inp["w_dw"], inp["b_dw"], inp["w_pw"],
+                                                  inp["b_pw"]).astype(np.float32)).reshape(inp["q"].shape)
+        ref = oracle.gated_window_attention(inp["q"], inp["k"], inp["v"], z_ref, M, shift, None, inp["bias_u"],
+                                            inp["bias_v"])
+        check(out.cpu().numpy().astype(np.float64), ref, "bf16", f"stack layer {l} M={M} shift={shift}")

@@ -444,7 +444,7 @@ extern "C" int wattn_cla_logits(const void* x, const float* w_dw, const float* b
   if (C < 32 || C > 256 || C % 32 != 0) return WATTN_ERR_HEAD_DIM;
   if (dtype != WATTN_BF16) return WATTN_ERR_DTYPE;
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * C;
-  if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
+  if (elems >= kMaxElems || (int64_t)B * Hgrid * Wgrid >= (1LL << 31)) return WATTN_ERR_SHAPE;
   const size_t tbytes = (size_t)elems * 2, dw_bytes = (size_t)C * 9 * 4, pw_bytes = (size_t)C * C * 4,
                b_bytes = (size_t)C * 4;
   auto rng = [](const void* p, size_t n) {

@@ -72,37 +72,41 @@ __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t*
   const int64_t ntiles = (ntok + CLA_TILE - 1) / CLA_TILE;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * CLA_TILE;
-    // ---- depth-wise: CLA_TILE * CH items of 8 channels
+    // ---- depth-wise: CLA_TILE * CH items of 8 channels.  The nine taps' loads are issued
+    //      together from clamped (in-bounds) addresses; taps outside the grid get weight 0.
+#pragma unroll 2
     for (int it = tid; it < CLA_TILE * CH; it += NT) {
       const int tl = it / CH, ch = it - tl * CH;
-      const int64_t t = t0 + tl;
+      const uint32_t t = (uint32_t)min(t0 + tl, ntok - 1);  // fewer than 2^31 tokens
+      const uint32_t img = t / (uint32_t)(P.Hg * P.Wg);
+      const uint32_t rem = t - img * (uint32_t)(P.Hg * P.Wg);
+      const int yy = (int)(rem / (uint32_t)P.Wg), xx = (int)rem - yy * P.Wg;
+      u32x4 xr[9];
+      bool ok[9];
+#pragma unroll
+      for (int tap = 0; tap < 9; ++tap) {
+        const int py = yy + tap / 3 - 1, px = xx + tap % 3 - 1;
+        ok[tap] = py >= 0 && py < P.Hg && px >= 0 && px < P.Wg;
+        const int cy = ok[tap] ? py : yy, cx = ok[tap] ? px : xx;
+        xr[tap] = *reinterpret_cast<const u32x4*>(x + ((int64_t)(img * P.Hg + cy) * P.Wg + cx) * C + 8 * ch);
+      }
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = sB[8 * ch + e];
-      if (t < ntok) {
-        const int64_t img = t / ((int64_t)P.Hg * P.Wg);
-        const int rem = (int)(t - img * P.Hg * P.Wg);
-        const int yy = rem / P.Wg, xx = rem - yy * P.Wg;
 #pragma unroll
-        for (int dy = -1; dy <= 1; ++dy) {
-#pragma unroll
-          for (int dx = -1; dx <= 1; ++dx) {
-            const int py = yy + dy, px = xx + dx;
-            if (py < 0 || py >= P.Hg || px < 0 || px >= P.Wg) continue;
-            const u32x4 xr = *reinterpret_cast<const u32x4*>(x + ((img * P.Hg + py) * P.Wg + px) * C + 8 * ch);
-            const float* wt = &sW[((dy + 1) * 3 + (dx + 1)) * C + 8 * ch];
-            const float4 w0 = *reinterpret_cast<const float4*>(wt);
-            const float4 w1 = *reinterpret_cast<const float4*>(wt + 4);
-            acc[0] = fmaf(w0.x, bf_lo(xr[0]), acc[0]);
-            acc[1] = fmaf(w0.y, bf_hi(xr[0]), acc[1]);
-            acc[2] = fmaf(w0.z, bf_lo(xr[1]), acc[2]);
-            acc[3] = fmaf(w0.w, bf_hi(xr[1]), acc[3]);
-            acc[4] = fmaf(w1.x, bf_lo(xr[2]), acc[4]);
-            acc[5] = fmaf(w1.y, bf_hi(xr[2]), acc[5]);
-            acc[6] = fmaf(w1.z, bf_lo(xr[3]), acc[6]);
-            acc[7] = fmaf(w1.w, bf_hi(xr[3]), acc[7]);
-          }
-        }
+      for (int tap = 0; tap < 9; ++tap) {
+        const float* wt = &sW[tap * C + 8 * ch];
+        const float4 w0 = *reinterpret_cast<const float4*>(wt);
+        const float4 w1 = *reinterpret_cast<const float4*>(wt + 4);
+        const float m = ok[tap] ? 1.0f : 0.0f;
+        acc[0] = fmaf(w0.x * m, bf_lo(xr[tap][0]), acc[0]);
+        acc[1] = fmaf(w0.y * m, bf_hi(xr[tap][0]), acc[1]);
+        acc[2] = fmaf(w0.z * m, bf_lo(xr[tap][1]), acc[2]);
+        acc[3] = fmaf(w0.w * m, bf_hi(xr[tap][1]), acc[3]);
+        acc[4] = fmaf(w1.x * m, bf_lo(xr[tap][2]), acc[4]);
+        acc[5] = fmaf(w1.y * m, bf_hi(xr[tap][2]), acc[5]);
+        acc[6] = fmaf(w1.z * m, bf_lo(xr[tap][3]), acc[6]);
+        acc[7] = fmaf(w1.w * m, bf_hi(xr[tap][3]), acc[7]);
       }
       *reinterpret_cast<u32x4*>(&sY[tl * YS + 8 * ch]) =
           u32x4{pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3]), pack_f16(acc[4], acc[5]), pack_f16(acc[6], acc[7])};
