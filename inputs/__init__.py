@@ -22,4 +22,9 @@ from .generate import (  # noqa: F401
     StackConfig,
     STACK_CONFIGS,
     make_stack_layer,
+    ModelConfig,
+    MODEL_CONFIGS,
+    block_params,
+    model_params,
+    images,
 )

@@ -280,6 +280,89 @@ def make_stack_layer(cfg: StackConfig, layer: int, batch: int | None = None):
     return dict(q=q, k=k, v=v, x=x, w_dw=w_dw, b_dw=b_dw, w_pw=w_pw, b_pw=b_pw, bias_u=U, bias_v=V)
 
 
+@dataclasses.dataclass(frozen=True)
+class ModelConfig:
+    """A FlashSwin-T forward pass: image side, patch size p (stem kernel 2p - 1, stride p), window
+    side M, embedding C, depths and heads per stage (d = C_s / heads_s = 32), classes."""
+    name: str
+    B: int
+    img: int
+    p: int
+    M: int
+    C: int = 96
+    depths: tuple = (2, 2, 6, 2)
+    heads: tuple = (3, 6, 12, 24)
+    n_classes: int = 1000
+    seed: int = 1008
+
+    @property
+    def tokens(self) -> int:
+        return self.B * (self.img // self.p) ** 2
+
+
+# FlashSwin-T at 256 px: patch 4 with M = 32, and the dense patch-2 grid with M = 32.
+MODEL_CONFIGS = {
+    "flashswin_t_p4_m32": ModelConfig("flashswin_t_p4_m32", 64, 256, 4, 32),
+    "flashswin_t_p2_m32": ModelConfig("flashswin_t_p2_m32", 16, 256, 2, 32),
+}
+
+
+def _block_params(rng, C: int, dtype: str):
+    def w(o, i):
+        return rng.normal(0.0, 1.0 / math.sqrt(i), size=(o, i)).astype(np.float32)
+
+    def small(n):
+        return rng.normal(0.0, 0.02, size=n).astype(np.float32)
+
+    P = dict(ln1_g=1.0 + small(C), ln1_b=small(C), w_qkv=w(3 * C, C), b_qkv=small(3 * C),
+             w_proj=w(C, C), b_proj=small(C), ln2_g=1.0 + small(C), ln2_b=small(C),
+             w_fc1=w(4 * C, C), b_fc1=small(4 * C), w_fc2=w(C, 4 * C), b_fc2=small(C))
+    if dtype == "bf16":
+        for key in ("w_qkv", "w_proj", "w_fc1", "w_fc2"):
+            P[key] = round_bf16(P[key])
+    return {k: np.asarray(v, np.float32) for k, v in P.items()}
+
+
+def block_params(C: int, seed: int, dtype: str = "bf16"):
+    """Seeded weights of one block: matrices ~ N(0, 1/fan_in) (rounded to bf16 for the bf16
+    path), norm gains 1 + N(0, 0.02^2), biases N(0, 0.02^2), all float32 arrays."""
+    return _block_params(_rng(seed), C, dtype)
+
+
+def model_params(cfg: ModelConfig, dtype: str = "bf16"):
+    """Seeded weights of the whole FlashSwin-T forward pass (structure as flashswin_forward
+    expects): stem convolution and norm, per stage its blocks, RoPE table and patch merging,
+    the final norm and the head."""
+    rng = _rng(cfg.seed)
+    k = 2 * cfg.p - 1
+    rb = (lambda a: round_bf16(a)) if dtype == "bf16" else (lambda a: a)
+    params = dict(stem_w=rb(rng.normal(0.0, 1.0 / math.sqrt(3 * k * k), size=(cfg.C, 3, k, k)).astype(np.float32)),
+                  stem_b=rng.normal(0.0, 0.02, size=cfg.C).astype(np.float32),
+                  stem_ln_g=(1.0 + rng.normal(0.0, 0.02, size=cfg.C)).astype(np.float32),
+                  stem_ln_b=rng.normal(0.0, 0.02, size=cfg.C).astype(np.float32), stages=[])
+    C = cfg.C
+    for s, (depth, heads) in enumerate(zip(cfg.depths, cfg.heads)):
+        st = dict(heads=heads, blocks=[_block_params(rng, C, dtype) for _ in range(depth)],
+                  theta=theta_table(heads, C // heads, 0.1, cfg.seed + 100 + s), merge=None)
+        if s + 1 < len(cfg.depths):
+            st["merge"] = dict(ln_g=(1.0 + rng.normal(0.0, 0.02, size=4 * C)).astype(np.float32),
+                               ln_b=rng.normal(0.0, 0.02, size=4 * C).astype(np.float32),
+                               w=rb(rng.normal(0.0, 1.0 / math.sqrt(4 * C), size=(2 * C, 4 * C)).astype(np.float32)))
+            C *= 2
+        params["stages"].append(st)
+    params["norm_g"] = (1.0 + rng.normal(0.0, 0.02, size=C)).astype(np.float32)
+    params["norm_b"] = rng.normal(0.0, 0.02, size=C).astype(np.float32)
+    params["head_w"] = rb(rng.normal(0.0, 1.0 / math.sqrt(C), size=(cfg.n_classes, C)).astype(np.float32))
+    params["head_b"] = np.zeros(cfg.n_classes, np.float32)
+    return params
+
+
+def images(B: int, side: int, seed: int, dtype: str = "bf16"):
+    """[B][side][side][3] images ~ N(0, 1) (NHWC), bf16-exact for the bf16 path."""
+    a = _rng(seed).standard_normal(size=(B, side, side, 3), dtype=np.float32)
+    return round_bf16(a) if dtype == "bf16" else a
+
+
 def cla_params(C: int, seed: int):
     """(w_dw [C][3][3], b_dw [C], w_pw [C][C], b_pw [C]) as float32."""
     rng = _rng(seed)

@@ -40,3 +40,13 @@ from .cla_oracle import (  # noqa: F401
     gated_window_attention_backward,
     cyclic_schedule,
 )
+from .model_oracle import (  # noqa: F401
+    layernorm,
+    linear,
+    gelu,
+    stem_conv,
+    patch_merge,
+    swin_block,
+    stage_window,
+    flashswin_forward,
+)
