@@ -300,6 +300,89 @@ int wattn_gated_local(const void* q, const void* k, const void* v, void* out, co
                       int B, int H, int Hgrid, int Wgrid, int w, int d, float eps, int dtype, void* stream);
 
 /*
+ * Model steps around the window attention (FLASHSWIN page, "How it works": Swin's hierarchy is
+ * kept, with an overlapping stem -- a convolution with kernel 2p - 1, stride p, padding p - 1 --
+ * in place of the patch embedding).  Activations are token-major bfloat16 [tokens][channels];
+ * linear weights bfloat16 [out][in]; biases, norm gains and norm biases float32.  Every call
+ * validates on the host first, launches on `stream` and allocates nothing.
+ */
+#define WATTN_ACT_NONE 0
+#define WATTN_ACT_GELU 1 /* exact GELU: 0.5 x (1 + erf(x / sqrt 2)) */
+
+/*
+ * wattn_linear -- y = act(x W^T + bias) (+ residual), fp32 accumulation on bf16 matrix cores.
+ *   x : [M][K] bf16; W : [N][K] bf16; bias : [N] float32 or NULL; residual : bf16 laid out like
+ *   y, or NULL (it may be y itself: an in-place residual update).
+ *   y : bf16 (dtype WATTN_BF16) or float32 (WATTN_BF16_OUT_FP32: no act, no residual).  Output
+ *       column n of token m goes to (n / split) * M * split + m * split + n % split: split = N
+ *       gives a plain [M][N] matrix, split = C with N = 3C gives q, k, v as three [M][C] tensors.
+ *   K % 32 == 0, N % 4 == 0, split % 4 == 0, N % split == 0 (WATTN_ERR_SHAPE); act one of
+ *   WATTN_ACT_* (WATTN_ERR_VALUE).  y must not overlap x, W or bias (WATTN_ERR_ALIAS).
+ */
+int wattn_linear(const void* x, const void* W, const float* bias, const void* residual, void* y, int M, int N,
+                 int K, int split, int act, int dtype, void* stream);
+
+/*
+ * wattn_layernorm -- y[t] = (x[t] - mean) / sqrt(var + eps) * gamma + beta over the C channels
+ * of each of T tokens (biased variance from fp32 sums).  x, y : [T][C] bf16 (no overlap);
+ * gamma, beta : [C] float32.  C % 8 == 0; eps > 0 and finite (WATTN_ERR_VALUE).
+ */
+int wattn_layernorm(const void* x, const float* gamma, const float* beta, void* y, int64_t T, int C, float eps,
+                    void* stream);
+
+/*
+ * wattn_patch_merge_norm -- the gather and norm of patch merging: output token (b, i, j) of
+ * [B][Hgrid/2][Wgrid/2] is the layer norm of the 4C vector concatenating input tokens
+ * (2i, 2j), (2i+1, 2j), (2i, 2j+1), (2i+1, 2j+1) of x [B][Hgrid][Wgrid][C].  y : [..][4C] bf16;
+ * gamma, beta : [4C] float32.  Hgrid, Wgrid even; the 4C -> 2C reduction is a wattn_linear.
+ */
+int wattn_patch_merge_norm(const void* x, const float* gamma, const float* beta, void* y, int B, int Hgrid,
+                           int Wgrid, int C, float eps, void* stream);
+
+/*
+ * wattn_stem_conv -- the overlapping stem: y[b][i][j][o] = bias[o] + sum_{c, di, dj < 2p-1}
+ * W[o][c][di][dj] img[b][p i + di - (p-1)][p j + dj - (p-1)][c], zero outside the image.
+ *   img : [B][Himg][Wimg][Cin] bf16 (NHWC); W : [Cout][Cin][2p-1][2p-1] bf16; bias : [Cout]
+ *   float32; y : [B][Himg/p][Wimg/p][Cout] bf16.  Himg, Wimg multiples of p; Cout % 8 == 0; the
+ *   weights must fit 64 KB as float32 ((2p-1)^2 Cin Cout <= 16384).  fp32 sums.
+ */
+int wattn_stem_conv(const void* img, const void* W, const float* bias, void* y, int B, int Himg, int Wimg, int Cin,
+                    int Cout, int p, void* stream);
+
+/* wattn_token_mean -- y[b][c] = mean over the n tokens of x[b][.][c]; x [B][n][C], y [B][C] bf16. */
+int wattn_token_mean(const void* x, void* y, int B, int n, int C, void* stream);
+
+/* Parameters of one pre-norm transformer block (device pointers; theta may be NULL). */
+typedef struct {
+  const float* ln1_g;  /* [C] */
+  const float* ln1_b;  /* [C] */
+  const void* w_qkv;   /* [3C][C] bf16: rows 0..C-1 give q, C..2C-1 k, 2C..3C-1 v (head h = c / 32) */
+  const float* b_qkv;  /* [3C] or NULL */
+  const void* w_proj;  /* [C][C] bf16 */
+  const float* b_proj; /* [C] or NULL */
+  const float* ln2_g;  /* [C] */
+  const float* ln2_b;  /* [C] */
+  const void* w_fc1;   /* [4C][C] bf16 */
+  const float* b_fc1;  /* [4C] or NULL */
+  const void* w_fc2;   /* [C][4C] bf16 */
+  const float* b_fc2;  /* [C] or NULL */
+  const float* theta;  /* [H][16] RoPE frequencies, or NULL */
+} wattn_block_params_t;
+
+/* Workspace bytes wattn_swin_block needs (10 * B * Hgrid * Wgrid * C); -1 for bad sizes. */
+int64_t wattn_swin_block_workspace(int B, int Hgrid, int Wgrid, int C);
+
+/*
+ * wattn_swin_block -- one pre-norm block in place on x [B][Hgrid][Wgrid][C] bf16 (C = 32 H):
+ *   x += proj(attention(LN1(x)))      attention: wattn_forward with window M, shift, theta
+ *   x += fc2(GELU(fc1(LN2(x))))       (norm eps 1e-5, MLP width 4C)
+ * workspace : device memory of at least wattn_swin_block_workspace(...) bytes (caller-owned,
+ * scratch); it must not overlap x.  Seven kernels on `stream`.  Sizes follow wattn_forward.
+ */
+int wattn_swin_block(void* x, const wattn_block_params_t* p, void* workspace, int64_t workspace_bytes, int B,
+                     int Hgrid, int Wgrid, int C, int H, int M, int shift, void* stream);
+
+/*
  * wattn_pair_count -- number of (query, key) pairs with a finite logit in a call with
  * these sizes (the masked pairs of wrapped windows excluded).  Pure host arithmetic:
  * no HIP call, no side effect.  Returns -1 for sizes wattn_forward would reject with

@@ -36,7 +36,9 @@ def test_exports_every_declared_symbol():
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
     assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_select_blocks",
                      "wattn_local_residual", "wattn_gated_local", "wattn_forward_gated", "wattn_backward_gated",
-                     "wattn_cla_logits", "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
+                     "wattn_cla_logits", "wattn_linear", "wattn_layernorm", "wattn_patch_merge_norm",
+                     "wattn_stem_conv", "wattn_token_mean", "wattn_swin_block_workspace", "wattn_swin_block",
+                     "wattn_pair_count", "wattn_status_string", "wattn_abi_version"}
     lib = _lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -314,3 +316,79 @@ def test_cla_logits_rejects_invalid_arguments(kw, status):
 def test_cla_logits_valid_arguments_reach_the_device_check():
     assert _call_cla() in (8, 9)
     assert _call_cla(bd=None, bp=None, C=256) in (8, 9)
+
+
+# ---- model steps: host-side rejections
+XA, WA, BA, YA = 0x2000000, 0x2400000, 0x2800000, 0x2C00000
+
+
+def _call_linear(x=XA, w=WA, b=BA, r=None, y=YA, M=64, N=96, K=96, split=96, act=0, dtype=0):
+    vp = ctypes.c_void_p
+    return _lib().wattn_linear(vp(x), vp(w), vp(b), vp(r), vp(y), M, N, K, split, act, dtype, vp(None))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(x=None), 1), (dict(w=None), 1), (dict(y=None), 1),
+        (dict(M=0), 2), (dict(N=0), 2), (dict(K=48), 2), (dict(N=98, split=98), 2), (dict(split=64), 2),
+        (dict(split=0), 2), (dict(act=2), 10), (dict(dtype=1), 6), (dict(dtype=2, act=1), 6),
+        (dict(dtype=2, r=YA), 6), (dict(y=XA + 64), 7), (dict(y=WA), 7), (dict(y=BA - 8), 7),
+        (dict(r=YA + 2), 7),
+    ],
+)
+def test_linear_rejects_invalid_arguments(kw, status):
+    assert _call_linear(**kw) == status
+
+
+def test_linear_valid_arguments_reach_the_device_check():
+    assert _call_linear() in (8, 9)
+    assert _call_linear(r=YA, act=0) in (8, 9)           # in-place residual
+    assert _call_linear(N=288, split=96) in (8, 9)       # q, k, v split
+    assert _call_linear(b=None, dtype=2) in (8, 9)
+
+
+def test_norm_stem_mean_reject_invalid_arguments():
+    vp, f = ctypes.c_void_p, ctypes.c_float
+    lib = _lib()
+    assert lib.wattn_layernorm(vp(None), vp(WA), vp(BA), vp(YA), 16, 96, f(1e-5), vp(None)) == 1
+    assert lib.wattn_layernorm(vp(XA), vp(WA), vp(BA), vp(YA), 16, 100, f(1e-5), vp(None)) == 2
+    assert lib.wattn_layernorm(vp(XA), vp(WA), vp(BA), vp(YA), 0, 96, f(1e-5), vp(None)) == 2
+    assert lib.wattn_layernorm(vp(XA), vp(WA), vp(BA), vp(YA), 16, 96, f(0.0), vp(None)) == 10
+    assert lib.wattn_layernorm(vp(XA), vp(WA), vp(BA), vp(XA + 32), 16, 96, f(1e-5), vp(None)) == 7
+    assert lib.wattn_layernorm(vp(XA), vp(WA), vp(BA), vp(YA), 16, 96, f(1e-5), vp(None)) in (8, 9)
+    assert lib.wattn_patch_merge_norm(vp(XA), vp(WA), vp(BA), vp(YA), 1, 7, 8, 96, f(1e-5), vp(None)) == 2
+    assert lib.wattn_patch_merge_norm(vp(XA), vp(WA), vp(BA), vp(YA), 1, 8, 8, 96, f(1e-5), vp(None)) in (8, 9)
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 4, vp(None)) in (8, 9)
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 62, 64, 3, 96, 4, vp(None)) == 2
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 100, 4, vp(None)) == 2
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 8, vp(None)) == 2  # LDS
+    assert lib.wattn_stem_conv(vp(None), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 4, vp(None)) == 1
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(XA + 64), 1, 64, 64, 3, 96, 4, vp(None)) == 7
+    assert lib.wattn_token_mean(vp(XA), vp(YA), 2, 64, 768, vp(None)) in (8, 9)
+    assert lib.wattn_token_mean(vp(XA), vp(XA), 2, 64, 768, vp(None)) == 7
+    assert lib.wattn_token_mean(vp(XA), vp(YA), 0, 64, 768, vp(None)) == 2
+
+
+def test_swin_block_rejects_invalid_arguments():
+    vp = ctypes.c_void_p
+    lib = _lib()
+    full = wattn.BlockParams(*([0x3000000 + 0x10000 * i for i in range(12)] + [None]))
+    assert lib.wattn_swin_block_workspace(1, 32, 32, 96) == 32 * 32 * 96 * 10
+    assert lib.wattn_swin_block_workspace(0, 32, 32, 96) == -1
+    ws = 0x4000000
+    wsb = 32 * 32 * 96 * 10
+    call = lambda p=full, x=XA, w=ws, wb=wsb, C=96, H=3, M=8, s=0, Hg=32: lib.wattn_swin_block(
+        vp(x), ctypes.byref(p) if p is not None else None, vp(w), wb, 1, Hg, 32, C, H, M, s, vp(None))
+    assert call() in (8, 9)
+    assert call(x=None) == 1
+    assert call(w=None) == 1
+    missing = wattn.BlockParams(*([0x3000000 + 0x10000 * i for i in range(12)] + [None]))
+    missing.w_fc1 = None
+    assert call(p=missing) == 1
+    assert call(wb=wsb - 1) == 2
+    assert call(C=64, H=3) == 4
+    assert call(C=96, H=2) == 4
+    assert call(M=12) == 2
+    assert call(s=8) == 3
+    assert call(w=XA + 64) == 7

@@ -1,0 +1,147 @@
+"""GPU parity of the model steps around the attention (through the C ABI) against the float64
+oracle on the same seeded inputs: linear layers (plain, q/k/v split, GELU, in-place residual,
+float32 output, ragged M and N), layer norm, the patch-merging gather and norm, the stem at
+p = 2 and 4, the token mean, one transformer block, and a miniature FlashSwin-T forward pass.
+
+Bounds.  Single kernels with a bf16 output: rel-L2 <= 5e-3 and max(|err| - 2^-8 |ref|) <= 1e-2
+(the attention's bf16-output bound).  One block: rel-L2 <= 1e-2 (the block rounds seven
+intermediate tensors to bf16, each adding up to 2^-9 relative).  The miniature model (four
+blocks, a merge, the head): rel-L2 <= 1e-2 on the logits.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from inputs import ModelConfig, block_params, images, model_params, round_bf16, theta_table
+from parity_util import check, errors, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, dt):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(torch.device("cuda:0"))
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _bf(shape, seed, scale=1.0):
+    return round_bf16((scale * np.random.default_rng(seed).standard_normal(size=shape)).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,split,act,res,f32", [
+    (4096, 288, 96, 96, 0, False, False),     # qkv projection, split into q, k, v
+    (1000, 384, 96, 384, 1, False, False),    # fc1 + GELU, ragged M
+    (3000, 96, 384, 96, 0, True, False),      # fc2 + residual, in place
+    (16, 1000, 768, 1000, 0, False, True),    # head: fp32 logits, N not a multiple of 16
+    (77, 68, 32, 68, 0, False, False),        # ragged M and N
+])
+def test_linear_matches_oracle(M, N, K, split, act, res, f32):
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    note(f"linear M={M} N={N} K={K} split={split} act={act} res={res} f32={f32}")
+    x, W = _bf((M, K), M + K), _bf((N, K), N + K + 1, 1.0 / np.sqrt(K))
+    b = np.random.default_rng(N).normal(0, 0.1, size=N).astype(np.float32)
+    r = _bf((M, N), 5) if res else None
+    tx, tW, tb = _dev(x, torch.bfloat16), _dev(W, torch.bfloat16), _dev(b, torch.float32)
+    if res:
+        tr = _dev(r, torch.bfloat16)
+        out = wattn.linear(tx, tW, tb, residual=tr, out=tr)
+    else:
+        out = wattn.linear(tx, tW, tb, act=act, split=split,
+                           out_dtype=torch.float32 if f32 else None)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x, W, b)
+    if act == 1:
+        ref = oracle.gelu(ref)
+    if res:
+        ref = ref + r
+    got = _np(out)
+    if split != N:
+        got = got.transpose(1, 0, 2).reshape(M, N)  # [parts][M][split] -> [M][N]
+    check(got, ref, "bf16", f"linear {M}x{N}x{K}", out_bf16=not f32)
+
+
+def test_layernorm_and_patch_merge_match_oracle():
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    x = round_bf16(_bf((2, 16, 24, 96), 11, 2.0) + np.float32(0.5))
+    g = (1.0 + np.random.default_rng(12).normal(0, 0.1, 96)).astype(np.float32)
+    b = np.random.default_rng(13).normal(0, 0.1, 96).astype(np.float32)
+    y = wattn.layernorm(_dev(x, torch.bfloat16), _dev(g, torch.float32), _dev(b, torch.float32))
+    torch.cuda.synchronize()
+    check(_np(y), oracle.layernorm(x, g, b), "bf16", "layernorm C=96", out_bf16=True)
+    g4 = (1.0 + np.random.default_rng(14).normal(0, 0.1, 384)).astype(np.float32)
+    b4 = np.random.default_rng(15).normal(0, 0.1, 384).astype(np.float32)
+    W = _bf((192, 384), 16, 1.0 / np.sqrt(384))
+    m = wattn.patch_merge_norm(_dev(x, torch.bfloat16), _dev(g4, torch.float32), _dev(b4, torch.float32))
+    z = wattn.linear(m, _dev(W, torch.bfloat16), None)
+    torch.cuda.synchronize()
+    cat = np.concatenate([x[:, 0::2, 0::2], x[:, 1::2, 0::2], x[:, 0::2, 1::2], x[:, 1::2, 1::2]], axis=-1)
+    check(_np(m), oracle.layernorm(cat, g4, b4), "bf16", "merge norm", out_bf16=True)
+    check(_np(z), oracle.patch_merge(x, g4, b4, W), "bf16", "patch merge", out_bf16=True)
+
+
+@pytest.mark.parametrize("p,side,B", [(2, 64, 2), (4, 64, 3), (4, 36, 1)])
+def test_stem_and_token_mean_match_oracle(p, side, B):
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    k = 2 * p - 1
+    img = images(B, side, 20 + p, "bf16")
+    W = _bf((96, 3, k, k), 21 + p, 1.0 / np.sqrt(3 * k * k))
+    b = np.random.default_rng(22).normal(0, 0.1, 96).astype(np.float32)
+    y = wattn.stem_conv(_dev(img, torch.bfloat16), _dev(W, torch.bfloat16), _dev(b, torch.float32), p=p)
+    mean = wattn.token_mean(y)
+    torch.cuda.synchronize()
+    ref = oracle.stem_conv(img, W, b, p)
+    check(_np(y), ref, "bf16", f"stem p={p}", out_bf16=True)
+    check(_np(mean), _np(y).mean(axis=(1, 2)), "bf16", "token mean", out_bf16=True)
+
+
+@pytest.mark.parametrize("Hg,M,s,H", [(32, 8, 0, 3), (32, 8, 4, 3), (64, 32, 16, 2)])
+def test_swin_block_matches_oracle(Hg, M, s, H):
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    C = 32 * H
+    note(f"block grid {Hg}x{Hg} C={C} M={M} shift={s}")
+    x = _bf((2, Hg, Hg, C), 30 + Hg + s)
+    P = block_params(C, 31 + s, "bf16")
+    th = theta_table(H, 32, 0.1, 32)
+    tp = {k: _dev(v, torch.bfloat16 if k.startswith("w_") else torch.float32) for k, v in P.items()}
+    tp["theta"] = _dev(th, torch.float32)
+    tx = _dev(x, torch.bfloat16)
+    wattn.swin_block(tx, tp, H=H, M=M, shift=s)
+    torch.cuda.synchronize()
+    ref = oracle.swin_block(x, P, H, M, s, th)
+    mx, rel = errors(_np(tx), ref)
+    note(f"  block: max|err| {mx:.3e}, rel-L2 {rel:.3e}")
+    assert np.all(np.isfinite(_np(tx))) and rel <= 1e-2
+
+
+def test_miniature_forward_pass_matches_oracle():
+    import torch
+
+    from vision_transformer_windowed_window_amd.model import FlashSwinT
+
+    cfg = ModelConfig("mini", 2, 64, 2, 8, C=64, depths=(2, 2), heads=(2, 4), n_classes=32, seed=41)
+    P = model_params(cfg, "bf16")
+    img = images(2, 64, 42, "bf16")
+    net = FlashSwinT(P, p=cfg.p, M=cfg.M)
+    logits = net(_dev(img, torch.bfloat16))
+    torch.cuda.synchronize()
+    ref = oracle.flashswin_forward(img, P, cfg.p, cfg.M)
+    mx, rel = errors(_np(logits), ref)
+    note(f"mini FlashSwin-T logits: max|err| {mx:.3e}, rel-L2 {rel:.3e} (max|ref| {np.abs(ref).max():.3e})")
+    assert np.all(np.isfinite(_np(logits))) and rel <= 1e-2

@@ -27,6 +27,14 @@ __all__ = [
     "forward",
     "backward",
     "cla_logits",
+    "linear",
+    "layernorm",
+    "patch_merge_norm",
+    "stem_conv",
+    "token_mean",
+    "swin_block",
+    "swin_block_workspace",
+    "BlockParams",
     "select_blocks",
     "local_residual",
     "gated_local_path",
@@ -58,6 +66,18 @@ STATUS = {
     9: "WATTN_ERR_POINTER",
     10: "WATTN_ERR_VALUE",
 }
+
+ACT_NONE = 0
+ACT_GELU = 1
+
+
+class BlockParams(ctypes.Structure):
+    """wattn_block_params_t: device pointers of one transformer block's parameters."""
+
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_proj", "b_proj", "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2",
+        "b_fc2", "theta")]
+
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -92,6 +112,21 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_forward_lse.restype = ci
     lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
     lib.wattn_backward.restype = ci
+    i64 = ctypes.c_int64
+    lib.wattn_linear.argtypes = [vp] * 5 + [ci] * 6 + [vp]
+    lib.wattn_linear.restype = ci
+    lib.wattn_layernorm.argtypes = [vp] * 4 + [i64, ci, ctypes.c_float, vp]
+    lib.wattn_layernorm.restype = ci
+    lib.wattn_patch_merge_norm.argtypes = [vp] * 4 + [ci] * 4 + [ctypes.c_float, vp]
+    lib.wattn_patch_merge_norm.restype = ci
+    lib.wattn_stem_conv.argtypes = [vp] * 4 + [ci] * 6 + [vp]
+    lib.wattn_stem_conv.restype = ci
+    lib.wattn_token_mean.argtypes = [vp, vp, ci, ci, ci, vp]
+    lib.wattn_token_mean.restype = ci
+    lib.wattn_swin_block_workspace.argtypes = [ci] * 4
+    lib.wattn_swin_block_workspace.restype = i64
+    lib.wattn_swin_block.argtypes = [vp, ctypes.POINTER(BlockParams), vp, i64] + [ci] * 7 + [vp]
+    lib.wattn_swin_block.restype = ci
     lib.wattn_cla_logits.argtypes = [vp] * 6 + [ci] * 5 + [vp]
     lib.wattn_cla_logits.restype = ci
     lib.wattn_forward_gated.argtypes = [vp] * 6 + [ci] * 7 + [vp, vp, vp, ci, ci, vp]
@@ -396,3 +431,100 @@ def cla_logits(x, w_dw, w_pw, b_dw=None, b_pw=None, *, out=None, stream=None):
     if st != 0:
         raise WattnError(st, status_string(st))
     return out
+
+
+def _check(st):
+    if st != 0:
+        raise WattnError(st, status_string(st))
+
+
+def _stream(t, stream):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream if stream is None else stream)
+
+
+def linear(x, W, bias=None, *, residual=None, act: int = ACT_NONE, split=None, out=None, out_dtype=None,
+           stream=None):
+    """y = act(x W^T + bias) (+ residual) over the last axis of x (bfloat16, K channels); W:
+    bfloat16 [N, K]; bias float32 [N] or None.  ``split`` stores column n in part n // split
+    (returns the [N // split, M, split] tensor).  ``out`` may be ``residual`` (in place)."""
+    import torch
+
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = W.shape[0]
+    split = N if split is None else split
+    odt = torch.bfloat16 if out_dtype is None else out_dtype
+    dtype = BF16 if odt == torch.bfloat16 else BF16_OUT_FP32
+    if out is None:
+        shape = (N // split, M, split) if split != N else tuple(x.shape[:-1]) + (N,)
+        out = torch.empty(shape, dtype=odt, device=x.device)
+    _check(load_library().wattn_linear(_ptr(x), _ptr(W), _ptr(bias), _ptr(residual), _ptr(out), M, N, K, split,
+                                       act, dtype, _stream(x, stream)))
+    return out
+
+
+def layernorm(x, gamma, beta, *, eps: float = 1e-5, out=None, stream=None):
+    """Layer norm over the last axis of x (bfloat16); gamma, beta float32."""
+    import torch
+
+    C = x.shape[-1]
+    out = torch.empty_like(x) if out is None else out
+    _check(load_library().wattn_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(out), x.numel() // C, C,
+                                          ctypes.c_float(eps), _stream(x, stream)))
+    return out
+
+
+def patch_merge_norm(x, gamma, beta, *, eps: float = 1e-5, stream=None):
+    """[B, Hg, Wg, C] -> [B, Hg/2, Wg/2, 4C]: 2 x 2 neighbours concatenated and normalised."""
+    import torch
+
+    B, Hg, Wg, C = x.shape
+    out = torch.empty((B, Hg // 2, Wg // 2, 4 * C), dtype=x.dtype, device=x.device)
+    _check(load_library().wattn_patch_merge_norm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(out), B, Hg, Wg, C,
+                                                 ctypes.c_float(eps), _stream(x, stream)))
+    return out
+
+
+def stem_conv(img, W, bias, *, p: int, stream=None):
+    """Overlapping stem on an NHWC bfloat16 image: kernel 2p - 1, stride p, padding p - 1."""
+    import torch
+
+    B, Hi, Wi, Cin = img.shape
+    Cout = W.shape[0]
+    out = torch.empty((B, Hi // p, Wi // p, Cout), dtype=torch.bfloat16, device=img.device)
+    _check(load_library().wattn_stem_conv(_ptr(img), _ptr(W), _ptr(bias), _ptr(out), B, Hi, Wi, Cin, Cout, p,
+                                          _stream(img, stream)))
+    return out
+
+
+def token_mean(x, *, stream=None):
+    """[B, ..., C] bfloat16 -> [B, C]: the mean over the tokens of each image."""
+    import torch
+
+    B, C = x.shape[0], x.shape[-1]
+    n = x.numel() // (B * C)
+    out = torch.empty((B, C), dtype=x.dtype, device=x.device)
+    _check(load_library().wattn_token_mean(_ptr(x), _ptr(out), B, n, C, _stream(x, stream)))
+    return out
+
+
+def swin_block_workspace(B: int, Hg: int, Wg: int, C: int) -> int:
+    return int(load_library().wattn_swin_block_workspace(B, Hg, Wg, C))
+
+
+def swin_block(x, params: dict, *, H: int, M: int, shift: int = 0, workspace=None, stream=None):
+    """One pre-norm block in place on x [B, Hg, Wg, C] (bfloat16, C = 32 H).  ``params`` maps
+    the wattn_block_params_t field names to device tensors (biases and theta may be None)."""
+    import torch
+
+    B, Hg, Wg, C = x.shape
+    need = swin_block_workspace(B, Hg, Wg, C)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    bp = BlockParams(*[None if params.get(name) is None else params[name].data_ptr()
+                       for name, _ in BlockParams._fields_])
+    _check(load_library().wattn_swin_block(_ptr(x), ctypes.byref(bp), _ptr(workspace), workspace.numel(), B, Hg, Wg,
+                                           C, H, M, shift, _stream(x, stream)))
+    return x

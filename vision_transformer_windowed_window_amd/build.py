@@ -49,6 +49,7 @@ def build(verbose: bool = False) -> str:
         kobj = os.path.join(tmp, "wattn_kernels.o")
         gobj = os.path.join(tmp, "wattn_gated.o")
         cobj = os.path.join(tmp, "wattn_cla.o")
+        mobj = os.path.join(tmp, "wattn_model.o")
         aobj = os.path.join(tmp, "wattn_api.o")
         _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
               os.path.join(CSRC, "wattn_kernels.hip"), "-o", kobj], verbose)
@@ -56,11 +57,13 @@ def build(verbose: bool = False) -> str:
               os.path.join(CSRC, "wattn_gated.hip"), "-o", gobj], verbose)
         _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
               os.path.join(CSRC, "wattn_cla.hip"), "-o", cobj], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
+              os.path.join(CSRC, "wattn_model.hip"), "-o", mobj], verbose)
         rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
         _run([hipcc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-c",
               os.path.join(CSRC, "wattn_api.cpp"), "-o", aobj], verbose)
         out_tmp = os.path.join(tmp, "libwattn.so")
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, cobj, aobj, "-o", out_tmp], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, cobj, mobj, aobj, "-o", out_tmp], verbose)
         shutil.move(out_tmp, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
         exe_tmp = os.path.join(tmp, "pipe_rates")

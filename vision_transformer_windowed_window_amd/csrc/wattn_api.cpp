@@ -26,6 +26,13 @@ hipError_t wattn_launch_gated(const LocalPlan& P, bool out_f32, const void* q, c
                               void* out, const float* gate, float tau, hipStream_t stream);
 hipError_t wattn_launch_cla(const ClaPlan& P, const void* x, const float* w_dw, const float* b_dw, const float* w_pw,
                             const float* b_pw, void* z, hipStream_t stream);
+hipError_t wattn_launch_linear(const LinearPlan& P, int act, bool res, bool out_f32, const void* x, const void* W,
+                               const float* bias, const void* r, void* y, hipStream_t stream);
+hipError_t wattn_launch_layernorm(const NormPlan& P, bool gather, const void* x, const float* gamma,
+                                  const float* beta, void* y, hipStream_t stream);
+hipError_t wattn_launch_stem(const StemPlan& P, const void* img, const void* W, const float* bias, void* y,
+                             hipStream_t stream);
+hipError_t wattn_launch_token_mean(const void* x, void* y, int B, int n, int C, hipStream_t stream);
 hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, const void* k, const void* v,
                             void* out, const float* theta, const void* bu, const void* bv, hipStream_t stream);
 
@@ -472,6 +479,211 @@ extern "C" int wattn_cla_logits(const void* x, const float* w_dw, const float* b
   P.grid = (int)std::min<int64_t>(tiles, 2048);
   const hipError_t e = wattn_launch_cla(P, x, w_dw, b_dw, w_pw, b_pw, z, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+// ---- model steps around the attention
+
+namespace {
+
+Range rng_of(const void* p, size_t n) {
+  return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + (p ? n : 0)};
+}
+
+bool any_overlap(Range out, const Range* ins, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ins[i].hi > ins[i].lo && out.hi > out.lo && overlaps(out, ins[i])) return true;
+  return false;
+}
+
+int device_ready() {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return WATTN_ERR_HIP;
+  }
+  return WATTN_OK;
+}
+
+int pointers_ok(const void* const* ptrs, const size_t* sizes, int n) {
+  for (int i = 0; i < n; ++i) {
+    const int st = pointer_ok(ptrs[i], sizes[i]);
+    if (st != WATTN_OK) return st;
+  }
+  return WATTN_OK;
+}
+
+int check_linear(int M, int N, int K, int split, int act, int dtype, bool res) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 30) || N > (1 << 20) || K > (1 << 20)) return WATTN_ERR_SHAPE;
+  if (K % 32 != 0 || N % 4 != 0 || split <= 0 || split % 4 != 0 || N % split != 0) return WATTN_ERR_SHAPE;
+  if (act != WATTN_ACT_NONE && act != WATTN_ACT_GELU) return WATTN_ERR_VALUE;
+  if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
+  if (dtype == WATTN_BF16_OUT_FP32 && (act != WATTN_ACT_NONE || res)) return WATTN_ERR_DTYPE;
+  return WATTN_OK;
+}
+
+LinearPlan linear_plan(int M, int N, int K, int split) {
+  LinearPlan P;
+  P.M = M; P.N = N; P.K = K; P.split = split;
+  P.part_stride = (int64_t)M * split;
+  return P;
+}
+
+}  // namespace
+
+extern "C" int wattn_linear(const void* x, const void* W, const float* bias, const void* residual, void* y, int M,
+                            int N, int K, int split, int act, int dtype, void* stream) {
+  if (x == nullptr || W == nullptr || y == nullptr) return WATTN_ERR_NULL;
+  int st = check_linear(M, N, K, split, act, dtype, residual != nullptr);
+  if (st != WATTN_OK) return st;
+  const size_t xb = (size_t)M * K * 2, wb = (size_t)N * K * 2, bb = (size_t)N * 4, rb = (size_t)M * N * 2;
+  const size_t yb = (size_t)M * N * (dtype == WATTN_BF16 ? 2 : 4);
+  const Range ins[3] = {rng_of(x, xb), rng_of(W, wb), rng_of(bias, bb)};
+  if (any_overlap(rng_of(y, yb), ins, 3)) return WATTN_ERR_ALIAS;
+  if (residual != nullptr && residual != y && overlaps(rng_of(y, yb), rng_of(residual, rb))) return WATTN_ERR_ALIAS;
+  if ((st = device_ready()) != WATTN_OK) return st;
+  const void* ptrs[5] = {x, W, bias, residual, y};
+  const size_t sizes[5] = {xb, wb, bb, rb, yb};
+  if ((st = pointers_ok(ptrs, sizes, 5)) != WATTN_OK) return st;
+  const hipError_t e = wattn_launch_linear(linear_plan(M, N, K, split), act, residual != nullptr,
+                                           dtype == WATTN_BF16_OUT_FP32, x, W, bias, residual, y,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+namespace {
+
+int norm_impl(const void* x, const float* gamma, const float* beta, void* y, int64_t T, int C, int Hg, int Wg,
+              float eps, bool gather, void* stream) {
+  if (x == nullptr || gamma == nullptr || beta == nullptr || y == nullptr) return WATTN_ERR_NULL;
+  if (T <= 0 || C <= 0 || C % 8 != 0 || C > (1 << 16) || T > (1LL << 31)) return WATTN_ERR_SHAPE;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return WATTN_ERR_VALUE;
+  const int Ct = gather ? 4 * C : C;
+  const int64_t in_tokens = gather ? 4 * T : T;
+  const size_t xb = (size_t)in_tokens * C * 2, yb = (size_t)T * Ct * 2, gb = (size_t)Ct * 4;
+  const Range ins[3] = {rng_of(x, xb), rng_of(gamma, gb), rng_of(beta, gb)};
+  if (any_overlap(rng_of(y, yb), ins, 3)) return WATTN_ERR_ALIAS;
+  int st;
+  if ((st = device_ready()) != WATTN_OK) return st;
+  const void* ptrs[4] = {x, gamma, beta, y};
+  const size_t sizes[4] = {xb, gb, gb, yb};
+  if ((st = pointers_ok(ptrs, sizes, 4)) != WATTN_OK) return st;
+  NormPlan P;
+  P.T = T; P.C = C; P.Hg = Hg; P.Wg = Wg; P.eps = eps;
+  const hipError_t e = wattn_launch_layernorm(P, gather, x, gamma, beta, y, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int wattn_layernorm(const void* x, const float* gamma, const float* beta, void* y, int64_t T, int C,
+                               float eps, void* stream) {
+  return norm_impl(x, gamma, beta, y, T, C, 0, 0, eps, false, stream);
+}
+
+extern "C" int wattn_patch_merge_norm(const void* x, const float* gamma, const float* beta, void* y, int B,
+                                      int Hgrid, int Wgrid, int C, float eps, void* stream) {
+  if (B <= 0 || Hgrid <= 0 || Wgrid <= 0 || Hgrid % 2 != 0 || Wgrid % 2 != 0 || Hgrid > 65535 || Wgrid > 65535)
+    return WATTN_ERR_SHAPE;
+  return norm_impl(x, gamma, beta, y, (int64_t)B * (Hgrid / 2) * (Wgrid / 2), C, Hgrid, Wgrid, eps, true, stream);
+}
+
+extern "C" int wattn_stem_conv(const void* img, const void* W, const float* bias, void* y, int B, int Himg, int Wimg,
+                               int Cin, int Cout, int p, void* stream) {
+  if (img == nullptr || W == nullptr || bias == nullptr || y == nullptr) return WATTN_ERR_NULL;
+  if (B <= 0 || Himg <= 0 || Wimg <= 0 || Cin <= 0 || Cout <= 0 || p <= 0 || Cout % 8 != 0) return WATTN_ERR_SHAPE;
+  if (Himg % p != 0 || Wimg % p != 0 || Himg > 65535 || Wimg > 65535) return WATTN_ERR_SHAPE;
+  const int k = 2 * p - 1;
+  if ((int64_t)k * k * Cin * Cout * 4 > 65536) return WATTN_ERR_SHAPE;  // weights staged in 64 KB of LDS
+  const int Ho = Himg / p, Wo = Wimg / p;
+  if ((int64_t)B * Ho * Wo * (Cout / 8) >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  const size_t ib = (size_t)B * Himg * Wimg * Cin * 2, wb = (size_t)Cout * Cin * k * k * 2, bb = (size_t)Cout * 4;
+  const size_t yb = (size_t)B * Ho * Wo * Cout * 2;
+  const Range ins[3] = {rng_of(img, ib), rng_of(W, wb), rng_of(bias, bb)};
+  if (any_overlap(rng_of(y, yb), ins, 3)) return WATTN_ERR_ALIAS;
+  int st;
+  if ((st = device_ready()) != WATTN_OK) return st;
+  const void* ptrs[4] = {img, W, bias, y};
+  const size_t sizes[4] = {ib, wb, bb, yb};
+  if ((st = pointers_ok(ptrs, sizes, 4)) != WATTN_OK) return st;
+  StemPlan P;
+  P.B = B; P.Hi = Himg; P.Wi = Wimg; P.Cin = Cin; P.Cout = Cout; P.p = p; P.Ho = Ho; P.Wo = Wo;
+  const hipError_t e = wattn_launch_stem(P, img, W, bias, y, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+extern "C" int wattn_token_mean(const void* x, void* y, int B, int n, int C, void* stream) {
+  if (x == nullptr || y == nullptr) return WATTN_ERR_NULL;
+  if (B <= 0 || n <= 0 || C <= 0 || (int64_t)B * C >= (1LL << 31) || (int64_t)B * n * C >= kMaxElems)
+    return WATTN_ERR_SHAPE;
+  const size_t xb = (size_t)B * n * C * 2, yb = (size_t)B * C * 2;
+  if (overlaps(rng_of(y, yb), rng_of(x, xb))) return WATTN_ERR_ALIAS;
+  int st;
+  if ((st = device_ready()) != WATTN_OK) return st;
+  const void* ptrs[2] = {x, y};
+  const size_t sizes[2] = {xb, yb};
+  if ((st = pointers_ok(ptrs, sizes, 2)) != WATTN_OK) return st;
+  const hipError_t e = wattn_launch_token_mean(x, y, B, n, C, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
+}
+
+extern "C" int64_t wattn_swin_block_workspace(int B, int Hgrid, int Wgrid, int C) {
+  if (B <= 0 || Hgrid <= 0 || Wgrid <= 0 || C <= 0) return -1;
+  return (int64_t)B * Hgrid * Wgrid * C * 2 * 5;  // normalised x, q/k/v (the attention output reuses the first)
+}
+
+extern "C" int wattn_swin_block(void* x, const wattn_block_params_t* p, void* workspace, int64_t workspace_bytes,
+                                int B, int Hgrid, int Wgrid, int C, int H, int M, int shift, void* stream) {
+  if (x == nullptr || p == nullptr || workspace == nullptr) return WATTN_ERR_NULL;
+  if (p->ln1_g == nullptr || p->ln1_b == nullptr || p->w_qkv == nullptr || p->w_proj == nullptr ||
+      p->ln2_g == nullptr || p->ln2_b == nullptr || p->w_fc1 == nullptr || p->w_fc2 == nullptr)
+    return WATTN_ERR_NULL;
+  int st = check_shape(B, H, Hgrid, Wgrid, M, shift);
+  if (st != WATTN_OK) return st;
+  if (C <= 0 || C % H != 0 || C / H != 32 || C % 32 != 0) return WATTN_ERR_HEAD_DIM;
+  const int64_t T = (int64_t)B * Hgrid * Wgrid;
+  if (T * C * 4 >= kMaxElems || (int64_t)Hgrid * Wgrid * C >= (1LL << 31) || T >= (1LL << 30)) return WATTN_ERR_SHAPE;
+  if (workspace_bytes < wattn_swin_block_workspace(B, Hgrid, Wgrid, C)) return WATTN_ERR_SHAPE;
+  const size_t xb = (size_t)T * C * 2;
+  if (overlaps(rng_of(x, xb), rng_of(workspace, (size_t)workspace_bytes))) return WATTN_ERR_ALIAS;
+  WattnPlan plan;
+  if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan, waves_for_window(M))) return WATTN_ERR_SHAPE;
+  if ((st = device_ready()) != WATTN_OK) return st;
+  const size_t cb = (size_t)C * 4;
+  const void* ptrs[16] = {x, workspace, p->ln1_g, p->ln1_b, p->w_qkv, p->b_qkv, p->w_proj, p->b_proj,
+                          p->ln2_g, p->ln2_b, p->w_fc1, p->b_fc1, p->w_fc2, p->b_fc2, p->theta, nullptr};
+  const size_t sizes[16] = {xb, (size_t)workspace_bytes, cb, cb, (size_t)3 * C * C * 2, 3 * cb,
+                            (size_t)C * C * 2, cb, cb, cb, (size_t)4 * C * C * 2, 4 * cb, (size_t)4 * C * C * 2, cb,
+                            (size_t)H * 16 * 4, 0};
+  if ((st = pointers_ok(ptrs, sizes, 15)) != WATTN_OK) return st;
+
+  // workspace: h = [0, TC) (normalised x, then the attention output, then the second norm),
+  // q/k/v = [TC, 4TC), MLP hidden = [TC, 5TC)
+  uint16_t* ws = static_cast<uint16_t*>(workspace);
+  uint16_t* h = ws;
+  uint16_t* qkv = ws + T * C;
+  uint16_t* hid = ws + T * C;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  NormPlan np;
+  np.T = T; np.C = C; np.Hg = 0; np.Wg = 0; np.eps = 1e-5f;
+  hipError_t e;
+  if ((e = wattn_launch_layernorm(np, false, x, p->ln1_g, p->ln1_b, h, s)) != hipSuccess) return WATTN_ERR_HIP;
+  if ((e = wattn_launch_linear(linear_plan((int)T, 3 * C, C, C), WATTN_ACT_NONE, false, false, h, p->w_qkv, p->b_qkv,
+                               nullptr, qkv, s)) != hipSuccess)
+    return WATTN_ERR_HIP;
+  if ((e = wattn_launch_bf16(plan, 2, p->theta != nullptr, false, qkv, qkv + T * C, qkv + 2 * T * C, h, p->theta,
+                             nullptr, nullptr, nullptr, nullptr, s)) != hipSuccess)
+    return WATTN_ERR_HIP;
+  if ((e = wattn_launch_linear(linear_plan((int)T, C, C, C), WATTN_ACT_NONE, true, false, h, p->w_proj, p->b_proj, x,
+                               x, s)) != hipSuccess)
+    return WATTN_ERR_HIP;
+  if ((e = wattn_launch_layernorm(np, false, x, p->ln2_g, p->ln2_b, h, s)) != hipSuccess) return WATTN_ERR_HIP;
+  if ((e = wattn_launch_linear(linear_plan((int)T, 4 * C, C, 4 * C), WATTN_ACT_GELU, false, false, h, p->w_fc1,
+                               p->b_fc1, nullptr, hid, s)) != hipSuccess)
+    return WATTN_ERR_HIP;
+  if ((e = wattn_launch_linear(linear_plan((int)T, C, 4 * C, C), WATTN_ACT_NONE, true, false, hid, p->w_fc2, p->b_fc2,
+                               x, x, s)) != hipSuccess)
+    return WATTN_ERR_HIP;
+  return WATTN_OK;
 }
 
 extern "C" int64_t wattn_pair_count(int B, int H, int Hgrid, int Wgrid, int M, int shift) {

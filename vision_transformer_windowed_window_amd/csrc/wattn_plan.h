@@ -67,3 +67,23 @@ struct ClaPlan {
   int B, Hg, Wg, C;
   int grid;
 };
+
+// Linear layer y = act(x W^T + b) (+ res): x [M][K], W [N][K]; output column n is stored in
+// part n / split at part * part_stride + m * split + n % split.
+struct LinearPlan {
+  int M, N, K, split;
+  int64_t part_stride;
+};
+
+// Layer norm over C channels of T output tokens (gathered 2 x 2 from a Hg x Wg map for patch
+// merging, in which case the row has 4C channels).
+struct NormPlan {
+  int64_t T;
+  int C, Hg, Wg;
+  float eps;
+};
+
+// Overlapping stem: kernel 2p - 1, stride p, padding p - 1, on an NHWC image.
+struct StemPlan {
+  int B, Hi, Wi, Cin, Cout, p, Ho, Wo;
+};
