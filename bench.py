@@ -18,7 +18,9 @@ out += O_local - O_lin-local, in place); the list form (wattn_select_blocks foll
 wattn_local_residual) is timed beside it.  With --pass stack a step runs six window-attention
 layers over the SR-style grid (8 x 192 x 192 tokens, 6 heads x 32) whose windows cycle 16, 32,
 64 (shifted on every second layer), each with a rank-16 bias and the convolutional gate: per
-layer wattn_cla_logits on the layer input, then wattn_forward_gated.
+layer wattn_cla_logits on the layer input, then wattn_forward_gated.  With --pass model a step
+is the FlashSwin-T forward pass of a batch of 256 px images (overlapping stem, 2-2-6-2 blocks,
+patch merging, head), every step in the library's kernels.
 """
 
 from __future__ import annotations
@@ -37,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "window-attn tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
 METRIC_BWD = "window-attn backward tokens/s + TFLOP/s (% bf16 MFMA peak), M=32 p=2 grid"
 METRIC_STACK = "window-attn stack tokens/s (cyclic windows 16/32/64, rank-16 bias, convolutional gate), SR grid"
+METRIC_MODEL = "FlashSwin-T forward img/s (stem, 12 blocks, merging, head)"
 METRIC_GATED = "gated local path tokens/s (routing + local softmax residual), % of HBM peak, p=2 grid"
 WARMUP_MIN_S = 0.5          # untimed back-to-back launches before timing (clock ramp)
 WARMUP_MAX_STEPS = 20000
@@ -62,9 +65,10 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack"],
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack", "model"],
                     help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path; "
-                         "stack: six layers with cyclic windows and the convolutional gate")
+                         "stack: six layers with cyclic windows and the convolutional gate; "
+                         "model: the FlashSwin-T forward pass (--workload flashswin_t_p4_m32 or _p2_m32)")
     return ap.parse_args()
 
 
@@ -482,6 +486,117 @@ def main_stack(args):
     print(json.dumps(rec), flush=True)
 
 
+def cpu_baseline_model(cfg, budget_s: float):
+    """Time the float64 oracle's forward pass on one image of the workload."""
+    import oracle
+    from inputs import images, model_params
+
+    P = model_params(cfg, "bf16")
+    img = images(1, cfg.img, cfg.seed + 1, "bf16")
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.flashswin_forward(img, P, cfg.p, cfg.M)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": done / el, "unit": "img/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"{done} forward pass(es) of one {cfg.img} px image, {el:.1f} s, numpy float64 with "
+                      "materialised window scores"}
+
+
+def main_model(args):
+    """--pass model: the FlashSwin-T forward pass."""
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+    from inputs import MODEL_CONFIGS, images, model_params
+    from vision_transformer_windowed_window_amd.model import FlashSwinT, stage_window
+
+    name = args.workload if args.workload in MODEL_CONFIGS else "flashswin_t_p4_m32"
+    cfg = MODEL_CONFIGS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    net = FlashSwinT(model_params(cfg, "bf16"), p=cfg.p, M=cfg.M)
+    imgs = [torch.from_numpy(images(cfg.B, cfg.img, cfg.seed + 10 + i, "bf16")).to(torch.bfloat16).to(dev)
+            for i in range(2)]
+
+    def step(i):
+        return net(imgs[i % 2])
+
+    t_w = time.perf_counter()
+    i = 0
+    while i < args.warmup or (time.perf_counter() - t_w < WARMUP_MIN_S and i < WARMUP_MAX_STEPS):
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_s = ev0.elapsed_time(ev1) / args.steps / 1e3
+
+    # the window-attention kernels of the pass, timed alone on inputs of their shapes
+    att_s, att_flops, parts = 0.0, 0.0, []
+    grid, C = cfg.img // cfg.p, cfg.C
+    for s_idx, (depth, heads) in enumerate(zip(cfg.depths, cfg.heads)):
+        g = torch.Generator(device="cpu").manual_seed(s_idx)
+        q, k, v = (torch.randn((cfg.B, grid, grid, heads, 32), generator=g).to(torch.bfloat16).to(dev)
+                   for _ in range(3))
+        th = net.stages[s_idx]["theta"]
+        for i in range(depth):
+            Mw, sh = stage_window(grid, cfg.M, 0 if i % 2 == 0 else cfg.M // 2)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            a.record(stream)
+            for _ in range(reps):
+                wattn.forward(q, k, v, M=Mw, shift=sh, theta=th)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps / 1e3
+            att_s += t
+            att_flops += 4.0 * cfg.B * grid * grid * Mw * Mw * 32 * heads
+            parts.append({"stage": s_idx, "grid": grid, "M": Mw, "shift": sh, "ms": t * 1e3})
+        grid //= 2
+        C *= 2
+    achieved = att_flops / att_s / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "kernel": "wattn_fwd_bf16_kernel over the pass's 12 attention calls (dense flops / their summed time)"}
+    rec = {
+        "metric": METRIC_MODEL,
+        "value": cfg.B / (ms_per_step / 1e3),
+        "unit": "img/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) NHWC images rounded to bf16; seeded random weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "img": cfg.img, "p": cfg.p, "M": cfg.M, "C": cfg.C,
+                   "depths": list(cfg.depths), "heads": list(cfg.heads), "global_batch": cfg.B,
+                   "tokens_stage1": cfg.tokens, "pass": "forward (inference), batch resident in HBM"},
+        "kernel_ms_avg": step_s * 1e3,
+        "attention_ms_in_pass": att_s * 1e3,
+        "attention_share": att_s / step_s,
+        "attention_calls": parts,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_model(cfg, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -494,6 +609,9 @@ def main():
         return
     if args.which == "stack":
         main_stack(args)
+        return
+    if args.which == "model":
+        main_model(args)
         return
 
     import numpy as np

@@ -343,13 +343,14 @@ int wattn_patch_merge_norm(const void* x, const float* gamma, const float* beta,
  * wattn_stem_conv -- the overlapping stem: y[b][i][j][o] = bias[o] + sum_{c, di, dj < 2p-1}
  * W[o][c][di][dj] img[b][p i + di - (p-1)][p j + dj - (p-1)][c], zero outside the image.
  *   img : [B][Himg][Wimg][Cin] bf16 (NHWC); W : [Cout][Cin][2p-1][2p-1] bf16; bias : [Cout]
- *   float32; y : [B][Himg/p][Wimg/p][Cout] bf16.  Himg, Wimg multiples of p; Cout % 8 == 0; the
+ *   float32; y : [B][Himg/p][Wimg/p][Cout] bf16.  Himg, Wimg multiples of p; Cout % 32 == 0; the
  *   weights must fit 64 KB as float32 ((2p-1)^2 Cin Cout <= 16384).  fp32 sums.
  */
 int wattn_stem_conv(const void* img, const void* W, const float* bias, void* y, int B, int Himg, int Wimg, int Cin,
                     int Cout, int p, void* stream);
 
-/* wattn_token_mean -- y[b][c] = mean over the n tokens of x[b][.][c]; x [B][n][C], y [B][C] bf16. */
+/* wattn_token_mean -- y[b][c] = mean over the n tokens of x[b][.][c]; x [B][n][C], y [B][C] bf16;
+ * C % 8 == 0, B <= 65535 (fp32 sums, one rounding). */
 int wattn_token_mean(const void* x, void* y, int B, int n, int C, void* stream);
 
 /* Parameters of one pre-norm transformer block (device pointers; theta may be NULL). */

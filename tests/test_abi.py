@@ -362,6 +362,7 @@ def test_norm_stem_mean_reject_invalid_arguments():
     assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 4, vp(None)) in (8, 9)
     assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 62, 64, 3, 96, 4, vp(None)) == 2
     assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 100, 4, vp(None)) == 2
+    assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 40, 4, vp(None)) == 2
     assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 8, vp(None)) == 2  # LDS
     assert lib.wattn_stem_conv(vp(None), vp(WA), vp(BA), vp(YA), 1, 64, 64, 3, 96, 4, vp(None)) == 1
     assert lib.wattn_stem_conv(vp(XA), vp(WA), vp(BA), vp(XA + 64), 1, 64, 64, 3, 96, 4, vp(None)) == 7

@@ -514,6 +514,7 @@ int pointers_ok(const void* const* ptrs, const size_t* sizes, int n) {
 
 int check_linear(int M, int N, int K, int split, int act, int dtype, bool res) {
   if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 30) || N > (1 << 20) || K > (1 << 20)) return WATTN_ERR_SHAPE;
+  if ((int64_t)((M + 127) / 128) * ((N + 127) / 128) > (1LL << 27)) return WATTN_ERR_SHAPE;  // grid size
   if (K % 32 != 0 || N % 4 != 0 || split <= 0 || split % 4 != 0 || N % split != 0) return WATTN_ERR_SHAPE;
   if (act != WATTN_ACT_NONE && act != WATTN_ACT_GELU) return WATTN_ERR_VALUE;
   if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
@@ -590,12 +591,12 @@ extern "C" int wattn_patch_merge_norm(const void* x, const float* gamma, const f
 extern "C" int wattn_stem_conv(const void* img, const void* W, const float* bias, void* y, int B, int Himg, int Wimg,
                                int Cin, int Cout, int p, void* stream) {
   if (img == nullptr || W == nullptr || bias == nullptr || y == nullptr) return WATTN_ERR_NULL;
-  if (B <= 0 || Himg <= 0 || Wimg <= 0 || Cin <= 0 || Cout <= 0 || p <= 0 || Cout % 8 != 0) return WATTN_ERR_SHAPE;
+  if (B <= 0 || Himg <= 0 || Wimg <= 0 || Cin <= 0 || Cout <= 0 || p <= 0 || Cout % 32 != 0) return WATTN_ERR_SHAPE;
   if (Himg % p != 0 || Wimg % p != 0 || Himg > 65535 || Wimg > 65535) return WATTN_ERR_SHAPE;
   const int k = 2 * p - 1;
   if ((int64_t)k * k * Cin * Cout * 4 > 65536) return WATTN_ERR_SHAPE;  // weights staged in 64 KB of LDS
   const int Ho = Himg / p, Wo = Wimg / p;
-  if ((int64_t)B * Ho * Wo * (Cout / 8) >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  if ((int64_t)B * Ho * Wo * (Cout / 32) >= (1LL << 31)) return WATTN_ERR_SHAPE;
   const size_t ib = (size_t)B * Himg * Wimg * Cin * 2, wb = (size_t)Cout * Cin * k * k * 2, bb = (size_t)Cout * 4;
   const size_t yb = (size_t)B * Ho * Wo * Cout * 2;
   const Range ins[3] = {rng_of(img, ib), rng_of(W, wb), rng_of(bias, bb)};
@@ -613,7 +614,8 @@ extern "C" int wattn_stem_conv(const void* img, const void* W, const float* bias
 
 extern "C" int wattn_token_mean(const void* x, void* y, int B, int n, int C, void* stream) {
   if (x == nullptr || y == nullptr) return WATTN_ERR_NULL;
-  if (B <= 0 || n <= 0 || C <= 0 || (int64_t)B * C >= (1LL << 31) || (int64_t)B * n * C >= kMaxElems)
+  if (B <= 0 || n <= 0 || C <= 0 || C % 8 != 0 || B > 65535 || (int64_t)B * C >= (1LL << 31) ||
+      (int64_t)B * n * C >= kMaxElems)
     return WATTN_ERR_SHAPE;
   const size_t xb = (size_t)B * n * C * 2, yb = (size_t)B * C * 2;
   if (overlaps(rng_of(y, yb), rng_of(x, xb))) return WATTN_ERR_ALIAS;

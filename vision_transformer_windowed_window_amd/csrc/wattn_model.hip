@@ -20,78 +20,106 @@ namespace {
 #include "wattn_device.h"
 
 // ---------------------------------------------------------------------------------------
-// y = act(x W^T + b) (+ res).  One wave per workgroup computes 32 tokens x 64 outputs as
-// y^T = W x^T: 16x16x32 bf16 MFMA with A = 16 rows of W (8 consecutive inputs per lane, read
-// straight from global memory: W is small and stays in the caches) and B = 16 tokens of x.  A
-// lane's accumulator holds four consecutive outputs of one token, stored as 8 bytes.  The
-// operands of the next k step are loaded while the current one multiplies.  Output column n
-// goes to part n / split at offset part * part_stride + m * split + n % split, which writes
-// q, k and v of a qkv projection as three separate [M][C] tensors.
+// y = act(x W^T + b) (+ res).  A workgroup of 4 waves computes a tile of 128 tokens x 128
+// outputs, the waves as 2 x 2 sub-tiles of 64 x 64, as y^T = W x^T on 16x16x32 bf16 MFMA: A =
+// 16 rows of W, B = 16 tokens of x, 8 consecutive inputs per lane.  Per 32-wide k step every
+// thread stages two 16-byte chunks of x and two of W into LDS (double buffered, rows padded to
+// 80 bytes so that the 16 rows a fragment read touches fall on distinct banks); each wave then
+// reads 4 + 4 fragments for 16 MFMAs.  A lane's accumulator holds four consecutive outputs of
+// one token, stored as 8 bytes.  Output column n goes to part n / split at offset
+// part * part_stride + m * split + n % split, which writes q, k and v of a qkv projection as
+// three separate [M][C] tensors.
 // ---------------------------------------------------------------------------------------
 
 enum { ACT_NONE = 0, ACT_GELU = 1 };
 
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+constexpr int LT = 128;   // tile rows (tokens) and columns (outputs)
+constexpr int LRS = 40;   // LDS row stride in bf16 (32 + 8 padding)
+
 template <int ACT, bool RES, bool OUTF32>
-__global__ __launch_bounds__(64) void wattn_linear_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ W,
-                                                          const float* __restrict__ bias,
-                                                          const uint16_t* res, void* y, const LinearPlan P) {
-  const int lane = threadIdx.x, c = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 64;
-  // rows this lane reads: tokens m0 + 16 mb + c, outputs n0 + 16 nb + c
-  const uint16_t* xr[2];
-  const uint16_t* wr[4];
-  bool xv[2], wv[4];
+__global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ W,
+                                                           const float* __restrict__ bias,
+                                                           const uint16_t* res, void* y, const LinearPlan P) {
+  __shared__ __align__(16) uint16_t sX[2][LT * LRS];
+  __shared__ __align__(16) uint16_t sW[2][LT * LRS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  // workgroups are dealt to the 8 XCDs round-robin: workgroup x + 8 r (x < 8) takes m tile
+  // x + 8 (r / ntn) and n tile r % ntn, so the n tiles of one m tile (which share its rows of
+  // x) run one after another in the same XCD's L2
+  const int ntn = (P.N + LT - 1) / LT;
+  const int xr = blockIdx.x >> 3;
+  const int mt = (blockIdx.x & 7) + 8 * (xr / ntn), nt = xr - (xr / ntn) * ntn;
+  if (mt * LT >= P.M) return;
+  const int m0 = mt * LT, n0 = nt * LT;
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;  // this wave's sub-tile
+  // staging: thread t moves chunk t % 4 of rows t / 4 and t / 4 + 64 of both tiles
+  const int srow = tid >> 2, sch = tid & 3;
+  const uint16_t* xs[2];
+  const uint16_t* ws[2];
+  bool xok[2], wok[2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 16 * mb + c;
-    xv[mb] = m < P.M;
-    xr[mb] = x + (int64_t)(xv[mb] ? m : 0) * P.K + 8 * g;
-  }
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + 16 * nb + c;
-    wv[nb] = n < P.N;
-    wr[nb] = W + (int64_t)(wv[nb] ? n : 0) * P.K + 8 * g;
+  for (int h = 0; h < 2; ++h) {
+    const int m = m0 + srow + 64 * h, n = n0 + srow + 64 * h;
+    xok[h] = m < P.M;
+    wok[h] = n < P.N;
+    xs[h] = x + (int64_t)(xok[h] ? m : 0) * P.K + 8 * sch;
+    ws[h] = W + (int64_t)(wok[h] ? n : 0) * P.K + 8 * sch;
   }
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto load = [&](int k0, u32x4 (&xa)[2], u32x4 (&wa)[4]) {
+  u32x4 px[2], pw[2];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) xa[mb] = xv[mb] ? *reinterpret_cast<const u32x4*>(xr[mb] + k0) : zero4;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) wa[nb] = wv[nb] ? *reinterpret_cast<const u32x4*>(wr[nb] + k0) : zero4;
+    for (int h = 0; h < 2; ++h) {
+      px[h] = xok[h] ? *reinterpret_cast<const u32x4*>(xs[h] + k0) : zero4;
+      pw[h] = wok[h] ? *reinterpret_cast<const u32x4*>(ws[h] + k0) : zero4;
+    }
   };
-  f32x4 acc[4][2];
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4*>(&sX[buf][(srow + 64 * h) * LRS + 8 * sch]) = px[h];
+      *reinterpret_cast<u32x4*>(&sW[buf][(srow + 64 * h) * LRS + 8 * sch]) = pw[h];
+    }
+  };
+  f32x4 acc[4][4];  // [n block][m block]
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 xa[2], wa[4], xb[2], wb[4];
-  load(0, xa, wa);
-  for (int k0 = 0; k0 < P.K; k0 += 64) {
-    const bool more = k0 + 32 < P.K;
-    if (more) load(k0 + 32, xb, wb);
+    for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = P.K / 32;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) fetch(32 * (ks + 1));
+    u32x4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = *reinterpret_cast<const u32x4*>(&sW[buf][(wn + 16 * i + c) * LRS + 8 * g]);
+      bfr[i] = *reinterpret_cast<const u32x4*>(&sX[buf][(wm + 16 * i + c) * LRS + 8 * g]);
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma16_bf16(wa[nb], xa[mb], acc[nb][mb]);
-    if (!more) break;
-    if (k0 + 64 < P.K) load(k0 + 64, xa, wa);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = mfma16_bf16(wb[nb], xb[mb], acc[nb][mb]);
+      for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma16_bf16(af[nb], bfr[mb], acc[nb][mb]);
+    if (more) stage(buf ^ 1);
+    __syncthreads();
   }
-  // epilogue: lane (c, g) holds outputs n0 + 16 nb + 4 g + e of token m0 + 16 mb + c
+  // epilogue: lane (c, g) holds outputs n0 + wn + 16 nb + 4 g + e of token m0 + wm + 16 mb + c
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = m0 + 16 * mb + c;
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + wm + 16 * mb + c;
     if (m >= P.M) continue;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + 16 * nb + 4 * g;
+      const int n = n0 + wn + 16 * nb + 4 * g;
       if (n >= P.N) continue;
       const int part = n / P.split, nn = n - part * P.split;
       const int64_t off = (int64_t)part * P.part_stride + (int64_t)m * P.split + nn;
@@ -199,7 +227,8 @@ __global__ __launch_bounds__(256) void wattn_layernorm_kernel(const uint16_t* __
 // ---------------------------------------------------------------------------------------
 // Overlapping stem: out[b][i][j][o] = bias[o] + sum_{c, di, dj} W[o][c][di][dj]
 // img[b][p i + di - (p-1)][p j + dj - (p-1)][c], kernel k = 2p - 1, zero padding.  A thread
-// computes 8 outputs of one token in fp32 from the weights staged in LDS as [tap][o].
+// computes 32 outputs of one token in fp32; the weights sit in LDS as [tap][Cout], so the
+// threads of a wave that share an output slice read the same LDS words (broadcast).
 // ---------------------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void wattn_stem_kernel(const uint16_t* __restrict__ img,
@@ -215,7 +244,7 @@ __global__ __launch_bounds__(256) void wattn_stem_kernel(const uint16_t* __restr
     sW[(rr * P.Cin + c) * P.Cout + o] = __uint_as_float((uint32_t)W[i] << 16);
   }
   __syncthreads();
-  const int groups = P.Cout / 8;
+  const int groups = P.Cout / 32;
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t ntok = (int64_t)P.B * P.Ho * P.Wo;
   if (item >= ntok * groups) return;
@@ -224,9 +253,9 @@ __global__ __launch_bounds__(256) void wattn_stem_kernel(const uint16_t* __restr
   const int64_t b = tok / ((int64_t)P.Ho * P.Wo);
   const int rem = (int)(tok - b * P.Ho * P.Wo);
   const int i = rem / P.Wo, j = rem - i * P.Wo;
-  float acc[8];
+  float acc[32];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = bias[8 * og + e];
+  for (int e = 0; e < 32; ++e) acc[e] = bias[32 * og + e];
   for (int di = 0; di < k; ++di) {
     const int yy = P.p * i + di - (P.p - 1);
     if (yy < 0 || yy >= P.Hi) continue;
@@ -236,39 +265,67 @@ __global__ __launch_bounds__(256) void wattn_stem_kernel(const uint16_t* __restr
       const uint16_t* px = img + ((b * P.Hi + yy) * P.Wi + xx) * P.Cin;
       for (int c = 0; c < P.Cin; ++c) {
         const float v = __uint_as_float((uint32_t)px[c] << 16);
-        const float* w = &sW[((di * k + dj) * P.Cin + c) * P.Cout + 8 * og];
+        const float4* w = reinterpret_cast<const float4*>(&sW[((di * k + dj) * P.Cin + c) * P.Cout + 32 * og]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w[e], v, acc[e]);
+        for (int q = 0; q < 8; ++q) {
+          const float4 wq = w[q];
+          acc[4 * q] = fmaf(wq.x, v, acc[4 * q]);
+          acc[4 * q + 1] = fmaf(wq.y, v, acc[4 * q + 1]);
+          acc[4 * q + 2] = fmaf(wq.z, v, acc[4 * q + 2]);
+          acc[4 * q + 3] = fmaf(wq.w, v, acc[4 * q + 3]);
+        }
       }
     }
   }
-  uint16_t* yo = y + tok * P.Cout + 8 * og;
-  *reinterpret_cast<u32x4*>(yo) =
-      u32x4{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]), pack_bf16(acc[6], acc[7])};
+  uint16_t* yo = y + tok * P.Cout + 32 * og;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<u32x4*>(yo + 8 * q) =
+        u32x4{pack_bf16(acc[8 * q], acc[8 * q + 1]), pack_bf16(acc[8 * q + 2], acc[8 * q + 3]),
+              pack_bf16(acc[8 * q + 4], acc[8 * q + 5]), pack_bf16(acc[8 * q + 6], acc[8 * q + 7])};
 }
 
-// Mean over the tokens of each image: y[b][c] = (1/n) sum_t x[b][t][c]; one thread per (b, c).
+// Mean over the tokens of each image: y[b][c] = (1/n) sum_t x[b][t][c].  A workgroup owns 64
+// channels of one image: thread t sums the 8 channels of chunk t % 8 over tokens t / 8,
+// t / 8 + 32, ...; the 32 partial sums per channel meet in LDS.
 __global__ __launch_bounds__(256) void wattn_token_mean_kernel(const uint16_t* __restrict__ x,
                                                                uint16_t* __restrict__ y, int B, int n, int C) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * C) return;
-  const int b = i / C, ch = i - b * C;
-  const uint16_t* p = x + (int64_t)b * n * C + ch;
-  float s = 0.f;
-  for (int t = 0; t < n; ++t) s += __uint_as_float((uint32_t)p[(int64_t)t * C] << 16);
-  y[i] = (uint16_t)(pack_bf16(s / n, 0.f) & 0xffffu);
+  __shared__ float part[32][65];
+  const int tid = threadIdx.x, ch = tid & 7, row = tid >> 3;
+  const int b = blockIdx.y, c0 = blockIdx.x * 64 + 8 * ch;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < C) {
+    const uint16_t* p = x + (int64_t)b * n * C + c0;
+    for (int t = row; t < n; t += 32) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p + (int64_t)t * C);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s[2 * q] += bf_lo(v[q]);
+        s[2 * q + 1] += bf_hi(v[q]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[row][8 * ch + e] = s[e];
+  __syncthreads();
+  if (tid < 64 && blockIdx.x * 64 + tid < C) {
+    float t = 0.f;
+    for (int r = 0; r < 32; ++r) t += part[r][tid];
+    y[(int64_t)b * C + blockIdx.x * 64 + tid] = (uint16_t)(pack_bf16(t / n, 0.f) & 0xffffu);
+  }
 }
 
 }  // namespace
 
 hipError_t wattn_launch_linear(const LinearPlan& P, int act, bool res, bool out_f32, const void* x, const void* W,
                                const float* bias, const void* r, void* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((P.M + 31) / 32), (unsigned)((P.N + 63) / 64));
+  const int64_t mtiles = (P.M + LT - 1) / LT, ntiles = (P.N + LT - 1) / LT;
+  const dim3 grid((unsigned)(8 * ntiles * ((mtiles + 7) / 8)));
   auto X = static_cast<const uint16_t*>(x);
   auto Wt = static_cast<const uint16_t*>(W);
   auto R = static_cast<const uint16_t*>(r);
 #define WATTN_LIN(A, RS, F) \
-  hipLaunchKernelGGL((wattn_linear_kernel<A, RS, F>), grid, dim3(64), 0, stream, X, Wt, bias, R, y, P)
+  hipLaunchKernelGGL((wattn_linear_kernel<A, RS, F>), grid, dim3(256), 0, stream, X, Wt, bias, R, y, P)
   if (out_f32) {
     if (act != ACT_NONE || res) return hipErrorInvalidValue;
     WATTN_LIN(ACT_NONE, false, true);
@@ -300,7 +357,7 @@ hipError_t wattn_launch_stem(const StemPlan& P, const void* img, const void* W, 
                              hipStream_t stream) {
   const int k = 2 * P.p - 1;
   const size_t lds = (size_t)k * k * P.Cin * P.Cout * sizeof(float);
-  const int64_t items = (int64_t)P.B * P.Ho * P.Wo * (P.Cout / 8);
+  const int64_t items = (int64_t)P.B * P.Ho * P.Wo * (P.Cout / 32);
   hipLaunchKernelGGL(wattn_stem_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), lds, stream,
                      static_cast<const uint16_t*>(img), static_cast<const uint16_t*>(W), bias,
                      static_cast<uint16_t*>(y), P);
@@ -308,7 +365,7 @@ hipError_t wattn_launch_stem(const StemPlan& P, const void* img, const void* W, 
 }
 
 hipError_t wattn_launch_token_mean(const void* x, void* y, int B, int n, int C, hipStream_t stream) {
-  hipLaunchKernelGGL(wattn_token_mean_kernel, dim3((unsigned)((B * C + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(wattn_token_mean_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)B), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), B, n, C);
   return hipGetLastError();
 }
