@@ -49,7 +49,7 @@ CSRC = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "csrc")
 # the sources each profiled kernel is compiled from (their hash tags the traffic records)
 KERNEL_SRCS = {
     "attention": [os.path.join(CSRC, f) for f in ("wattn_kernels.hip", "wattn_device.h", "wattn_plan.h")],
-    "gated": [os.path.join(CSRC, f) for f in ("wattn_gated.hip", "wattn_device.h", "wattn_plan.h")],
+    "gated": [os.path.join(CSRC, f) for f in ("wattn_gated.hip", "wattn_device.h", "wattn_aux_plan.h")],
 }
 PIPE_RATES = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "pipe_rates")
 MFMA_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 / _f16

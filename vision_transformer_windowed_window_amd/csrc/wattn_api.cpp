@@ -10,6 +10,7 @@
 #include <cmath>
 
 #include "wattn.h"
+#include "wattn_aux_plan.h"
 #include "wattn_plan.h"
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,

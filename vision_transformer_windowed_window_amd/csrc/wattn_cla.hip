@@ -23,7 +23,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "wattn_plan.h"
+#include "wattn_aux_plan.h"
 
 namespace {
 
