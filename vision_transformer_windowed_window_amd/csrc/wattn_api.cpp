@@ -476,8 +476,9 @@ extern "C" int wattn_cla_logits(const void* x, const float* w_dw, const float* b
   }
   ClaPlan P;
   P.B = B; P.Hg = Hgrid; P.Wg = Wgrid; P.C = C;
-  const int64_t tiles = (elems / C + 63) / 64;
-  P.grid = (int)std::min<int64_t>(tiles, 2048);
+  const int64_t strips = ((int64_t)Wgrid + 15) / 16, bands = ((int64_t)Hgrid + 15) / 16;
+  if (strips * bands * B >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  P.grid = (int)(strips * bands * B);  // one workgroup per 16-column, 16-row strip of an image
   const hipError_t e = wattn_launch_cla(P, x, w_dw, b_dw, w_pw, b_pw, z, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }

@@ -16,7 +16,7 @@ struct LocalPlan {
 };
 
 // Launch description of the gate-logit convolutions: the token grid, the channel count and the
-// number of workgroups (each loops over tiles of 64 tokens).
+// number of workgroups (one per strip of 16 columns and 16 rows of an image).
 struct ClaPlan {
   int B, Hg, Wg, C;
   int grid;

@@ -9,10 +9,11 @@
 //   x : [B][Hg][Wg][C] bf16 (channels last), w_dw [C][3][3], b_dw [C], w_pw [C][C] (out x in),
 //   b_pw [C] fp32; z : [B][Hg][Wg][C] bf16.  Zero padding, stride 1, no activation between.
 //
-// A workgroup has C/32 waves and loops over tiles of 64 consecutive tokens (flattened
-// b, y, x order).  Per tile:
+// A workgroup has C/32 waves and owns a strip of 16 columns and 16 output rows of one image.
+// It slides down the strip with three input rows (with their halo columns) in LDS, loading
+// each input row once and two rows ahead while the current row is computed.  Per output row:
 //   depth-wise : each thread computes 8 channels of a token from the nine neighbouring tokens'
-//                16-byte chunks (fp32 FMAs, weights from LDS) and stores them to LDS as fp16;
+//                16-byte chunks in LDS (fp32 FMAs) and stores them to LDS as fp16;
 //   point-wise : z^T = W Y^T on 16x16x32 fp16 MFMA.  Wave w owns output channels
 //                32 w .. 32 w + 31 and keeps their rows of W (fp16) in registers for the
 //                whole kernel; the B operand (channels 8 g .. 8 g + 7 of token c) comes from the
@@ -29,7 +30,8 @@ namespace {
 
 #include "wattn_device.h"
 
-constexpr int CLA_TILE = 64;  // tokens per tile
+constexpr int SW = 16;  // strip width (tokens per output row of a workgroup)
+constexpr int SH = 16;  // output rows per workgroup
 
 template <int C>
 __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t* __restrict__ x,
@@ -38,18 +40,29 @@ __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t*
                                                                  const float* __restrict__ w_pw,
                                                                  const float* __restrict__ b_pw,
                                                                  uint16_t* __restrict__ z, const ClaPlan P) {
-  constexpr int NT = 2 * C;            // threads: C / 32 waves
-  constexpr int CH = C / 8;            // 16-byte chunks per token
-  constexpr int KS = C / 32;           // k steps of the point-wise product
-  constexpr int YS = C + 8;            // LDS row stride (fp16) of the tile, padded against bank conflicts
-  __shared__ __align__(16) float sW[9 * C];   // depth-wise weights, [tap][channel]
-  __shared__ __align__(16) float sB[C];       // depth-wise bias
-  __shared__ __align__(16) uint16_t sY[CLA_TILE * YS];
+  constexpr int NT = 2 * C;              // threads: C / 32 waves
+  constexpr int CH = C / 8;              // 16-byte chunks per token
+  constexpr int KS = C / 32;             // k steps of the point-wise product
+  constexpr int YS = C + 8;              // LDS row stride (fp16) of the depth-wise tile
+  constexpr int RW = SW + 2;             // input row width with the halo columns
+  constexpr int RCH = RW * CH;           // 16-byte chunks of one input row
+  constexpr int PF = (RCH + NT - 1) / NT;  // chunks per thread when a row is loaded
+  // depth-wise weights as [tap][half][chunk][4] (channel 8 chunk + 4 half + e) and the bias as
+  // [half][chunk][4]: the lanes of a wave read consecutive 16-byte words, free of bank conflicts
+  __shared__ __align__(16) float sW[9 * C];
+  __shared__ __align__(16) float sB[C];
+  __shared__ __align__(16) uint16_t sX[3][RW * C];   // three input rows (bf16), rolling
+  __shared__ __align__(16) uint16_t sY[SW * YS];     // depth-wise output of one row (fp16)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  for (int i = tid; i < 9 * C; i += NT) sW[(i % 9) * C + i / 9] = w_dw[i];  // [C][3][3] -> [tap][C]
-  for (int i = tid; i < C; i += NT) sB[i] = b_dw != nullptr ? b_dw[i] : 0.f;
+  // channel cidx = 8 chunk + 4 half + e sits at half * C/2 + 4 chunk + e of its tap's C floats
+  auto wofs = [](int cidx) { return ((cidx >> 2) & 1) * (C / 2) + (cidx >> 3) * 4 + (cidx & 3); };
+  for (int i = tid; i < 9 * C; i += NT) {  // w_dw is [C][3][3]
+    const int cidx = i / 9, tap = i - cidx * 9;
+    sW[tap * C + wofs(cidx)] = w_dw[i];
+  }
+  for (int i = tid; i < C; i += NT) sB[wofs(i)] = b_dw != nullptr ? b_dw[i] : 0.f;
 
   // this wave's rows of W: output channels 32 wave + 16 ob + c, input channels 32 ks + 8 g .. + 7
   u32x4 Wf[2][KS];
@@ -66,65 +79,79 @@ __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t*
 #pragma unroll
     for (int e = 0; e < 4; ++e) bias[ob][e] = b_pw != nullptr ? b_pw[32 * wave + 16 * ob + 4 * g + e] : 0.f;
   }
-  __syncthreads();
 
-  const int64_t ntok = (int64_t)P.B * P.Hg * P.Wg;
-  const int64_t ntiles = (ntok + CLA_TILE - 1) / CLA_TILE;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t t0 = tile * CLA_TILE;
-    // ---- depth-wise: CLA_TILE * CH items of 8 channels.  The nine taps' loads are issued
-    //      together from clamped (in-bounds) addresses; taps outside the grid get weight 0.
-#pragma unroll 2
-    for (int it = tid; it < CLA_TILE * CH; it += NT) {
-      const int tl = it / CH, ch = it - tl * CH;
-      const uint32_t t = (uint32_t)min(t0 + tl, ntok - 1);  // fewer than 2^31 tokens
-      const uint32_t img = t / (uint32_t)(P.Hg * P.Wg);
-      const uint32_t rem = t - img * (uint32_t)(P.Hg * P.Wg);
-      const int yy = (int)(rem / (uint32_t)P.Wg), xx = (int)rem - yy * P.Wg;
-      u32x4 xr[9];
-      bool ok[9];
+  // this workgroup: image b, columns x0 .. x0 + SW - 1, output rows y0 .. y0 + SH - 1
+  const int strips = (P.Wg + SW - 1) / SW, bands = (P.Hg + SH - 1) / SH;
+  const int b = blockIdx.x / (strips * bands), rr = blockIdx.x - b * strips * bands;
+  const int y0 = (rr / strips) * SH, x0 = (rr % strips) * SW;
+  const int y1 = min(y0 + SH, P.Hg);
+  const int64_t img = (int64_t)b * P.Hg * P.Wg;
+
+  // input row yy (zero outside the image) as this thread's chunks of the RW x C row
+  auto fetch_row = [&](int yy, u32x4 (&pre)[PF]) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      const int it = tid + f * NT;
+      const int tx = it / CH, ch = it - tx * CH;
+      const int xx = x0 - 1 + tx;
+      const bool ok = it < RCH && yy >= 0 && yy < P.Hg && xx >= 0 && xx < P.Wg;
+      pre[f] = ok ? *reinterpret_cast<const u32x4*>(x + (img + (int64_t)yy * P.Wg + xx) * C + 8 * ch)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_row = [&](int slot, const u32x4 (&pre)[PF]) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      const int it = tid + f * NT;
+      if (it < RCH) *reinterpret_cast<u32x4*>(&sX[slot][it * 8]) = pre[f];
+    }
+  };
+  auto slot_of = [](int yy) { return (yy + 3) % 3; };  // yy >= -1
+
+  // one output row: rows y - 1 and y are in LDS; `pre` holds row y + 1 and is refilled with
+  // row y + 3, so two rows are in flight while a row is computed
+  auto do_row = [&](int y, u32x4 (&pre)[PF]) {
+    store_row(slot_of(y + 1), pre);
+    if (y + 3 <= y1) fetch_row(y + 3, pre);
+    __syncthreads();
+    // ---- depth-wise: SW tokens x CH chunks of 8 channels
+    for (int it = tid; it < SW * CH; it += NT) {
+      const int tx = it / CH, ch = it - tx * CH;
+      const float4 b0 = *reinterpret_cast<const float4*>(&sB[4 * ch]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&sB[C / 2 + 4 * ch]);
+      float acc[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
       for (int tap = 0; tap < 9; ++tap) {
-        const int py = yy + tap / 3 - 1, px = xx + tap % 3 - 1;
-        ok[tap] = py >= 0 && py < P.Hg && px >= 0 && px < P.Wg;
-        const int cy = ok[tap] ? py : yy, cx = ok[tap] ? px : xx;
-        xr[tap] = *reinterpret_cast<const u32x4*>(x + ((int64_t)(img * P.Hg + cy) * P.Wg + cx) * C + 8 * ch);
+        const int dy = tap / 3, dx = tap % 3;
+        const u32x4 xr = *reinterpret_cast<const u32x4*>(&sX[slot_of(y - 1 + dy)][(tx + dx) * C + 8 * ch]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sW[tap * C + 4 * ch]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sW[tap * C + C / 2 + 4 * ch]);
+        acc[0] = fmaf(w0.x, bf_lo(xr[0]), acc[0]);
+        acc[1] = fmaf(w0.y, bf_hi(xr[0]), acc[1]);
+        acc[2] = fmaf(w0.z, bf_lo(xr[1]), acc[2]);
+        acc[3] = fmaf(w0.w, bf_hi(xr[1]), acc[3]);
+        acc[4] = fmaf(w1.x, bf_lo(xr[2]), acc[4]);
+        acc[5] = fmaf(w1.y, bf_hi(xr[2]), acc[5]);
+        acc[6] = fmaf(w1.z, bf_lo(xr[3]), acc[6]);
+        acc[7] = fmaf(w1.w, bf_hi(xr[3]), acc[7]);
       }
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = sB[8 * ch + e];
-#pragma unroll
-      for (int tap = 0; tap < 9; ++tap) {
-        const float* wt = &sW[tap * C + 8 * ch];
-        const float4 w0 = *reinterpret_cast<const float4*>(wt);
-        const float4 w1 = *reinterpret_cast<const float4*>(wt + 4);
-        const float m = ok[tap] ? 1.0f : 0.0f;
-        acc[0] = fmaf(w0.x * m, bf_lo(xr[tap][0]), acc[0]);
-        acc[1] = fmaf(w0.y * m, bf_hi(xr[tap][0]), acc[1]);
-        acc[2] = fmaf(w0.z * m, bf_lo(xr[tap][1]), acc[2]);
-        acc[3] = fmaf(w0.w * m, bf_hi(xr[tap][1]), acc[3]);
-        acc[4] = fmaf(w1.x * m, bf_lo(xr[tap][2]), acc[4]);
-        acc[5] = fmaf(w1.y * m, bf_hi(xr[tap][2]), acc[5]);
-        acc[6] = fmaf(w1.z * m, bf_lo(xr[tap][3]), acc[6]);
-        acc[7] = fmaf(w1.w * m, bf_hi(xr[tap][3]), acc[7]);
-      }
-      *reinterpret_cast<u32x4*>(&sY[tl * YS + 8 * ch]) =
+      *reinterpret_cast<u32x4*>(&sY[tx * YS + 8 * ch]) =
           u32x4{pack_f16(acc[0], acc[1]), pack_f16(acc[2], acc[3]), pack_f16(acc[4], acc[5]), pack_f16(acc[6], acc[7])};
     }
     __syncthreads();
-    // ---- point-wise: per 16-token block, z^T[o][token] for this wave's 32 output channels
+    // ---- point-wise: z^T[o][token] for this wave's 32 output channels, 16-token blocks
 #pragma unroll
-    for (int tb = 0; tb < CLA_TILE / 16; ++tb) {
-      const int tl = 16 * tb + c;
+    for (int tb = 0; tb < SW / 16; ++tb) {
+      const int tx = 16 * tb + c;
       f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 Yf = *reinterpret_cast<const u32x4*>(&sY[tl * YS + 32 * ks + 8 * g]);
+        const u32x4 Yf = *reinterpret_cast<const u32x4*>(&sY[tx * YS + 32 * ks + 8 * g]);
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob) acc[ob] = mfma16_f16(Wf[ob][ks], Yf, acc[ob]);
       }
-      const int64_t t = t0 + tl;
-      if (t < ntok) {
+      if (x0 + tx < P.Wg) {
+        const int64_t t = img + (int64_t)y * P.Wg + x0 + tx;
 #pragma unroll
         for (int ob = 0; ob < 2; ++ob) {
           const int o = 32 * wave + 16 * ob + 4 * g;
@@ -134,7 +161,18 @@ __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t*
         }
       }
     }
-    __syncthreads();  // the next tile overwrites sY
+  };
+
+  u32x4 preA[PF], preB[PF];
+  fetch_row(y0 - 1, preA);
+  store_row(slot_of(y0 - 1), preA);
+  fetch_row(y0, preA);
+  store_row(slot_of(y0), preA);
+  fetch_row(y0 + 1, preA);
+  fetch_row(y0 + 2, preB);
+  for (int y = y0; y < y1; y += 2) {
+    do_row(y, preA);
+    if (y + 1 < y1) do_row(y + 1, preB);
   }
 }
 
