@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define WATTN_ABI_VERSION 3
+#define WATTN_ABI_VERSION 4
 
 /* Element types.  The bf16 modes run QK^T and PV on bf16 matrix cores with fp32 RoPE,
  * fp32 softmax and fp32 accumulation; they differ only in the type of `out`.  A bf16
@@ -135,6 +135,13 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
                       int dtype, void* stream);
 
 /*
+ * wattn_backward_scratch_bytes -- bytes of the scratch buffer wattn_backward and
+ * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 32 T) with T = B Hgrid Wgrid H
+ * query rows.  -1 for a size <= 0 or d != 32.
+ */
+int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
+
+/*
  * wattn_backward -- gradients of loss = sum(dout * out) of the shifted-window attention
  * (the FLASHSWIN page's memory claims cover the scores "and their gradient": the backward
  * pass recomputes P per tile from q, k and lse and never stores an N x N matrix).
@@ -147,7 +154,11 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
  *   lse     : float32 [B][Hgrid][Wgrid][H] from wattn_forward_lse on the same inputs.
  *   theta   : float32 [H][d/2] as in the forward pass, or NULL (no RoPE).
  * Outputs (device pointers, caller-owned, overwritten):
- *   delta   : float32 [B][Hgrid][Wgrid][H], scratch: rowsum(dout * out) per query.
+ *   scratch : wattn_backward_scratch_bytes(B, H, Hgrid, Wgrid, d) bytes of device memory,
+ *             16-byte aligned (WATTN_ERR_POINTER otherwise), contents undefined on entry and
+ *             on return.  The query-tile kernel writes rowsum(dout * out) per query, the
+ *             rotated and scaled queries (fp16) and the output gradient (bf16) there once;
+ *             the key-tile kernel streams them back instead of redoing that work per tile.
  *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
  *   dtheta  : float32 [H][d/2] (zeroed, then accumulated with atomic adds, so its last bits
  *             depend on the order of the additions); required iff theta is not NULL.
@@ -167,7 +178,7 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
  * to fp16 for dq and dk; everything accumulates in fp32.
  */
 int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                   const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta,
+                   const float* lse, float* scratch, float* dq, float* dk, float* dv, float* dtheta,
                    int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
                    const float* theta, const void* bias_u, const void* bias_v, int r,
                    float* dbias_u, float* dbias_v, int dtype, void* stream);
@@ -204,7 +215,7 @@ int wattn_forward_gated(const void* q, const void* k, const void* v, void* out, 
  * All other arguments, checks and numerics are those of wattn_backward.
  */
 int wattn_backward_gated(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                         const float* lse, const void* gate_z, float* delta, float* dq, float* dk, float* dv,
+                         const float* lse, const void* gate_z, float* scratch, float* dq, float* dk, float* dv,
                          float* dtheta, float* dgate_z, int B, int H, int Hgrid, int Wgrid, int M, int shift,
                          int d, const float* theta, const void* bias_u, const void* bias_v, int r,
                          float* dbias_u, float* dbias_v, int dtype, void* stream);

@@ -34,7 +34,8 @@ def _call(q=P1, k=P2, v=P3, out=P4, B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32, thet
 def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
-    assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_select_blocks",
+    assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_backward_scratch_bytes",
+                     "wattn_select_blocks",
                      "wattn_local_residual", "wattn_gated_local", "wattn_forward_gated", "wattn_backward_gated",
                      "wattn_cla_logits", "wattn_linear", "wattn_layernorm", "wattn_patch_merge_norm",
                      "wattn_stem_conv", "wattn_token_mean", "wattn_swin_block_workspace", "wattn_swin_block",
@@ -149,10 +150,20 @@ def _call_bwd(**kw):
         (dict(r=16, bu=BU, bv=BV, dbu=G1, dbv=0xF00000), 7), (dict(r=16, bu=BU, bv=BV, dbu=0xE00000, dbv=BV), 7),
         (dict(dq=P1), 7), (dict(dk=G1 + 64), 7), (dict(dv=LS), 7), (dict(delta=G3 + 4), 7),
         (dict(theta=TH, dtheta=TH), 7), (dict(theta=TH, dtheta=G1), 7),
+        (dict(dq=DL + 0x10000), 7), (dict(delta=DL + 8), 9),
     ],
 )
 def test_backward_rejects_invalid_arguments(kw, status):
     assert _call_bwd(**kw) == status
+
+
+def test_backward_scratch_bytes():
+    # 512 query rows: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32 bf16 gradients
+    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32
+    # 3 rows: the statistics are padded to 4 floats so the rows after them start 16-byte aligned
+    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32
+    assert _lib().wattn_backward_scratch_bytes(0, 2, 16, 16, 32) == -1
+    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 64) == -1
 
 
 # ---- the gated local path: host-side rejections

@@ -113,6 +113,8 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
     lib.wattn_backward.restype = ci
     i64 = ctypes.c_int64
+    lib.wattn_backward_scratch_bytes.argtypes = [ci] * 5
+    lib.wattn_backward_scratch_bytes.restype = i64
     lib.wattn_linear.argtypes = [vp] * 5 + [ci] * 6 + [vp]
     lib.wattn_linear.restype = ci
     lib.wattn_layernorm.argtypes = [vp] * 4 + [i64, ci, ctypes.c_float, vp]
@@ -281,7 +283,7 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bia
     dtype = BF16 if out.dtype == torch.bfloat16 else BF16_OUT_FP32
     f32 = dict(dtype=torch.float32, device=q.device)
     dq, dk, dv = (torch.empty(q.shape, **f32) for _ in range(3))
-    delta = torch.empty((B, Hg, Wg, H), **f32)
+    scratch = torch.empty(lib.wattn_backward_scratch_bytes(B, H, Hg, Wg, d), dtype=torch.uint8, device=q.device)
     dtheta = None if theta is None else torch.empty((H, d // 2), **f32)
     dbu = None if bias_u is None else torch.empty(bias_u.shape, **f32)
     dbv = None if bias_v is None else torch.empty(bias_v.shape, **f32)
@@ -292,7 +294,7 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bia
             raise ValueError("gate_z must be a contiguous device tensor shaped and typed like q")
         dz = torch.empty(q.shape, **f32)
         st = lib.wattn_backward_gated(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(gate_z), _ptr(delta), _ptr(dq),
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(gate_z), _ptr(scratch), _ptr(dq),
             _ptr(dk), _ptr(dv), _ptr(dtheta), _ptr(dz), B, H, Hg, Wg, M, shift, d, _ptr(theta), _ptr(bias_u),
             _ptr(bias_v), r, _ptr(dbu), _ptr(dbv), dtype, ctypes.c_void_p(stream),
         )
@@ -300,7 +302,7 @@ def backward(q, k, v, out, dout, lse, *, M: int, shift: int = 0, theta=None, bia
             raise WattnError(st, status_string(st))
         return dq, dk, dv, dtheta, dbu, dbv, dz
     st = lib.wattn_backward(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(scratch), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(dtheta), B, H, Hg, Wg, M, shift, d, _ptr(theta), _ptr(bias_u), _ptr(bias_v), r, _ptr(dbu), _ptr(dbv),
         dtype, ctypes.c_void_p(stream),
     )

@@ -17,7 +17,7 @@ hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out
                              const void* k, const void* v, void* out, const float* theta, const void* bu,
                              const void* bv, float* lse, const void* gz, hipStream_t stream);
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
-                            const void* v, const void* out, const void* dout, const float* lse, float* delta,
+                            const void* v, const void* out, const void* dout, const float* lse, float* scratch,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
                             const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream);
 hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, int* count, hipStream_t stream);
@@ -263,14 +263,18 @@ extern "C" int wattn_forward_gated(const void* q, const void* k, const void* v, 
 
 namespace {
 
+// Backward scratch for `rows` query rows (T * H): the rowsum statistic as float32 [rows], padded
+// to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32] each.
+int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 32 * rows) * 4; }
+
 // Backward pass shared by wattn_backward and wattn_backward_gated (gz and dz both NULL or both set).
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                  const void* gz, float* delta, float* dq, float* dk, float* dv, float* dtheta, float* dz, int B,
+                  const void* gz, float* scratch, float* dq, float* dk, float* dv, float* dtheta, float* dz, int B,
                   int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
                   const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype, void* stream) {
   // ---- argument checks (no HIP call before this block ends)
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
-      delta == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+      scratch == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
     return WATTN_ERR_NULL;
   if ((theta == nullptr) != (dtheta == nullptr)) return WATTN_ERR_NULL;
   if ((gz == nullptr) != (dz == nullptr)) return WATTN_ERR_NULL;
@@ -289,7 +293,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   const size_t tbytes = (size_t)elems * 2;                                    // q, k, v
   const size_t gbytes = (size_t)elems * (dtype == WATTN_BF16 ? 2 : 4);        // out, dout
   const size_t fbytes = (size_t)elems * 4;                                    // dq, dk, dv
-  const size_t rbytes = (size_t)(elems / d) * 4;                              // lse, delta
+  const size_t rbytes = (size_t)(elems / d) * 4;                              // lse
+  const size_t sbytes = (size_t)backward_scratch_bytes(elems / d);            // scratch
   const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
   const size_t b_bytes = (size_t)H * M * M * r * 2;   // bias factors (bf16)
   const size_t db_bytes = (size_t)H * M * M * r * 4;  // their gradients (float32)
@@ -299,7 +304,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   const Range ins[10] = {rng(q, tbytes), rng(k, tbytes), rng(v, tbytes), rng(out, gbytes), rng(dout, gbytes),
                          rng(lse, rbytes), rng(theta, th_bytes), rng(bias_u, b_bytes), rng(bias_v, b_bytes),
                          rng(gz, tbytes)};
-  const Range outs[8] = {rng(delta, rbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
+  const Range outs[8] = {rng(scratch, sbytes), rng(dq, fbytes), rng(dk, fbytes), rng(dv, fbytes),
                          rng(dtheta, th_bytes), rng(dbias_u, db_bytes), rng(dbias_v, db_bytes), rng(dz, fbytes)};
   for (int i = 0; i < 8; ++i) {
     if (outs[i].hi == outs[i].lo) continue;
@@ -308,6 +313,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     for (int j = 0; j < i; ++j)
       if (outs[j].hi > outs[j].lo && overlaps(outs[i], outs[j])) return WATTN_ERR_ALIAS;
   }
+  if (reinterpret_cast<uintptr_t>(scratch) % 16 != 0) return WATTN_ERR_POINTER;
   WattnPlan plan;
   if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan, std::min(waves_for_window(M), 4))) return WATTN_ERR_SHAPE;
 
@@ -317,39 +323,44 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     (void)hipGetLastError();
     return WATTN_ERR_HIP;
   }
-  const void* ptrs[18] = {q,     k,  v,      out,    dout,   lse,     delta,   dq, dk,
+  const void* ptrs[18] = {q,     k,  v,      out,    dout,   lse,     scratch, dq, dk,
                           dv,    theta, dtheta, bias_u, bias_v, dbias_u, dbias_v, gz, dz};
-  const size_t sizes[18] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, rbytes, fbytes, fbytes,
+  const size_t sizes[18] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, sbytes, fbytes, fbytes,
                             fbytes, th_bytes, th_bytes, b_bytes, b_bytes, db_bytes, db_bytes, tbytes, fbytes};
   for (int i = 0; i < 18; ++i) {
     st = pointer_ok(ptrs[i], sizes[i]);
     if (st != WATTN_OK) return st;
   }
   const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
-                                        lse, delta, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v, gz,
+                                        lse, scratch, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v, gz,
                                         dz, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }
 
 }  // namespace
 
+extern "C" int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d) {
+  if (B <= 0 || H <= 0 || Hgrid <= 0 || Wgrid <= 0 || d != 32) return -1;
+  return backward_scratch_bytes((int64_t)B * Hgrid * Wgrid * H);
+}
+
 extern "C" int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                              const float* lse, float* delta, float* dq, float* dk, float* dv, float* dtheta, int B,
+                              const float* lse, float* scratch, float* dq, float* dk, float* dv, float* dtheta, int B,
                               int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta,
                               const void* bias_u, const void* bias_v, int r, float* dbias_u, float* dbias_v,
                               int dtype, void* stream) {
-  return backward_impl(q, k, v, out, dout, lse, nullptr, delta, dq, dk, dv, dtheta, nullptr, B, H, Hgrid, Wgrid, M,
+  return backward_impl(q, k, v, out, dout, lse, nullptr, scratch, dq, dk, dv, dtheta, nullptr, B, H, Hgrid, Wgrid, M,
                        shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream);
 }
 
 extern "C" int wattn_backward_gated(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                                    const float* lse, const void* gate_z, float* delta, float* dq, float* dk,
+                                    const float* lse, const void* gate_z, float* scratch, float* dq, float* dk,
                                     float* dv, float* dtheta, float* dgate_z, int B, int H, int Hgrid, int Wgrid,
                                     int M, int shift, int d, const float* theta, const void* bias_u,
                                     const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype,
                                     void* stream) {
   if (gate_z == nullptr || dgate_z == nullptr) return WATTN_ERR_NULL;
-  return backward_impl(q, k, v, out, dout, lse, gate_z, delta, dq, dk, dv, dtheta, dgate_z, B, H, Hgrid, Wgrid, M,
+  return backward_impl(q, k, v, out, dout, lse, gate_z, scratch, dq, dk, dv, dtheta, dgate_z, B, H, Hgrid, Wgrid, M,
                        shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream);
 }
 

@@ -821,7 +821,8 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu,
-    const uint16_t* __restrict__ gz, float* __restrict__ dz, const WattnPlan P) {
+    const uint16_t* __restrict__ gz, float* __restrict__ dz, uint16_t* __restrict__ qt,
+    uint16_t* __restrict__ dot, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sK[2][KT * D];
@@ -966,6 +967,11 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
       }
       Qf[a][p] = pack_f16(x0 * qscale, x1 * qscale);
     }
+    // the key-tile kernel streams these operand-ready forms instead of re-deriving them
+    if (qvalid[a]) {
+      *reinterpret_cast<u32x4*>(qt + qoff[a] + 8 * g) = Qf[a];
+      *reinterpret_cast<u32x4*>(dot + qoff[a] + 8 * g) = dOf[a];
+    }
   }
   store(0);
   walker_advance(W, X);
@@ -1094,13 +1100,12 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
-template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
+template <int NW, bool ROPE, bool BIAS>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const void* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
-    const uint16_t* __restrict__ gz, const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sQ[2][QTT * D];
@@ -1163,24 +1168,12 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   walker_init(Wb, X, bk, 0, rowstride, colstride);
   u32x4 pq, po, pu = {0u, 0u, 0u, 0u};
   float pl = 0.f, pd = 0.f;
-  int lpos = 0;
   auto fetch = [&](int tile) {
     const bool valid = tile * QTT + lk < n;
     const int off = valid ? W.off : W.last;
-    pq = *reinterpret_cast<const u32x4*>(q + X.img + off);
-    float go[8];
-    load8<OUTF32>(dout, X.img + off, go);
-    if (GATE) {  // the attention's output gradient: dout * sigmoid(z)
-      const u32x4 zr = *reinterpret_cast<const u32x4*>(gz + X.img + off);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        go[2 * p] *= sigmoidf_fast(bf_lo(zr[p]));
-        go[2 * p + 1] *= sigmoidf_fast(bf_hi(zr[p]));
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) po[p] = pack_bf16(go[2 * p], go[2 * p + 1]);
-    lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
+    // rotated, scaled fp16 q and bf16 dO (times the gate) from the query-tile kernel
+    pq = *reinterpret_cast<const u32x4*>(qt + X.img + off);
+    po = *reinterpret_cast<const u32x4*>(dot + X.img + off);
     if (tid < QTT) {
       const bool sv = tile * QTT + tid < n;
       const int so = (sv ? Ws.off : Ws.last) / D;
@@ -1194,21 +1187,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     }
   };
   auto store = [&](int buf) {
-    u32x4 qr;
-    const int lp = min(lpos, M - 1);
-    const float qscale = LOG2E * 0.17677669529663687f;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float x0 = bf_lo(pq[p]), x1 = bf_hi(pq[p]);
-      if (ROPE) {
-        const float2 t = sTab[(4 * lch + p) * TSTR + lp];
-        const float r0 = x0 * t.x - x1 * t.y, r1 = x0 * t.y + x1 * t.x;
-        x0 = r0;
-        x1 = r1;
-      }
-      qr[p] = pack_f16(x0 * qscale, x1 * qscale);
-    }
-    *reinterpret_cast<u32x4*>(&sQ[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = qr;
+    *reinterpret_cast<u32x4*>(&sQ[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = pq;
     *reinterpret_cast<u32x4*>(&sO[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = po;
     if (tid < QTT) {
       sL[buf][tid] = pl;
@@ -1459,7 +1438,8 @@ template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
 static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, const void* out,
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
-                                  float* dbv, const void* gz, float* dz, hipStream_t stream) {
+                                  float* dbv, const void* gz, float* dz, uint16_t* qt, uint16_t* dot,
+                                  hipStream_t stream) {
   if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
@@ -1469,13 +1449,13 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   auto BV = static_cast<const uint16_t*>(bv);
   auto GZ = static_cast<const uint16_t*>(gz);
   hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
-                     table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz,
-                     plan);
+                     table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz, qt,
+                     dot, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
-                     table_bytes, stream, Q, K, V, dout, lse, static_cast<const float*>(delta), dk, dv, dtheta, theta,
-                     BU, BV, dbv, GZ, plan);
+  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
+                     static_cast<const uint16_t*>(qt), K, V, static_cast<const uint16_t*>(dot), lse,
+                     static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv, plan);
   return hipGetLastError();
 }
 
@@ -1484,8 +1464,9 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
                                 float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
                                 const void* bu, const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
-                                hipStream_t stream) {
-#define WATTN_BWD_ARGS plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, stream
+                                uint16_t* qt, uint16_t* dot, hipStream_t stream) {
+#define WATTN_BWD_ARGS \
+  plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, stream
   const int sel = (bias ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
     case 0: return launch_bwd_inst<NW, false, false, false, GATE>(WATTN_BWD_ARGS);
@@ -1501,7 +1482,7 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
 }
 
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
-                            const void* v, const void* out, const void* dout, const float* lse, float* delta,
+                            const void* v, const void* out, const void* dout, const float* lse, float* scratch,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
                             const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream) {
   const bool bias = bu != nullptr;
@@ -1516,8 +1497,13 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
     const int64_t cnt = (int64_t)plan.H * plan.M * plan.M * 16;
     if ((e = fill(dbu, cnt)) != hipSuccess || (e = fill(dbv, cnt)) != hipSuccess) return e;
   }
+  // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32]
+  const int64_t th = (int64_t)plan.B * plan.Hg * plan.Wg * plan.H;
+  float* delta = scratch;
+  uint16_t* qt = reinterpret_cast<uint16_t*>(scratch + ((th + 3) & ~int64_t(3)));
+  uint16_t* dot = qt + th * D;
 #define WATTN_BWD_ARGS plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
-                       dbu, dbv, gz, dz, stream
+                       dbu, dbv, gz, dz, qt, dot, stream
   const bool gate = gz != nullptr;
   switch (plan.nw) {
     case 2: return gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS);
