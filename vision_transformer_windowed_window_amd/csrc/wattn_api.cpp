@@ -487,9 +487,10 @@ extern "C" int wattn_cla_logits(const void* x, const float* w_dw, const float* b
   }
   ClaPlan P;
   P.B = B; P.Hg = Hgrid; P.Wg = Wgrid; P.C = C;
-  const int64_t strips = ((int64_t)Wgrid + 15) / 16, bands = ((int64_t)Hgrid + 15) / 16;
-  if (strips * bands * B >= (1LL << 31)) return WATTN_ERR_SHAPE;
-  P.grid = (int)(strips * bands * B);  // one workgroup per 16-column, 16-row strip of an image
+  const int64_t rows = ((int64_t)Wgrid + 15) / 16 * Hgrid * B;  // at most the token count
+  if (rows >= (1LL << 31)) return WATTN_ERR_SHAPE;
+  P.rows = (int)rows;  // split into equal runs at launch
+  P.per = P.grid = 0;
   const hipError_t e = wattn_launch_cla(P, x, w_dw, b_dw, w_pw, b_pw, z, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }

@@ -19,7 +19,9 @@ struct LocalPlan {
 // number of workgroups (one per strip of 16 columns and 16 rows of an image).
 struct ClaPlan {
   int B, Hg, Wg, C;
-  int grid;
+  int rows;  // output rows of all 16-column strips: B * ceil(Wg / 16) * Hg
+  int per;   // rows per workgroup (set at launch)
+  int grid;  // workgroups (set at launch)
 };
 
 // Linear layer y = act(x W^T + b) (+ res): x [M][K], W [N][K]; output column n is stored in
