@@ -790,8 +790,7 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float x[8])
 // window position and add the pairs' angle-gradient terms pos * (g . J x) to sDth
 template <bool ROPE, int TSTR>
 __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j0, int pos, const float2* sTab,
-                                             const uint16_t* __restrict__ xsrc, int64_t xoff, float* sDth,
-                                             float out[4]) {
+                                             const u32x2 raw, float* sDth, float out[4]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float a = acc[2 * t] * scale, b = acc[2 * t + 1] * scale;
@@ -805,7 +804,6 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
     }
   }
   if (ROPE) {
-    const u32x2 raw = *reinterpret_cast<const u32x2*>(xsrc + xoff);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float x0 = bf_lo(raw[t]), x1 = bf_hi(raw[t]);
@@ -848,6 +846,10 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
   int qpos_r[2], qpos_c[2];
   int64_t qoff[2];
   bool qvalid[2];
+  // all loads of both query blocks first, with no branch around them (a padded query's offset
+  // is the region's first token, so every address is valid), so that they are in flight together
+  float go[2][8], o[2][8], lraw[2];
+  u32x4 zraw[2], braw[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int iq = X.t.q0 + wave * 32 + 16 * a + c;
@@ -857,27 +859,34 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     qpos_r[a] = X.t.r0 + li;
     qpos_c[a] = X.t.c0 + lj;
     qoff[a] = X.img + X.regbase + li * rowstride + lj * colstride;
-    float go[8], o[8];
+    qraw[a] = *reinterpret_cast<const u32x4*>(q + qoff[a] + 8 * g);
+    load8<OUTF32>(dout, qoff[a] + 8 * g, go[a]);
+    load8<OUTF32>(out, qoff[a] + 8 * g, o[a]);
+    lraw[a] = lse[qoff[a] / D];
+    if (GATE) zraw[a] = *reinterpret_cast<const u32x4*>(gz + qoff[a] + 8 * g);
+    // lanes g = 2, 3 reload the first half of the 16 bias channels and ignore it
+    if (BIAS)
+      braw[a] = *reinterpret_cast<const u32x4*>(
+          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 8 * (g & 1));
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
     float Dp = 0.f, L2 = 0.f;
     if (qvalid[a]) {
-      qraw[a] = *reinterpret_cast<const u32x4*>(q + qoff[a] + 8 * g);
-      load8<OUTF32>(dout, qoff[a] + 8 * g, go);
-      load8<OUTF32>(out, qoff[a] + 8 * g, o);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Dp += go[e] * o[e];
-      L2 = lse[qoff[a] / D] * LOG2E;
+      for (int e = 0; e < 8; ++e) Dp += go[a][e] * o[a][e];
+      L2 = lraw[a] * LOG2E;
       if (GATE) {
         // out is sigmoid(z) * attention: the attention's output gradient is dout * sigmoid(z),
         // dz = dout * out * (1 - sigmoid(z)), and D = rowsum(dout * out) is unchanged
-        const u32x4 zr = *reinterpret_cast<const u32x4*>(gz + qoff[a] + 8 * g);
         float gzv[8];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float s0 = sigmoidf_fast(bf_lo(zr[p])), s1 = sigmoidf_fast(bf_hi(zr[p]));
-          gzv[2 * p] = go[2 * p] * o[2 * p] * (1.0f - s0);
-          gzv[2 * p + 1] = go[2 * p + 1] * o[2 * p + 1] * (1.0f - s1);
-          go[2 * p] *= s0;
-          go[2 * p + 1] *= s1;
+          const float s0 = sigmoidf_fast(bf_lo(zraw[a][p])), s1 = sigmoidf_fast(bf_hi(zraw[a][p]));
+          gzv[2 * p] = go[a][2 * p] * o[a][2 * p] * (1.0f - s0);
+          gzv[2 * p + 1] = go[a][2 * p + 1] * o[a][2 * p + 1] * (1.0f - s1);
+          go[a][2 * p] *= s0;
+          go[a][2 * p + 1] *= s1;
         }
         float* dst = dz + qoff[a] + 8 * g;
         *reinterpret_cast<float4*>(dst) = make_float4(gzv[0], gzv[1], gzv[2], gzv[3]);
@@ -886,21 +895,19 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     } else {
       qraw[a] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) go[e] = 0.f;
+      for (int e = 0; e < 8; ++e) go[a][e] = 0.f;
     }
     const float Dn = xsum32(xsum16(Dp));  // the four lanes of query c hold 8 dims each
     if (qvalid[a] && g == 0) delta[qoff[a] / D] = Dn;
     Qb[a] = u32x4{0u, 0u, 0u, 0u};
     if (BIAS && qvalid[a] && g < 2) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(
-          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 8 * g);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(raw[p]) * LOG2E, bf_hi(raw[p]) * LOG2E);
+      for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(braw[a][p]) * LOG2E, bf_hi(braw[a][p]) * LOG2E);
     }
     CnL[a] = f32x4{-L2, -L2, -L2, -L2};
     CnD[a] = f32x4{-Dn, -Dn, -Dn, -Dn};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[2 * p], go[2 * p + 1]);
+    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
   }
 
   // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V; threads 0 .. 2 KT - 1
@@ -1081,6 +1088,15 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
       for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dU[a][e]);
     }
   }
+  // the raw q channels of the dtheta sums, all loads issued before the first use
+  u32x2 qr2[2][2] = {};
+  if (ROPE) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+        if (qvalid[a]) qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (!qvalid[a]) continue;
@@ -1088,8 +1104,7 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     for (int cb = 0; cb < 2; ++cb) {
       float r4[4];
       const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];  // channels 0..15 rotate with the row
-      finish_grad4<ROPE, TSTR>(dQ[cb][a], 0.17677669529663687f, 8 * cb + 2 * g, pos, sTab, q,
-                               qoff[a] + 16 * cb + 4 * g, sDth, r4);
+      finish_grad4<ROPE, TSTR>(dQ[cb][a], 0.17677669529663687f, 8 * cb + 2 * g, pos, sTab, qr2[a][cb], sDth, r4);
       *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
@@ -1166,22 +1181,24 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   walker_init(W, X, lk, 8 * lch, rowstride, colstride);
   walker_init(Ws, X, tid < QTT ? tid : 0, 0, rowstride, colstride);
   walker_init(Wb, X, bk, 0, rowstride, colstride);
+  // Every thread issues every load of the next tile, from an in-bounds address (threads past
+  // the statistics or bias rows reload a valid row), and the arithmetic on the loaded values
+  // waits until the tile is stored to LDS: with no branch around a load and no use right after
+  // it, the loads of tile t + 1 stay in flight during the compute of tile t.
   u32x4 pq, po, pu = {0u, 0u, 0u, 0u};
   float pl = 0.f, pd = 0.f;
+  bool psv = false;
   auto fetch = [&](int tile) {
     const bool valid = tile * QTT + lk < n;
     const int off = valid ? W.off : W.last;
     // rotated, scaled fp16 q and bf16 dO (times the gate) from the query-tile kernel
     pq = *reinterpret_cast<const u32x4*>(qt + X.img + off);
     po = *reinterpret_cast<const u32x4*>(dot + X.img + off);
-    if (tid < QTT) {
-      const bool sv = tile * QTT + tid < n;
-      const int so = (sv ? Ws.off : Ws.last) / D;
-      // a padded query gets the statistic +inf: its scores become -inf, so P = dS = 0
-      pl = sv ? -lse[X.img / D + so] * LOG2E : -INFINITY;
-      pd = -delta[X.img / D + so];
-    }
-    if (bthread) {
+    psv = tile * QTT + (tid < QTT ? tid : 0) < n;
+    const int so = (psv ? Ws.off : Ws.last) / D;
+    pl = lse[X.img / D + so];
+    pd = delta[X.img / D + so];
+    if (BIAS) {
       const int qn = (tile * QTT + bk < n) ? (X.t.r0 + Wb.ci) * M + (X.t.c0 + Wb.cj) : 0;
       pu = *reinterpret_cast<const u32x4*>(bu + ((int64_t)X.t.h * M * M + qn) * 16 + 8 * bch);
     }
@@ -1190,8 +1207,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     *reinterpret_cast<u32x4*>(&sQ[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = pq;
     *reinterpret_cast<u32x4*>(&sO[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = po;
     if (tid < QTT) {
-      sL[buf][tid] = pl;
-      sDl[buf][tid] = pd;
+      // a padded query gets the statistic +inf: its scores become -inf, so P = dS = 0
+      sL[buf][tid] = psv ? -pl * LOG2E : -INFINITY;
+      sDl[buf][tid] = -pd;
     }
     if (bthread) {
       u32x4 ur;
@@ -1335,7 +1353,16 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     }
   }
 
-  // ---- epilogue: dv, dk = R^T (dS^T Q~) ln 2, and the k part of dtheta
+  // ---- epilogue: dv, dk = R^T (dS^T Q~) ln 2, and the k part of dtheta (the raw k channels
+  //      of the dtheta sums loaded first, all before the first use)
+  u32x2 kr2[2][2] = {};
+  if (ROPE) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        if (kvalid[a]) kr2[a][x] = *reinterpret_cast<const u32x2*>(k + koffs[a] + 16 * x + 4 * g);
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (!kvalid[a]) continue;
@@ -1345,7 +1372,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
           make_float4(dV[x][a][0], dV[x][a][1], dV[x][a][2], dV[x][a][3]);
       float r4[4];
       const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
-      finish_grad4<ROPE, TSTR>(dK[x][a], LN2, 8 * x + 2 * g, pos, sTab, k, koffs[a] + 16 * x + 4 * g, sDth, r4);
+      finish_grad4<ROPE, TSTR>(dK[x][a], LN2, 8 * x + 2 * g, pos, sTab, kr2[a][x], sDth, r4);
       *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
