@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
                                                            const uint16_t* res, void* y, const LinearPlan P) {
   __shared__ __align__(16) uint16_t sX[2][LT * LRS];
   __shared__ __align__(16) uint16_t sW[2][LT * LRS];
+  __shared__ float sBias[LT];  // bias of the tile's outputs (0 past N or without a bias)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   // workgroups are dealt to the 8 XCDs round-robin: workgroup x + 8 r (x < 8) takes m tile
@@ -93,6 +94,7 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
 
   const int nk = P.K / 32;
   fetch(0);
+  if (tid < LT) sBias[tid] = (bias != nullptr && n0 + tid < P.N) ? bias[n0 + tid] : 0.f;
   stage(0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
@@ -112,30 +114,39 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
     if (more) stage(buf ^ 1);
     __syncthreads();
   }
-  // epilogue: lane (c, g) holds outputs n0 + wn + 16 nb + 4 g + e of token m0 + wm + 16 mb + c
+  // epilogue: lane (c, g) holds outputs n0 + wn + 16 nb + 4 g + e of token m0 + wm + 16 mb + c.
+  // The bias comes from LDS; the four residual words of a token block are loaded together, from
+  // clamped in-bounds addresses (N is a multiple of 4), so that one wait covers them.
+  auto out_off = [&](int m, int n) {
+    const int part = n / P.split, nn = n - part * P.split;
+    return (int64_t)part * P.part_stride + (int64_t)m * P.split + nn;
+  };
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int m = m0 + wm + 16 * mb + c;
     if (m >= P.M) continue;
+    u32x2 rv[4];
+    if (RES) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        rv[nb] = *reinterpret_cast<const u32x2*>(res + out_off(m, min(n0 + wn + 16 * nb + 4 * g, P.N - 4)));
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int n = n0 + wn + 16 * nb + 4 * g;
       if (n >= P.N) continue;
-      const int part = n / P.split, nn = n - part * P.split;
-      const int64_t off = (int64_t)part * P.part_stride + (int64_t)m * P.split + nn;
-      float r[4];
+      const int64_t off = out_off(m, n);
+      const float4 bv = *reinterpret_cast<const float4*>(&sBias[wn + 16 * nb + 4 * g]);
+      float r[4] = {acc[nb][mb][0] + bv.x, acc[nb][mb][1] + bv.y, acc[nb][mb][2] + bv.z, acc[nb][mb][3] + bv.w};
+      if (ACT == ACT_GELU) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float t = acc[nb][mb][e] + (bias != nullptr ? bias[n + e] : 0.f);
-        if (ACT == ACT_GELU) t = gelu_erf(t);
-        r[e] = t;
+        for (int e = 0; e < 4; ++e) r[e] = gelu_erf(r[e]);
       }
       if (RES) {
-        const u32x2 rv = *reinterpret_cast<const u32x2*>(res + off);
-        r[0] += bf_lo(rv[0]);
-        r[1] += bf_hi(rv[0]);
-        r[2] += bf_lo(rv[1]);
-        r[3] += bf_hi(rv[1]);
+        r[0] += bf_lo(rv[nb][0]);
+        r[1] += bf_hi(rv[nb][0]);
+        r[2] += bf_lo(rv[nb][1]);
+        r[3] += bf_hi(rv[nb][1]);
       }
       if (OUTF32) {
         *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(r[0], r[1], r[2], r[3]);
