@@ -22,11 +22,14 @@ namespace {
 // ---------------------------------------------------------------------------------------
 // y = act(x W^T + b) (+ res).  A workgroup of 4 waves computes a tile of 128 tokens x 128
 // outputs, the waves as 2 x 2 sub-tiles of 64 x 64, as y^T = W x^T on 16x16x32 bf16 MFMA: A =
-// 16 rows of W, B = 16 tokens of x, 8 consecutive inputs per lane.  Per 32-wide k step every
-// thread stages two 16-byte chunks of x and two of W into LDS (double buffered, rows padded to
-// 80 bytes so that the 16 rows a fragment read touches fall on distinct banks); each wave then
-// reads 4 + 4 fragments for 16 MFMAs.  A lane's accumulator holds four consecutive outputs of
-// one token, stored as 8 bytes.  Output column n goes to part n / split at offset
+// 16 rows of W, B = 16 tokens of x, 8 consecutive inputs per lane.  The 32-wide k slices of x
+// and W go from global memory straight into LDS (16 bytes per lane, no registers), three slices
+// in flight: the slice two steps ahead is requested while the current one is multiplied.  A
+// slice row is 64 bytes; chunk j of row r sits in LDS slot j ^ ((r >> 2) & 3), so that the 16
+// rows a fragment read touches fall on distinct banks (the loads fetch the swizzled chunk, as
+// the LDS position of a lane's data is fixed by its lane index).  Each wave reads 4 + 4
+// fragments per slice for 16 MFMAs.  A lane's accumulator holds four consecutive outputs of one
+// token, stored as 8 bytes.  Output column n goes to part n / split at offset
 // part * part_stride + m * split + n % split, which writes q, k and v of a qkv projection as
 // three separate [M][C] tensors.
 // ---------------------------------------------------------------------------------------
@@ -35,18 +38,20 @@ enum { ACT_NONE = 0, ACT_GELU = 1 };
 
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-constexpr int LT = 128;   // tile rows (tokens) and columns (outputs)
-constexpr int LRS = 40;   // LDS row stride in bf16 (32 + 8 padding)
+constexpr int LT = 128;     // tile rows (tokens) and columns (outputs)
+constexpr int LSTAGE = 3;   // k slices in flight
+constexpr int LSL = LT * 32;  // bf16 elements of one operand's slice
+
+__device__ __forceinline__ int lswz(int row) { return (row >> 2) & 3; }
 
 template <int ACT, bool RES, bool OUTF32>
 __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ W,
                                                            const float* __restrict__ bias,
                                                            const uint16_t* res, void* y, const LinearPlan P) {
-  __shared__ __align__(16) uint16_t sX[2][LT * LRS];
-  __shared__ __align__(16) uint16_t sW[2][LT * LRS];
+  __shared__ __align__(16) uint16_t sS[LSTAGE][2][LSL];  // [stage][x, W][row * 32 + swizzled chunk * 8]
   __shared__ float sBias[LT];  // bias of the tile's outputs (0 past N or without a bias)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   // workgroups are dealt to the 8 XCDs round-robin: workgroup x + 8 r (x < 8) takes m tile
   // x + 8 (r / ntn) and n tile r % ntn, so the n tiles of one m tile (which share its rows of
@@ -57,33 +62,26 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
   if (mt * LT >= P.M) return;
   const int m0 = mt * LT, n0 = nt * LT;
   const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;  // this wave's sub-tile
-  // staging: thread t moves chunk t % 4 of rows t / 4 and t / 4 + 64 of both tiles
-  const int srow = tid >> 2, sch = tid & 3;
+  // loads: instruction h of wave w fills LDS chunks 256 h + 64 w + lane of a slice, i.e. row
+  // 64 h + 16 w + lane / 4, slot lane % 4, from the chunk that the swizzle puts there; rows
+  // past M (N) reload the last row, whose products are never stored
   const uint16_t* xs[2];
   const uint16_t* ws[2];
-  bool xok[2], wok[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int m = m0 + srow + 64 * h, n = n0 + srow + 64 * h;
-    xok[h] = m < P.M;
-    wok[h] = n < P.N;
-    xs[h] = x + (int64_t)(xok[h] ? m : 0) * P.K + 8 * sch;
-    ws[h] = W + (int64_t)(wok[h] ? n : 0) * P.K + 8 * sch;
+    const int row = 64 * h + 16 * wave + (lane >> 2), chunk = (lane & 3) ^ lswz(row);
+    xs[h] = x + (int64_t)min(m0 + row, P.M - 1) * P.K + 8 * chunk;
+    ws[h] = W + (int64_t)min(n0 + row, P.N - 1) * P.K + 8 * chunk;
   }
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 px[2], pw[2];
-  auto fetch = [&](int k0) {
+  auto issue = [&](int ks, int stage) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      px[h] = xok[h] ? *reinterpret_cast<const u32x4*>(xs[h] + k0) : zero4;
-      pw[h] = wok[h] ? *reinterpret_cast<const u32x4*>(ws[h] + k0) : zero4;
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<u32x4*>(&sX[buf][(srow + 64 * h) * LRS + 8 * sch]) = px[h];
-      *reinterpret_cast<u32x4*>(&sW[buf][(srow + 64 * h) * LRS + 8 * sch]) = pw[h];
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(xs[h] + 32 * ks),
+                                       (__attribute__((address_space(3))) void*)(&sS[stage][0][(256 * h + 64 * wave) * 8]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ws[h] + 32 * ks),
+                                       (__attribute__((address_space(3))) void*)(&sS[stage][1][(256 * h + 64 * wave) * 8]),
+                                       16, 0, 0);
     }
   };
   f32x4 acc[4][4];  // [n block][m block]
@@ -93,26 +91,51 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = P.K / 32;
-  fetch(0);
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  // (waits for the slices issued above too, as they are older: step 0 needs slice 0 anyway)
   if (tid < LT) sBias[tid] = (bias != nullptr && n0 + tid < P.N) ? bias[n0 + tid] : 0.f;
-  stage(0);
-  __syncthreads();
+  // The compiler orders LDS reads after direct-to-LDS loads by waiting for every load in
+  // flight, which would drain the pipeline each step; the barrier and the fragment reads are
+  // therefore written out, with the waits they need and no more.
   for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) fetch(32 * (ks + 1));
+    const int stage = ks % LSTAGE;
+    // this wave's loads of slice ks are done when at most slice ks + 1's four loads are still in
+    // flight; the barrier then covers every wave's loads (and, on the first step, sBias)
+    if (ks + 1 < nk)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // slice ks + 2 goes into the stage slice ks - 1 used, which every wave finished reading
+    // (its reads end with a wait) before the barrier above
+    if (ks + 2 < nk) issue(ks + 2, (ks + 2) % LSTAGE);
+    // fragments: rows wn + 16 i + c of W and wm + 16 i + c of x, chunk g (swizzled); the
+    // reads complete inside the statement, so their registers are written when it ends
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)&sS[stage][0][0];
+    const uint32_t ax = base + (uint32_t)((wm + c) * 64 + 16 * (g ^ lswz(wm + c)));
+    const uint32_t aw = base + (uint32_t)(LSL * 2 + (wn + c) * 64 + 16 * (g ^ lswz(wn + c)));
     u32x4 af[4], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = *reinterpret_cast<const u32x4*>(&sW[buf][(wn + 16 * i + c) * LRS + 8 * g]);
-      bfr[i] = *reinterpret_cast<const u32x4*>(&sX[buf][(wm + 16 * i + c) * LRS + 8 * g]);
-    }
+    // rows 16 i + c with i = 1..3 share (16 i + c) >> 2 & 3 = (c >> 2) & 3 ^ 0: 16 i adds
+    // 4 i to row >> 2, a multiple of 4, so the swizzle is that of row c and each fragment is
+    // 1024 bytes further on
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:1024\n\t"
+        "ds_read_b128 %6, %9 offset:2048\n\t"
+        "ds_read_b128 %7, %9 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(bfr[0]), "=&v"(bfr[1]), "=&v"(bfr[2]),
+          "=&v"(bfr[3])  // early clobber: a read may land before the next one takes its address
+        : "v"(aw), "v"(ax)
+        : "memory");
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = mfma16_bf16(af[nb], bfr[mb], acc[nb][mb]);
-    if (more) stage(buf ^ 1);
-    __syncthreads();
   }
   // epilogue: lane (c, g) holds outputs n0 + wn + 16 nb + 4 g + e of token m0 + wm + 16 mb + c.
   // The bias comes from LDS; the four residual words of a token block are loaded together, from
