@@ -36,7 +36,25 @@ namespace {
 
 enum { ACT_NONE = 0, ACT_GELU = 1 };
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// GELU(x) = 0.5 x (1 + erf(x / sqrt 2)).  With z = |x| / sqrt 2, 1 + erf(x / sqrt 2) is
+// erfc(z) for x < 0 and 2 - erfc(z) for x >= 0, and erfc(z) = t exp(-z^2 + P(t)) with
+// t = 1 / (1 + z / 2) and P of degree 7 fitted by csrc/fit_erfc.py (relative error of erfc
+// below 6.4e-7 in exact arithmetic; the float32 evaluation here adds rounding up to about 2e-5
+// of erfc where -z^2 is large).  Hardware reciprocal and exp2.
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, z, 1.0f));
+  float p = -1.836619680e-01f;
+  p = fmaf(p, t, 7.339941066e-01f);
+  p = fmaf(p, t, -9.701263864e-01f);
+  p = fmaf(p, t, 3.209165196e-01f);
+  p = fmaf(p, t, -2.418480100e-02f);
+  p = fmaf(p, t, 3.892575659e-01f);
+  p = fmaf(p, t, 9.993278403e-01f);
+  p = fmaf(p, t, -1.265523516e+00f);
+  const float q = t * __builtin_amdgcn_exp2f(fmaf(-z, z, p) * 1.4426950408889634f);
+  return 0.5f * x * (x >= 0.f ? 2.0f - q : q);
+}
 
 constexpr int LT = 128;     // tile rows (tokens) and columns (outputs)
 constexpr int LSTAGE = 3;   // k slices in flight
