@@ -103,3 +103,48 @@ def test_backward_matches_oracle(case):
         assert got["dtheta"] is None
     if not r:
         assert got["dbias_u"] is None and got["dbias_v"] is None
+
+
+def test_backward_scratch_contract():
+    """wattn_backward called through the C ABI with a caller-owned scratch of exactly
+    wattn_backward_scratch_bytes, pre-filled with NaN bytes: dq, dk and dv equal the binding's
+    (every element of them is written by one thread, with no atomics), so the scratch's
+    contents on entry do not matter.  A scratch that is not 16-byte aligned is refused
+    (WATTN_ERR_POINTER) before any launch."""
+    import ctypes
+
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    B, Hg, Wg, H, M, s = 1, 48, 32, 2, 16, 5
+    q, k, v, th, dout, _, _ = _setup(B, Hg, Wg, H, M, 977)
+    dev = torch.device("cuda:0")
+    t = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+    tq, tk, tv, tth, tdo = t(q), t(k), t(v), t(th, torch.float32), t(dout, torch.float32)
+    out, lse = wattn.forward(tq, tk, tv, M=M, shift=s, theta=tth, out_dtype=torch.float32, return_lse=True)
+    ref = wattn.backward(tq, tk, tv, out, tdo, lse, M=M, shift=s, theta=tth)
+    lib = wattn.load_library()
+    nbytes = lib.wattn_backward_scratch_bytes(B, H, Hg, Wg, 32)
+    rows = B * Hg * Wg * H
+    assert nbytes == 4 * ((rows + 3) // 4 * 4 + 32 * rows)
+    scratch = torch.full((nbytes + 64,), 0xFF, dtype=torch.uint8, device=dev)  # NaN bytes
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    dth = torch.empty((H, 16), dtype=torch.float32, device=dev)
+    vp = ctypes.c_void_p
+    stream = vp(torch.cuda.current_stream(dev).cuda_stream)
+
+    def call(scr):
+        return lib.wattn_backward(vp(tq.data_ptr()), vp(tk.data_ptr()), vp(tv.data_ptr()), vp(out.data_ptr()),
+                                  vp(tdo.data_ptr()), vp(lse.data_ptr()), vp(scr), vp(dq.data_ptr()),
+                                  vp(dk.data_ptr()), vp(dv.data_ptr()), vp(dth.data_ptr()), B, H, Hg, Wg, M, s, 32,
+                                  vp(tth.data_ptr()), None, None, 0, None, None, 2, stream)  # fp32 out
+
+    assert call(scratch.data_ptr() + 8) == 9  # not 16-byte aligned
+    assert call(scratch.data_ptr()) == 0
+    torch.cuda.synchronize()
+    for name, a, b in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+        assert torch.equal(a, b), name
+    # dtheta is accumulated with atomics, so its last bits follow the order of the additions
+    r3 = ref[3].cpu().numpy()
+    np.testing.assert_allclose(dth.cpu().numpy(), r3, rtol=1e-4, atol=1e-5 * float(np.abs(r3).max()))
