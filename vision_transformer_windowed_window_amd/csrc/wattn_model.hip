@@ -133,9 +133,9 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
     const uint32_t ax = base + (uint32_t)((wm + c) * 64 + 16 * (g ^ lswz(wm + c)));
     const uint32_t aw = base + (uint32_t)(LSL * 2 + (wn + c) * 64 + 16 * (g ^ lswz(wn + c)));
     u32x4 af[4], bfr[4];
-    // rows 16 i + c with i = 1..3 share (16 i + c) >> 2 & 3 = (c >> 2) & 3 ^ 0: 16 i adds
-    // 4 i to row >> 2, a multiple of 4, so the swizzle is that of row c and each fragment is
-    // 1024 bytes further on
+    // the swizzle of row base + 16 i + c is that of row c ((row >> 2) & 3, and 16 i and the
+    // sub-tile bases 0 and 64 add multiples of 4 to row >> 2), so fragment i is 1024 bytes
+    // (16 rows of 64 bytes) past fragment 0
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
         "ds_read_b128 %1, %8 offset:1024\n\t"
