@@ -68,6 +68,28 @@ def test_linear_matches_oracle(M, N, K, split, act, res, f32):
     check(got, ref, "bf16", f"linear {M}x{N}x{K}", out_bf16=not f32)
 
 
+@pytest.mark.parametrize("C", [24, 768, 1600])  # rows held in registers (1 and 6 chunks per lane); wider rows
+def test_layernorm_widths_match_oracle(C):
+    import torch
+
+    import vision_transformer_windowed_window_amd as wattn
+
+    x = round_bf16(_bf((3, 7, 5, C), 17 + C, 2.0) + np.float32(-0.25))  # 105 tokens: a ragged last workgroup
+    g = (1.0 + np.random.default_rng(C).normal(0, 0.1, C)).astype(np.float32)
+    b = np.random.default_rng(C + 1).normal(0, 0.1, C).astype(np.float32)
+    y = wattn.layernorm(_dev(x, torch.bfloat16), _dev(g, torch.float32), _dev(b, torch.float32))
+    torch.cuda.synchronize()
+    check(_np(y), oracle.layernorm(x, g, b), "bf16", f"layernorm C={C}", out_bf16=True)
+    if C == 768:  # patch merging over 4 x 384 = 1536 channels, the widest row kept in registers
+        xs = round_bf16(_bf((1, 6, 10, 384), 19, 1.5))
+        g4 = (1.0 + np.random.default_rng(20).normal(0, 0.1, 1536)).astype(np.float32)
+        b4 = np.random.default_rng(21).normal(0, 0.1, 1536).astype(np.float32)
+        m = wattn.patch_merge_norm(_dev(xs, torch.bfloat16), _dev(g4, torch.float32), _dev(b4, torch.float32))
+        torch.cuda.synchronize()
+        cat = np.concatenate([xs[:, 0::2, 0::2], xs[:, 1::2, 0::2], xs[:, 0::2, 1::2], xs[:, 1::2, 1::2]], axis=-1)
+        check(_np(m), oracle.layernorm(cat, g4, b4), "bf16", "merge norm C=4x384", out_bf16=True)
+
+
 def test_layernorm_and_patch_merge_match_oracle():
     import torch
 

@@ -276,6 +276,90 @@ __global__ __launch_bounds__(256) void wattn_layernorm_kernel(const uint16_t* __
   }
 }
 
+// The same for rows of at most 16 * CPL chunks (the normalised width of the model's norms is at
+// most 1536): each lane keeps its CPL chunks of the row in registers between the two passes,
+// and the workgroup stages gamma and beta in LDS.  Every row load is issued (a lane past the
+// row's chunks reloads the last chunk and zeroes it), before the gain and bias loads, so one
+// memory latency covers them all.
+constexpr int LN_MAXC = 1536;
+
+template <bool GATHER, int CPL>
+__global__ __launch_bounds__(256) void wattn_layernorm_reg_kernel(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ gamma,
+                                                                  const float* __restrict__ beta,
+                                                                  uint16_t* __restrict__ y, const NormPlan P) {
+  __shared__ __align__(16) float sG[LN_MAXC];
+  __shared__ __align__(16) float sBt[LN_MAXC];
+  const int tid = threadIdx.x, l16 = tid & 15;
+  const int64_t t0 = (int64_t)blockIdx.x * 16 + (tid >> 4);  // output token
+  const bool valid = t0 < P.T;
+  const int64_t t = valid ? t0 : P.T - 1;
+  const int Ct = GATHER ? 4 * P.C : P.C;  // channels of the normalised row
+  const int nch = Ct / 8;
+  int64_t src[4];
+  if (GATHER) {
+    const int Wo = P.Wg / 2, Ho = P.Hg / 2;
+    const int64_t b = t / ((int64_t)Ho * Wo);
+    const int rem = (int)(t - b * Ho * Wo);
+    const int i = rem / Wo, jx = rem - i * Wo;
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      src[qd] = ((b * P.Hg + 2 * i + (qd & 1)) * P.Wg + 2 * jx + (qd >> 1)) * P.C;
+  } else {
+    src[0] = t * P.C;
+  }
+  auto chunk_ptr = [&](int j) -> const uint16_t* {
+    if (!GATHER) return x + src[0] + 8 * j;
+    const int part = (8 * j) / P.C;
+    return x + src[part] + (8 * j - part * P.C);
+  };
+  u32x4 xr[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) xr[i] = *reinterpret_cast<const u32x4*>(chunk_ptr(min(l16 + 16 * i, nch - 1)));
+  for (int i = tid; i < Ct; i += 256) {
+    sG[i] = gamma[i];
+    sBt[i] = beta[i];
+  }
+  float s = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    if (l16 + 16 * i >= nch) xr[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = bf_lo(xr[i][p]), b2 = bf_hi(xr[i][p]);
+      s += a + b2;
+      s2 = fmaf(a, a, fmaf(b2, b2, s2));
+    }
+  }
+  s = sum16(s);
+  s2 = sum16(s2);
+  const float mean = s / Ct;
+  const float var = fmaxf(s2 / Ct - mean * mean, 0.f);
+  const float rstd = rsqrtf(var + P.eps);
+  __syncthreads();  // sG, sBt
+  if (!valid) return;
+  uint16_t* yo = y + t * Ct;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int j = l16 + 16 * i;
+    if (j >= nch) break;
+    const float4 g0 = *reinterpret_cast<const float4*>(&sG[8 * j]);
+    const float4 g1 = *reinterpret_cast<const float4*>(&sG[8 * j + 4]);
+    const float4 b0 = *reinterpret_cast<const float4*>(&sBt[8 * j]);
+    const float4 b1 = *reinterpret_cast<const float4*>(&sBt[8 * j + 4]);
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    u32x4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float a = (bf_lo(xr[i][p]) - mean) * rstd * gg[2 * p] + bb[2 * p];
+      const float b2 = (bf_hi(xr[i][p]) - mean) * rstd * gg[2 * p + 1] + bb[2 * p + 1];
+      o[p] = pack_bf16(a, b2);
+    }
+    *reinterpret_cast<u32x4*>(yo + 8 * j) = o;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Overlapping stem: out[b][i][j][o] = bias[o] + sum_{c, di, dj} W[o][c][di][dj]
 // img[b][p i + di - (p-1)][p j + dj - (p-1)][c], kernel k = 2p - 1, zero padding.  A thread
@@ -393,16 +477,29 @@ hipError_t wattn_launch_linear(const LinearPlan& P, int act, bool res, bool out_
   return hipGetLastError();
 }
 
+template <bool G>
+static hipError_t launch_layernorm_g(const NormPlan& P, const void* x, const float* gamma, const float* beta, void* y,
+                                     hipStream_t stream) {
+  const dim3 grid((unsigned)((P.T + 15) / 16));
+  auto X = static_cast<const uint16_t*>(x);
+  auto Y = static_cast<uint16_t*>(y);
+  const int Ct = G ? 4 * P.C : P.C;
+  const int cpl = (Ct / 8 + 15) / 16;  // chunks per lane
+#define WATTN_LN(K) hipLaunchKernelGGL(K, grid, dim3(256), 0, stream, X, gamma, beta, Y, P)
+  if (Ct > LN_MAXC) WATTN_LN((wattn_layernorm_kernel<G>));
+  else if (cpl <= 1) WATTN_LN((wattn_layernorm_reg_kernel<G, 1>));
+  else if (cpl <= 2) WATTN_LN((wattn_layernorm_reg_kernel<G, 2>));
+  else if (cpl <= 3) WATTN_LN((wattn_layernorm_reg_kernel<G, 3>));
+  else if (cpl <= 6) WATTN_LN((wattn_layernorm_reg_kernel<G, 6>));
+  else WATTN_LN((wattn_layernorm_reg_kernel<G, 12>));
+#undef WATTN_LN
+  return hipGetLastError();
+}
+
 hipError_t wattn_launch_layernorm(const NormPlan& P, bool gather, const void* x, const float* gamma,
                                   const float* beta, void* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((P.T + 15) / 16));
-  if (gather)
-    hipLaunchKernelGGL((wattn_layernorm_kernel<true>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(x),
-                       gamma, beta, static_cast<uint16_t*>(y), P);
-  else
-    hipLaunchKernelGGL((wattn_layernorm_kernel<false>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(x), gamma, beta, static_cast<uint16_t*>(y), P);
-  return hipGetLastError();
+  return gather ? launch_layernorm_g<true>(P, x, gamma, beta, y, stream)
+                : launch_layernorm_g<false>(P, x, gamma, beta, y, stream);
 }
 
 hipError_t wattn_launch_stem(const StemPlan& P, const void* img, const void* W, const float* bias, void* y,
