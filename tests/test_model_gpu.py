@@ -39,6 +39,7 @@ def _bf(shape, seed, scale=1.0):
     (3000, 96, 384, 96, 0, True, False),      # fc2 + residual, in place
     (16, 1000, 768, 1000, 0, False, True),    # head: fp32 logits, N not a multiple of 16
     (77, 68, 32, 68, 0, False, False),        # ragged M and N
+    (200, 132, 3072, 132, 0, True, False),    # the longest K of the model (96 k slices), residual
 ])
 def test_linear_matches_oracle(M, N, K, split, act, res, f32):
     import torch
