@@ -152,6 +152,22 @@ def test_sr_m96_rib_full_size_sampled():
     check(g, r, cfg.dtype, f"sr_m96_rib ({len(units)} window-heads)")
 
 
+@pytest.mark.parametrize("shift", [0, 64])
+def test_largest_window(shift):
+    """M = 128, the largest window the library takes: one 16384-token window per head (at shift
+    64 it splits into four wrap regions), RoPE with the 130-row table of the 8-wave kernel.  The
+    oracle computes the whole window-head of each of the two heads."""
+    M, H = 128, 2
+    note(f"start M=128 shift={shift}")
+    q, k, v = qkv((1, 128, 128, H, 32), 4100 + shift, "bf16")
+    inp = dict(q=q, k=k, v=v, theta=theta_table(H, 32, 0.1, 4101), bias_u=None, bias_v=None)
+    got = run_gpu(inp, "bf16", M, shift)
+    refs = oracle_sampled(inp, M, shift, [(0, 0, 0, 0), (0, 0, 0, 1)])
+    g = np.concatenate([got[b, y, x, h, :] for (b, y, x, h, _) in refs])
+    r = np.concatenate([o for (_, _, _, _, o) in refs])
+    check(g, r, "bf16", f"M=128 shift={shift}")
+
+
 # --------------------------------------------------------------------- other properties
 
 
