@@ -75,6 +75,7 @@ CASES = [
     ("m16_s8_bias_bf16_out", 1, 32, 32, 2, 16, 8, True, False, 16),
     ("m24_s0_bias_norope", 2, 48, 48, 1, 24, 0, False, True, 16),
     ("m40_s13_bias", 1, 40, 80, 1, 40, 13, True, True, 16),
+    ("m128_s64", 1, 128, 128, 1, 128, 64, True, True),  # the largest window, four wrap regions
 ]
 
 
