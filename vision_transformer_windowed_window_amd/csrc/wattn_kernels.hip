@@ -74,7 +74,7 @@ constexpr int MAXM = 128;      // largest window side (cos/sin table rows)
 __device__ __forceinline__ float sigmoidf_fast(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * LOG2E));
 }
-constexpr float RESCALE_LIMIT = 65536.0f;  // 2^16
+constexpr float REF_HEADROOM = 16.0f;  // the forward reference sits this far (base 2) above the row maximum
 
 struct Task {
   int b, h, q0;
@@ -387,33 +387,36 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
 
   // ---- online-softmax state per query block a (lanes c, c+16, c+32, c+48 share a query)
   f32x4 O[2][2];  // [dim block][query block]: dims 16 db + 4 g + e of query 16 a + c
-  f32x4 Cn[2];    // -m broadcast, the accumulator preset of the score product
-  float m[2], l[2];
+  f32x4 L[2];     // row sums: every entry of L[a] is the running sum of query 16 a + c
+  f32x4 Cn[2];    // -r broadcast, the accumulator preset of the score product
+  float r[2];     // reference of the query (base 2): p = 2^(s - r)
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     O[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
     O[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    L[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     Cn[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[a] = 0.f;
-    l[a] = 0.f;
+    r[a] = 0.f;
   }
   const int n = X.n;
   const bool wave_live = X.t.q0 + wave * 32 < n;  // wave-uniform
+  const u32x4 ONES4 = {ONES, ONES, ONES, ONES};   // bf16 ones: the row-sum operand
 
-  // one key tile: four 32-key steps of the score product, online softmax and value product
   // LDS operand fragments of one 32-key step
-  struct Frags {
+  struct KFrags {
     u32x4 Kf[2];  // score operand A: key kb + 8(c/4) + 4b + c%4, channels 8g .. 8g+7 (fp16)
     u32x4 Kb[2];  // bias operand A: channels 8(g%2) .. 8(g%2)+7 of the same keys
-    u32x4 V[2];   // value operand A (V^T): dims 16 db + c, keys kb + 8g .. 8g+7
   };
-  auto load_frags = [&](int buf, int kb, Frags& F) {
+  auto load_kfrags = [&](int buf, int kb, KFrags& F) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int key = kb + krow + 4 * b;
       F.Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
       if (BIAS) F.Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
     }
+  };
+  // value operand A (V^T): dims 16 db + c, keys kb + 8g .. 8g+7
+  auto load_vfrags = [&](int buf, int kb, u32x4 (&Vf)[2]) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       u32x2 h[2];
@@ -423,27 +426,36 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
         const int ch = 2 * db + vch;
         h[hh] = lds_read_tr16(&sV[buf][row * D + ((ch ^ vswz(row)) * 8) + vsub]);
       }
-      F.V[db] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+      Vf[db] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
     }
   };
 
-  // one key tile: up to four 32-key steps; the fragments of step st + 1 are read from LDS
-  // while step st is computed
+  // One key tile: up to four 32-key steps.  The score fragments of step st + 1 are read from
+  // LDS while step st is computed; the value fragments of a step are read at its start and
+  // land while its exponentials run.
+  //
+  // Lazy reference: p = 2^(s - r) with r at least 16 above every score seen when it was
+  // set, so p <= 2^-16 until a score exceeds the running maximum by more than 16.  A step
+  // in which some p reaches 2 (bf16 exponent bit 7 set in one of the packed pairs; an
+  // overflow to inf sets it too) is redone exactly: r grows to the step's row maximum + 16
+  // and O and the row sums are scaled by 2^-delta.  Row sums are accumulated on the matrix
+  // core (bf16 ones times P^T), over exactly the bf16 P the value product consumes.
   auto compute_tile = [&](int buf, int tile) {
     if (!wave_live) return;
     const int nst = min(KT / 32, (n - tile * KT + 31) / 32);  // steps holding keys (uniform)
-    Frags F[2];
-    load_frags(buf, 0, F[0]);
+    KFrags F[2];
+    load_kfrags(buf, 0, F[0]);
 #pragma unroll
     for (int st = 0; st < KT / 32; ++st) {
       if (st < nst) {
         const int kg = tile * KT + st * 32;  // first key of the step (uniform)
-        const Frags& cur = F[st & 1];
-        if (st + 1 < nst) load_frags(buf, (st + 1) * 32, F[(st + 1) & 1]);
+        const KFrags& cur = F[st & 1];
+        u32x4 Vf[2];
+        load_vfrags(buf, st * 32, Vf);
+        if (st + 1 < nst) load_kfrags(buf, (st + 1) * 32, F[(st + 1) & 1]);
 
-        // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus m
+        // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus r
         f32x4 S[2][2];
-        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -453,7 +465,6 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
             S[a][b] = BIAS ? mfma16_f16(cur.Kb[b], Qb[a], Cn[a]) : Cn[a];
             S[a][b] = mfma16_f16(cur.Kf[b], Qf[a], S[a][b]);
           }
-        __builtin_amdgcn_s_setprio(0);
         if (kg + 32 > n) {
 #pragma unroll
           for (int a = 0; a < 2; ++a)
@@ -465,21 +476,19 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
         }
         const bool first = (tile == 0) && (st == 0);
         uint32_t Pp[2][4];
-        float ln[2];  // this lane's share of the row sum after the step
         bool exact = first;
         if (!first) {
+          uint32_t bits = 0u;
 #pragma unroll
-          for (int a = 0; a < 2; ++a) {
+          for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const f32x4& s = S[a][t >> 1];
               const int e0 = 2 * (t & 1);
               Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0]), __builtin_amdgcn_exp2f(s[e0 + 1]));
+              bits |= Pp[a][t];
             }
-            ln[a] = dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, l[a]))));
-          }
-          // the step's own sum (all p >= 0): above the limit iff some p is near or above it
-          exact = __any(fmaxf(ln[0] - l[0], ln[1] - l[1]) > RESCALE_LIMIT);
+          exact = __any((bits & 0x40004000u) != 0u);  // some p >= 2 (or inf / NaN)
         }
         if (exact) {
 #pragma unroll
@@ -487,30 +496,30 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
             float mx = fmaxf(fmaxf(S[a][0][0], S[a][0][1]), fmaxf(S[a][0][2], S[a][0][3]));
             mx = fmaxf(mx, fmaxf(fmaxf(S[a][1][0], S[a][1][1]), fmaxf(S[a][1][2], S[a][1][3])));
             mx = xmax32(xmax16(mx));
-            const float delta = first ? mx : fmaxf(mx, 0.f);
+            // first step: reference = row max + 16; later: grow only where the step passed r
+            const float delta = (first || mx > 0.f) ? mx + REF_HEADROOM : 0.f;
             if (!first) {
               const float f = __builtin_amdgcn_exp2f(-delta);
-              l[a] *= f;
+              L[a] *= f;
               O[0][a] *= f;
               O[1][a] *= f;
             }
-            m[a] += delta;
-            Cn[a] = f32x4{-m[a], -m[a], -m[a], -m[a]};
+            r[a] += delta;
+            Cn[a] = f32x4{-r[a], -r[a], -r[a], -r[a]};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
               const f32x4& s = S[a][t >> 1];
               const int e0 = 2 * (t & 1);
               Pp[a][t] = pack_bf16(__builtin_amdgcn_exp2f(s[e0] - delta), __builtin_amdgcn_exp2f(s[e0 + 1] - delta));
             }
-            ln[a] = dot2_bf16(Pp[a][3], ONES, dot2_bf16(Pp[a][2], ONES, dot2_bf16(Pp[a][1], ONES, dot2_bf16(Pp[a][0], ONES, l[a]))));
           }
         }
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-          l[a] = ln[a];
           const u32x4 Pa = {Pp[a][0], Pp[a][1], Pp[a][2], Pp[a][3]};  // keys kb + 8g .. 8g+7 of query 16a + c
 #pragma unroll
-          for (int db = 0; db < 2; ++db) O[db][a] = mfma16_bf16(cur.V[db], Pa, O[db][a]);
+          for (int db = 0; db < 2; ++db) O[db][a] = mfma16_bf16(Vf[db], Pa, O[db][a]);
+          L[a] = mfma16_bf16(ONES4, Pa, L[a]);
         }
       }
     }
@@ -532,7 +541,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
   // ---- epilogue: normalise, scatter to the original positions
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const float lt = xsum32(xsum16(l[a]));
+    const float lt = L[a][0];
     const int iq = X.t.q0 + wave * 32 + 16 * a + c;
     if (iq < n) {
       const float inv = 1.0f / lt;
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       split_idx(X, (uint32_t)iq, li, lj);
       const int64_t off = X.img + X.regbase + li * rowstride + lj * colstride;
       // natural-log log-sum-exp of the row: m and l are kept in base 2 (log2(e) folded into q)
-      if (lse != nullptr && g == 0) lse[off / D] = (m[a] + __log2f(lt)) * LN2;
+      if (lse != nullptr && g == 0) lse[off / D] = (r[a] + __log2f(lt)) * LN2;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         f32x4 o = O[db][a] * inv;
