@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="time only the named workload (by default the forward pass also times the other "
+                         "bf16 workloads for a few seconds each, reported under 'configs')")
+    ap.add_argument("--sweep-steps", type=int, default=30, help="timed steps of each swept workload")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack", "model"],
                     help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path; "
                          "stack: six layers with cyclic windows and the convolutional gate; "
@@ -115,6 +119,9 @@ def pipe_bound(exps: float, mfma_flops: float, kernel_s: float):
     simds = rates["simds"]
     t_exp = exps / 64.0 * ns["exp_f32"] / simds * 1e-3          # us, 64 lanes per instruction
     t_mfma = mfma_flops / MFMA_FLOPS * ns["mfma_f32_16x16x32_bf16"] / simds * 1e-3
+    # the attention kernel's steady state: one 32 x 32 step per 1024 executed pairs, on every SIMD
+    step_ns = rates.get("softmax_step_ns")
+    t_steps = exps / 1024.0 / simds * step_ns * 1e-3 if step_ns else None
     return {
         "source": "vision_transformer_windowed_window_amd/pipe_rates",
         "ns_per_instruction": ns,
@@ -124,6 +131,10 @@ def pipe_bound(exps: float, mfma_flops: float, kernel_s: float):
         "kernel_vs_exp_plus_mfma": (t_exp + t_mfma) / (kernel_s * 1e6),
         "mfma_fma_split_vs_serial": rates["split_mfma_fma_ns_per_iteration"] / rates["serial_mfma_fma_ns_per_iteration"],
         "mfma_exp_interleaved_vs_serial": rates["interleaved_4mfma_16exp_ns"] / rates["serial_4mfma_16exp_ns"],
+        "softmax_step_ns": step_ns,
+        "steady_state_step_floor_us": t_steps,
+        "kernel_vs_step_floor": (t_steps / (kernel_s * 1e6)) if t_steps else None,
+        "shader_clock_ghz_mfma_load": rates.get("shader_clock_ghz_mfma_load"),
     }
 
 
@@ -597,6 +608,120 @@ def main_model(args):
     print(json.dumps(rec), flush=True)
 
 
+def make_fwd_sets(cfg, args, torch, dev):
+    """Resident input sets of a forward workload (the batch permuted per set) and its parameters."""
+    import numpy as np
+
+    from inputs import make_inputs
+
+    tdt = torch.bfloat16
+    odt = torch.float32 if args.out_dtype == "fp32" else torch.bfloat16
+    base = make_inputs(cfg)
+    sets = []
+    for i in range(args.input_sets):
+        g = torch.Generator(device="cpu").manual_seed(i)
+        perm = torch.randperm(cfg.B, generator=g) if i else torch.arange(cfg.B)
+        t = {key: torch.from_numpy(np.ascontiguousarray(base[key])).to(tdt)[perm].contiguous().to(dev)
+             for key in ("q", "k", "v")}
+        t["out"] = torch.empty(t["q"].shape, dtype=odt, device=dev)
+        sets.append(t)
+    params = {
+        "theta": None if base["theta"] is None else torch.from_numpy(base["theta"]).to(dev),
+        "bias_u": None if base["bias_u"] is None else torch.from_numpy(base["bias_u"]).to(tdt).to(dev),
+        "bias_v": None if base["bias_v"] is None else torch.from_numpy(base["bias_v"]).to(tdt).to(dev),
+    }
+    return sets, params
+
+
+def time_steps(step, steps: int, warmup: int, torch, warmup_min_s: float = WARMUP_MIN_S):
+    """Untimed warm-up, then `steps` back-to-back steps bracketed by events on the stream the
+    kernels run on.  Returns (wall seconds per step, kernel seconds per step, peak extra bytes)."""
+    # The GPU's clocks only reach their sustained level after tens of milliseconds of load, so
+    # the warm-up runs at least warmup_min_s seconds of back-to-back launches.
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or (time.perf_counter() - t_w < warmup_min_s and i < WARMUP_MAX_STEPS):
+        step(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    # The host enqueues faster than the kernel runs, so the stream never idles between the
+    # launches and the event interval over K is the kernel's average duration.
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    peak_extra = torch.cuda.max_memory_allocated() - mem0
+    return elapsed / steps, ev0.elapsed_time(ev1) / steps / 1e3, int(peak_extra)
+
+
+def fwd_figures(cfg, wattn, out_dtype: str, which: str, kernel_s: float):
+    """Flop and byte counts of one step and the roofline record of the dominant kernel."""
+    dense = cfg.dense_flops() * (2.5 if which == "bwd" else 1.0)  # backward: 5 products vs 2
+    pairs = wattn.pair_count(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, cfg.shift)
+    executed = 2.0 * pairs * (cfg.d + cfg.r + cfg.d)
+    osz = 4 if out_dtype == "fp32" else 2
+    el = cfg.tokens * cfg.H * cfg.d
+    if which == "fwd":
+        alg_bytes = 3 * el * 2 + el * osz  # q, k, v read once, out written once
+    else:
+        executed *= 2.5
+        # q, k, v, out, dout and lse read once; dq, dk, dv and the row scratch written once
+        alg_bytes = 3 * el * 2 + 2 * el * osz + cfg.tokens * cfg.H * 4 + 3 * el * 4 + cfg.tokens * cfg.H * 4
+    compute_bound = cfg.N / 2 >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3  # AI vs ridge (FLOP/B)
+    if compute_bound:
+        achieved = dense / kernel_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    else:
+        achieved = alg_bytes / kernel_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    return dense, pairs, executed, alg_bytes, roof
+
+
+def sweep_record(cfg, args, wattn, torch, dev):
+    """Time one more forward workload briefly (a few seconds) with the headline's protocol."""
+    sets, prm = make_fwd_sets(cfg, args, torch, dev)
+
+    def step(i):
+        t = sets[i % len(sets)]
+        wattn.forward(t["q"], t["k"], t["v"], M=cfg.M, shift=cfg.shift, theta=prm["theta"], bias_u=prm["bias_u"],
+                      bias_v=prm["bias_v"], out=t["out"])
+
+    steps = max(5, min(args.steps, args.sweep_steps))
+    wall_s, kern_s, peak_extra = time_steps(step, steps, 3, torch, warmup_min_s=0.2)
+    dense, pairs, executed, alg_bytes, roof = fwd_figures(cfg, wattn, args.out_dtype, "fwd", kern_s)
+    roof["traffic"] = traffic_from_profiles(cfg.name, args.out_dtype)
+    del sets
+    torch.cuda.empty_cache()
+    return {
+        "shape": {"B": cfg.B, "Hgrid": cfg.Hg, "Wgrid": cfg.Wg, "M": cfg.M, "shift": cfg.shift, "H": cfg.H,
+                  "d": cfg.d, "r": cfg.r, "rope": cfg.rope},
+        "steps": steps,
+        "kernel_ms": kern_s * 1e3,
+        "ms_per_step": wall_s * 1e3,
+        "tokens_per_s": cfg.tokens / kern_s,
+        "tflops_dense_kernel": dense / kern_s / 1e12,
+        "tflops_executed_kernel": executed / kern_s / 1e12,
+        "pct_bf16_peak_dense": 100.0 * dense / kern_s / 1e12 / PEAK_BF16_TFLOPS,
+        "algorithmic_gbs_kernel": alg_bytes / kern_s / 1e9,
+        "pct_hbm_peak": 100.0 * alg_bytes / kern_s / 1e9 / PEAK_HBM_GBS,
+        "peak_extra_device_bytes": peak_extra,
+        "materialised_scores_bytes": int(cfg.tokens * cfg.H * cfg.N * 4),
+        "roofline": roof,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -614,33 +739,20 @@ def main():
         main_model(args)
         return
 
-    import numpy as np
     import torch
 
     import vision_transformer_windowed_window_amd as wattn
-    from inputs import CONFIGS, make_inputs
+    from inputs import CONFIGS
 
     cfg = CONFIGS[args.workload]
     assert cfg.dtype == "bf16", "the benchmark covers the bf16 workloads"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    tdt = torch.bfloat16
     odt = torch.float32 if args.out_dtype == "fp32" else torch.bfloat16
 
     # ---- inputs resident in HBM (several sets, rotated)
-    base = make_inputs(cfg)
-    sets = []
-    for i in range(args.input_sets):
-        g = torch.Generator(device="cpu").manual_seed(i)
-        perm = torch.randperm(cfg.B, generator=g) if i else torch.arange(cfg.B)
-        t = {key: torch.from_numpy(np.ascontiguousarray(base[key])).to(tdt)[perm].contiguous().to(dev)
-             for key in ("q", "k", "v")}
-        t["out"] = torch.empty(t["q"].shape, dtype=odt, device=dev)
-        sets.append(t)
-    theta = None if base["theta"] is None else torch.from_numpy(base["theta"]).to(dev)
-    bu = None if base["bias_u"] is None else torch.from_numpy(base["bias_u"]).to(tdt).to(dev)
-    bv = None if base["bias_v"] is None else torch.from_numpy(base["bias_v"]).to(tdt).to(dev)
-    del base
+    sets, prm = make_fwd_sets(cfg, args, torch, dev)
+    theta, bu, bv = prm["theta"], prm["bias_u"], prm["bias_v"]
 
     def step(i):
         t = sets[i % len(sets)]
@@ -660,60 +772,11 @@ def main():
             wattn.backward(t["q"], t["k"], t["v"], t["out"], t["dout"], t["lse"], M=cfg.M, shift=cfg.shift,
                            theta=theta, bias_u=bu, bias_v=bv)
 
-    # Untimed warm-up: W steps, continued until at least WARMUP_MIN_S seconds of back-to-back
-    # launches have run, because the GPU's clocks only reach their sustained level after tens
-    # of milliseconds of load (a handful of launches measures the ramp, not the kernel).
-    t_w = time.perf_counter()
-    i = 0
-    while i < args.warmup or (time.perf_counter() - t_w < WARMUP_MIN_S and i < WARMUP_MAX_STEPS):
-        step(i)
-        i += 1
-        if i % 50 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    mem0 = torch.cuda.memory_allocated()
-    torch.cuda.reset_peak_memory_stats()
-
-    # The K launches go back to back into the stream the kernel runs on; two events bracket
-    # them there, so their interval over K is the kernel's average duration (the host
-    # enqueues faster than the kernel runs, so the stream never idles between launches).
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    peak_extra = torch.cuda.max_memory_allocated() - mem0
-
-    ms_per_step = elapsed * 1e3 / args.steps
+    wall_s, avg_kern_s, peak_extra = time_steps(step, args.steps, args.warmup, torch)
+    ms_per_step = wall_s * 1e3
     tokens = cfg.tokens
-    value = tokens / (ms_per_step / 1e3)
-    avg_kern_s = ev0.elapsed_time(ev1) / args.steps / 1e3
-    dense = cfg.dense_flops() * (2.5 if args.which == "bwd" else 1.0)  # backward: 5 products vs 2
-    pairs = wattn.pair_count(cfg.B, cfg.H, cfg.Hg, cfg.Wg, cfg.M, cfg.shift)
-    d_qk = cfg.d + cfg.r
-    executed = 2.0 * pairs * (d_qk + cfg.d)
-    osz = 4 if args.out_dtype == "fp32" else 2
-    el = tokens * cfg.H * cfg.d
-    if args.which == "fwd":
-        alg_bytes = 3 * el * 2 + el * osz  # q, k, v read once, out written once
-    else:
-        executed *= 2.5
-        # q, k, v, out, dout and lse read once; dq, dk, dv and the row scratch written once
-        alg_bytes = 3 * el * 2 + 2 * el * osz + tokens * cfg.H * 4 + 3 * el * 4 + tokens * cfg.H * 4
-    compute_bound = cfg.N / 2 >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3  # AI vs ridge (FLOP/B)
-    if compute_bound:
-        achieved = dense / avg_kern_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS}
-    else:
-        achieved = alg_bytes / avg_kern_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
+    value = tokens / wall_s
+    dense, pairs, executed, alg_bytes, roof = fwd_figures(cfg, wattn, args.out_dtype, args.which, avg_kern_s)
     roof["traffic"] = traffic_from_profiles(args.workload if args.which == "fwd" else args.workload + "_bwd",
                                             args.out_dtype)
 
@@ -736,18 +799,29 @@ def main():
             "H": cfg.H, "d": cfg.d, "r": cfg.r, "rope": cfg.rope, "out_dtype": args.out_dtype,
             "global_batch": cfg.B, "tokens_per_step": tokens, "input_sets": args.input_sets,
         },
-        "tflops_dense": dense / (ms_per_step / 1e3) / 1e12,
-        "pct_bf16_peak_dense": 100.0 * dense / (ms_per_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "tflops_dense": dense / wall_s / 1e12,
+        "pct_bf16_peak_dense": 100.0 * dense / wall_s / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_ms_avg": avg_kern_s * 1e3,
         "tflops_dense_kernel": dense / avg_kern_s / 1e12,
         "tflops_executed_kernel": executed / avg_kern_s / 1e12,
         "mfma_frac_executed": executed / avg_kern_s / 1e12 / PEAK_BF16_TFLOPS,
         "algorithmic_gbs_kernel": alg_bytes / avg_kern_s / 1e9,
-        "peak_extra_device_bytes": int(peak_extra),
+        "peak_extra_device_bytes": peak_extra,
         "roofline": roof,
     }
     if args.which == "fwd":
         rec["pipe_bound"] = pipe_bound(float(pairs), executed, avg_kern_s)
+        if rec["pipe_bound"] is not None:
+            rec["shader_clock_ghz"] = rec["pipe_bound"].get("shader_clock_ghz_mfma_load")
+        if not args.no_sweep:
+            # the other workloads of the forward pass, each timed for a few seconds after the
+            # headline (the tiny fp32 case is a parity case only)
+            del sets
+            torch.cuda.empty_cache()
+            rec["configs"] = {}
+            for name in ("swin_t_m8", "large_m32", "dense_p2_m16", "dense_p2_m8", "sr_m96_rib"):
+                if name != cfg.name:
+                    rec["configs"][name] = sweep_record(CONFIGS[name], args, wattn, torch, dev)
     else:
         rec["config"]["pass"] = "backward (dq, dk, dv, dtheta" + (", dbias_u, dbias_v" if cfg.r else "") + ")"
     if not args.no_cpu_baseline:
