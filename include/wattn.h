@@ -136,7 +136,7 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
 
 /*
  * wattn_backward_scratch_bytes -- bytes of the scratch buffer wattn_backward and
- * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 32 T) with T = B Hgrid Wgrid H
+ * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 32 T) + 16 with T = B Hgrid Wgrid H
  * query rows.  -1 for a size <= 0 or d != 32.
  */
 int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
@@ -157,8 +157,9 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *   scratch : wattn_backward_scratch_bytes(B, H, Hgrid, Wgrid, d) bytes of device memory,
  *             16-byte aligned (WATTN_ERR_POINTER otherwise), contents undefined on entry and
  *             on return.  The query-tile kernel writes rowsum(dout * out) per query, the
- *             rotated and scaled queries (fp16) and the output gradient (bf16) there once;
- *             the key-tile kernel streams them back instead of redoing that work per tile.
+ *             rotated and scaled queries (fp16), the output gradient (bf16) and the largest
+ *             output-gradient entry there once; the key-tile kernel streams them back
+ *             instead of redoing that work per tile.
  *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
  *   dtheta  : float32 [H][d/2] (zeroed, then accumulated with atomic adds, so its last bits
  *             depend on the order of the additions); required iff theta is not NULL.
@@ -175,7 +176,11 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *
  * Numerics: the scores are recomputed as in the forward pass (fp16 operands, P =
  * exp2(s log2(e) - lse log2(e)) in fp32); P is rounded to bf16 for dv, dS = P (dP - delta)
- * to fp16 for dq and dk; everything accumulates in fp32.
+ * to fp16 for dq and dk; everything accumulates in fp32.  dS is rounded with a power-of-two
+ * scale 2^e that puts the largest output-gradient entry in [4, 8) (per query row for dq and
+ * dbias_u, over the whole call for dk, dv and dbias_v; |e| <= 96), and the fp32 products
+ * are divided by 2^e, so the relative accuracy of every gradient does not depend on the
+ * magnitude of dout (gradients scale exactly with a power-of-two factor on dout).
  */
 int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                    const float* lse, float* scratch, float* dq, float* dk, float* dv, float* dtheta,

@@ -158,10 +158,11 @@ def test_backward_rejects_invalid_arguments(kw, status):
 
 
 def test_backward_scratch_bytes():
-    # 512 query rows: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32 bf16 gradients
-    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32
+    # 512 query rows: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32 bf16
+    # gradients, then 16 bytes for the largest output-gradient entry
+    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32 + 16
     # 3 rows: the statistics are padded to 4 floats so the rows after them start 16-byte aligned
-    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32
+    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32 + 16
     assert _lib().wattn_backward_scratch_bytes(0, 2, 16, 16, 32) == -1
     assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 64) == -1
 

@@ -81,10 +81,18 @@ CASES = [
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_matches_oracle(case):
+    _check_case(case)
+
+
+def _check_case(case, dout_scale=1.0):
     label, B, Hg, Wg, H, M, s, rope, out_f32 = case[:9]
     r = case[9] if len(case) > 9 else 0
     note(f"backward {label}: B={B} grid={Hg}x{Wg} H={H} M={M} shift={s} rope={rope} fp32_out={out_f32} r={r}")
     q, k, v, th, dout, U, V = _setup(B, Hg, Wg, H, M, 900 + M + s, rope, out_f32, r)
+    if dout_scale != 1.0:
+        dout = (dout * dout_scale).astype(np.float32)
+        if not out_f32:
+            dout = round_bf16(dout)
     got = _gpu(q, k, v, th, dout, M, s, out_f32, U, V)
     # the row-statistic forward pass writes the same output as the plain one, bit for bit
     assert np.array_equal(got["out"], got["plain"])
@@ -104,6 +112,23 @@ def test_backward_matches_oracle(case):
         assert got["dtheta"] is None
     if not r:
         assert got["dbias_u"] is None and got["dbias_v"] is None
+
+
+# Output gradients far from N(0, 1) (training gradients are often ~1e-4 .. 1e-8 per entry):
+# without its power-of-two scale, dS = P (dP - D) rounded to fp16 would fall into the
+# subnormal range or flush to zero and dq / dk would lose their accuracy.  The bounds are the
+# relative ones above, so the gradients must keep their accuracy at every scale.
+SCALE_CASES = [
+    ("m32_s16_x1e-6", 1e-6, ("m32_s16", 1, 64, 64, 2, 32, 16, True, True)),
+    ("m32_s16_x1e3", 1e3, ("m32_s16", 1, 64, 64, 2, 32, 16, True, True)),
+    ("m16_s8_bias_x1e-8", 1e-8, ("m16_s8_bias", 1, 32, 32, 2, 16, 8, True, True, 16)),
+    ("m32_s16_bf16_out_x1e-5", 1e-5, ("m32_s16_bf16_out", 1, 64, 64, 1, 32, 16, True, False)),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=[c[0] for c in SCALE_CASES])
+def test_backward_output_gradient_scale(case):
+    _check_case(case[2], dout_scale=case[1])
 
 
 def test_backward_scratch_contract():
@@ -128,7 +153,7 @@ def test_backward_scratch_contract():
     lib = wattn.load_library()
     nbytes = lib.wattn_backward_scratch_bytes(B, H, Hg, Wg, 32)
     rows = B * Hg * Wg * H
-    assert nbytes == 4 * ((rows + 3) // 4 * 4 + 32 * rows)
+    assert nbytes == 4 * ((rows + 3) // 4 * 4 + 32 * rows) + 16
     scratch = torch.full((nbytes + 64,), 0xFF, dtype=torch.uint8, device=dev)  # NaN bytes
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
     dth = torch.empty((H, 16), dtype=torch.float32, device=dev)

@@ -270,7 +270,7 @@ namespace {
 
 // Backward scratch for `rows` query rows (T * H): the rowsum statistic as float32 [rows], padded
 // to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32] each.
-int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 32 * rows) * 4; }
+int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 32 * rows) * 4 + 16; }
 
 // Backward pass shared by wattn_backward and wattn_backward_gated (gz and dz both NULL or both set).
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,

@@ -821,6 +821,20 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
   }
 }
 
+// dS = P (dP - D) is rounded to fp16 for the products of dq and dk: its size follows dout,
+// and training gradients are often small enough that dS would fall into fp16's subnormal
+// range or to zero.  Both kernels therefore round 2^e dS instead, with e chosen from the
+// largest output-gradient entry g_max so that 2^e g_max lies in [4, 8), and divide the
+// accumulated products by 2^e in fp32.  The factor is folded into the score preset (P
+// becomes 2^e P), so it costs no instruction per score.  The query-tile kernel takes e per
+// query row (its products sum over keys only); the key-tile kernel sums over the queries of
+// a region, so it takes one e for the call, from the largest entry over all rows.
+constexpr int GRAD_EXP_LIMIT = 96;
+__device__ __forceinline__ int grad_scale_exp(float gmax) {
+  const int e = 3 - __builtin_amdgcn_frexp_expf(gmax);  // gmax in [2^(x-1), 2^x): 2^e gmax in [4, 8)
+  return max(-GRAD_EXP_LIMIT, min(GRAD_EXP_LIMIT, e));    // 0 and non-finite gmax give e = 3
+}
+
 // ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
 template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
 __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
@@ -829,13 +843,14 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu,
     const uint16_t* __restrict__ gz, float* __restrict__ dz, uint16_t* __restrict__ qt,
-    uint16_t* __restrict__ dot, const WattnPlan P) {
+    uint16_t* __restrict__ dot, uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];  // bias factor v of the keys (fp16)
   __shared__ float sDth[D / 2];
+  __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
   const int tid = threadIdx.x;
@@ -848,7 +863,8 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   if (tid < D / 2) sDth[tid] = 0.f;
 
-  // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic;
+  // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
+  //      (preset with the row's gradient-scale exponent);
   //      with a bias, u * log2(e) in channels 0..15 of a zero-padded k = 32 operand
   u32x4 qraw[2], dOf[2], Qb[2];
   f32x4 CnL[2], CnD[2];
@@ -878,6 +894,8 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
       braw[a] = *reinterpret_cast<const u32x4*>(
           bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 8 * (g & 1));
   }
+  int gexp[2];     // gradient-scale exponent of each query row
+  float wgmax = 0.f;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     float Dp = 0.f, L2 = 0.f;
@@ -908,6 +926,13 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     }
     const float Dn = xsum32(xsum16(Dp));  // the four lanes of query c hold 8 dims each
     if (qvalid[a] && g == 0) delta[qoff[a] / D] = Dn;
+    float gm = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gm = fmaxf(gm, fabsf(go[a][e]));
+    gm = xmax32(xmax16(gm));  // largest entry of the row's (gated) output gradient
+    wgmax = fmaxf(wgmax, gm);
+    gexp[a] = grad_scale_exp(gm);
+    L2 -= (float)gexp[a];     // P becomes 2^e P
     Qb[a] = u32x4{0u, 0u, 0u, 0u};
     if (BIAS && qvalid[a] && g < 2) {
 #pragma unroll
@@ -963,9 +988,22 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     }
   };
 
+  // largest output-gradient entry of the workgroup, for the key-tile kernel's scale
+  {
+    float wm = wgmax;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) wm = fmaxf(wm, __shfl_xor(wm, o));  // lanes c of a row group
+    if (lane == 0) sGmax[wave] = wm;                                      // xmax32/16 covered g
+  }
   fetch(0);
   if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
   __syncthreads();
+  if (tid == 0) {
+    float wm = sGmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) wm = fmaxf(wm, sGmax[w]);
+    atomicMax(gmax_bits, __float_as_uint(wm));  // non-negative floats order as their bits
+  }
   // queries: rotate (fp32), scale by log2(e) / sqrt(d), round to fp16
   u32x4 Qf[2];
 #pragma unroll
@@ -1093,8 +1131,9 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     for (int a = 0; a < 2; ++a) {
       if (!qvalid[a]) continue;
       float* dst = dbu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 4 * g;
+      const float us = __builtin_ldexpf(1.0f, -gexp[a]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dU[a][e]);
+      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dU[a][e] * us);
     }
   }
   // the raw q channels of the dtheta sums, all loads issued before the first use
@@ -1113,7 +1152,8 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     for (int cb = 0; cb < 2; ++cb) {
       float r4[4];
       const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];  // channels 0..15 rotate with the row
-      finish_grad4<ROPE, TSTR>(dQ[cb][a], 0.17677669529663687f, 8 * cb + 2 * g, pos, sTab, qr2[a][cb], sDth, r4);
+      finish_grad4<ROPE, TSTR>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos,
+                               sTab, qr2[a][cb], sDth, r4);
       *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
@@ -1129,7 +1169,8 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
-    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv, const WattnPlan P) {
+    const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
+    const uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
   __shared__ __align__(16) uint16_t sQ[2][QTT * D];
@@ -1149,6 +1190,10 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int M = P.M, n = X.n;
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   if (tid < D / 2) sDth[tid] = 0.f;
+  // one gradient-scale exponent for the call, from the largest output-gradient entry that
+  // the query-tile kernel found over all rows (see grad_scale_exp)
+  const int gexp = grad_scale_exp(__uint_as_float(__builtin_nontemporal_load(gmax_bits)));
+  const float gshift = (float)gexp;
 
   // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands; with a bias, the
   //      factor v_b in channels 0..15 of a zero-padded k = 32 operand
@@ -1217,7 +1262,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     *reinterpret_cast<u32x4*>(&sO[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = po;
     if (tid < QTT) {
       // a padded query gets the statistic +inf: its scores become -inf, so P = dS = 0
-      sL[buf][tid] = psv ? -pl * LOG2E : -INFINITY;
+      sL[buf][tid] = psv ? gshift - pl * LOG2E : -INFINITY;  // P becomes 2^e P
       sDl[buf][tid] = -pd;
     }
     if (bthread) {
@@ -1351,14 +1396,15 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   }
 
   // ---- the gradient of the bias factor v_b (shared by every window and image: added into its
-  //      window position with atomics; the u tile carried log2(e))
+  //      window position with atomics; the u tile carried log2(e)), all products unscaled by 2^-e
+  const float gunscale = __builtin_ldexpf(1.0f, -gexp), gunscale_ln2 = gunscale * LN2;
   if (BIAS) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!kvalid[a]) continue;
       float* dst = dbv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * 16 + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dVb[a][e] * LN2);
+      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dVb[a][e] * gunscale_ln2);
     }
   }
 
@@ -1378,10 +1424,11 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       *reinterpret_cast<float4*>(dv + koffs[a] + 16 * x + 4 * g) =
-          make_float4(dV[x][a][0], dV[x][a][1], dV[x][a][2], dV[x][a][3]);
+          make_float4(dV[x][a][0] * gunscale, dV[x][a][1] * gunscale, dV[x][a][2] * gunscale,
+                      dV[x][a][3] * gunscale);
       float r4[4];
       const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
-      finish_grad4<ROPE, TSTR>(dK[x][a], LN2, 8 * x + 2 * g, pos, sTab, kr2[a][x], sDth, r4);
+      finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], sDth, r4);
       *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
@@ -1475,7 +1522,7 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
                                   float* dbv, const void* gz, float* dz, uint16_t* qt, uint16_t* dot,
-                                  hipStream_t stream) {
+                                  uint32_t* gmax, hipStream_t stream) {
   if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
@@ -1486,12 +1533,13 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   auto GZ = static_cast<const uint16_t*>(gz);
   hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
                      table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz, qt,
-                     dot, plan);
+                     dot, gmax, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
                      static_cast<const uint16_t*>(qt), K, V, static_cast<const uint16_t*>(dot), lse,
-                     static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv, plan);
+                     static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv,
+                     static_cast<const uint32_t*>(gmax), plan);
   return hipGetLastError();
 }
 
@@ -1500,9 +1548,9 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
                                 float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
                                 const void* bu, const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
-                                uint16_t* qt, uint16_t* dot, hipStream_t stream) {
+                                uint16_t* qt, uint16_t* dot, uint32_t* gmax, hipStream_t stream) {
 #define WATTN_BWD_ARGS \
-  plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, stream
+  plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, gmax, stream
   const int sel = (bias ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
     case 0: return launch_bwd_inst<NW, false, false, false, GATE>(WATTN_BWD_ARGS);
@@ -1533,13 +1581,17 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
     const int64_t cnt = (int64_t)plan.H * plan.M * plan.M * 16;
     if ((e = fill(dbu, cnt)) != hipSuccess || (e = fill(dbv, cnt)) != hipSuccess) return e;
   }
-  // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32]
+  // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32],
+  // then 16 bytes holding the largest output-gradient entry (as float bits, zeroed first)
   const int64_t th = (int64_t)plan.B * plan.Hg * plan.Wg * plan.H;
   float* delta = scratch;
   uint16_t* qt = reinterpret_cast<uint16_t*>(scratch + ((th + 3) & ~int64_t(3)));
   uint16_t* dot = qt + th * D;
+  float* gmax_slot = reinterpret_cast<float*>(dot + th * D);
+  if ((e = fill(gmax_slot, 4)) != hipSuccess) return e;
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(gmax_slot);
 #define WATTN_BWD_ARGS plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
-                       dbu, dbv, gz, dz, qt, dot, stream
+                       dbu, dbv, gz, dz, qt, dot, gmax, stream
   const bool gate = gz != nullptr;
   switch (plan.nw) {
     case 2: return gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS);
