@@ -69,7 +69,8 @@ typedef enum {
   WATTN_ERR_ALIAS = 7,    /* out overlaps an input buffer */
   WATTN_ERR_HIP = 8,      /* HIP runtime error (no device, launch failure, ...) */
   WATTN_ERR_POINTER = 9,  /* a buffer is not device-accessible memory */
-  WATTN_ERR_VALUE = 10    /* a scalar parameter out of range (eps of the gated local path) */
+  WATTN_ERR_VALUE = 10,   /* a scalar parameter out of range (eps of the gated local path) */
+  WATTN_ERR_SCRATCH = 11  /* the call needs more scratch than wattn_backward_noalloc holds */
 } wattn_status_t;
 
 #define WATTN_MAX_M 128
@@ -187,6 +188,29 @@ int wattn_backward(const void* q, const void* k, const void* v, const void* out,
                    int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
                    const float* theta, const void* bias_u, const void* bias_v, int r,
                    float* dbias_u, float* dbias_v, int dtype, void* stream);
+
+/*
+ * wattn_backward_noalloc -- wattn_backward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without `scratch`, the same kernels, outputs and numerics.
+ *
+ * The scratch comes from a file-scope device array of the library (64 MiB on every GPU the
+ * library runs on, held until the process ends), so the call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.  Calls that need more than that, i.e. more than
+ * 508400 query rows B * Hgrid * Wgrid * H (wattn_backward_scratch_bytes > 64 MiB), return
+ * WATTN_ERR_SCRATCH before any HIP call.  The first call on a device looks the array's address
+ * up on that device (the device of `stream`; the current one for the null stream).
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents behind; what must
+ * start at zero is cleared by the call itself on `stream`.  Calls that overlap on one GPU (on
+ * different streams, or from several host threads without ordering) race on the array and
+ * give undefined results: order them on one stream.
+ */
+int wattn_backward_noalloc(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                           const float* lse, float* dq, float* dk, float* dv, float* dtheta,
+                           int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                           const float* theta, const void* bias_u, const void* bias_v, int r,
+                           float* dbias_u, float* dbias_v, int dtype, void* stream);
 
 /*
  * Convolutional gate on the attention output (Rank-Factorized Implicit Neural Bias: Scaling

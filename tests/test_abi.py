@@ -35,6 +35,7 @@ def test_exports_every_declared_symbol():
     text = open(HEADER).read()
     names = set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(wattn_\w+)\s*\(", text, flags=re.M))
     assert names == {"wattn_forward", "wattn_forward_lse", "wattn_backward", "wattn_backward_scratch_bytes",
+                     "wattn_backward_noalloc",
                      "wattn_select_blocks",
                      "wattn_local_residual", "wattn_gated_local", "wattn_forward_gated", "wattn_backward_gated",
                      "wattn_cla_logits", "wattn_linear", "wattn_layernorm", "wattn_patch_merge_norm",
@@ -155,6 +156,32 @@ def _call_bwd(**kw):
 )
 def test_backward_rejects_invalid_arguments(kw, status):
     assert _call_bwd(**kw) == status
+
+
+def _call_bwd_noalloc(B=1, H=2, Hg=16, Wg=16, M=8, s=0, d=32):
+    vp = ctypes.c_void_p
+    return _lib().wattn_backward_noalloc(vp(P1), vp(P2), vp(P3), vp(P4), vp(P4 + 0x800000), vp(P4 + 0x1000000),
+                                         vp(P4 + 0x2000000), vp(P4 + 0x3000000), vp(P4 + 0x4000000), vp(None),
+                                         B, H, Hg, Wg, M, s, d, vp(None), vp(None), vp(None), 0, vp(None),
+                                         vp(None), 0, vp(None))
+
+
+def test_backward_noalloc_rejects_before_any_hip_call():
+    """The no-allocation backward pass refuses a problem whose scratch would exceed the 64 MiB it
+    holds (WATTN_ERR_SCRATCH = 11), and the usual argument errors, on the host."""
+    lib = _lib()
+    rows_max = ((64 << 20) - 16) // 132
+    assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max, 32) <= 64 << 20
+    assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max + 1, 32) > 64 << 20
+    # 16 x 128 x 128 x 3 heads = 786432 query rows: too many
+    assert _call_bwd_noalloc(B=16, H=3, Hg=128, Wg=128, M=32, s=16) == 11
+    assert _call_bwd_noalloc(B=1, H=2, Hg=16, Wg=16, M=8, s=8) == 3   # shift outside [0, M)
+    assert _call_bwd_noalloc(B=1, H=2, Hg=16, Wg=16, M=8, d=64) == 4  # head dimension
+    vp = ctypes.c_void_p
+    assert lib.wattn_backward_noalloc(vp(P1), vp(None), vp(P3), vp(P4), vp(P4), vp(P4), vp(P4), vp(P4), vp(P4),
+                                      vp(None), 1, 2, 16, 16, 8, 0, 32, vp(None), vp(None), vp(None), 0, vp(None),
+                                      vp(None), 0, vp(None)) == 1
+    assert wattn.status_string(11).startswith("problem needs more scratch")
 
 
 def test_backward_scratch_bytes():

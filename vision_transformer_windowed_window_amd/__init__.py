@@ -65,6 +65,7 @@ STATUS = {
     8: "WATTN_ERR_HIP",
     9: "WATTN_ERR_POINTER",
     10: "WATTN_ERR_VALUE",
+    11: "WATTN_ERR_SCRATCH",
 }
 
 ACT_NONE = 0
@@ -112,6 +113,8 @@ def load_library() -> ctypes.CDLL:
     lib.wattn_forward_lse.restype = ci
     lib.wattn_backward.argtypes = [vp] * 11 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
     lib.wattn_backward.restype = ci
+    lib.wattn_backward_noalloc.argtypes = [vp] * 10 + [ci] * 7 + [vp, vp, vp, ci, vp, vp, ci, vp]
+    lib.wattn_backward_noalloc.restype = ci
     i64 = ctypes.c_int64
     lib.wattn_backward_scratch_bytes.argtypes = [ci] * 5
     lib.wattn_backward_scratch_bytes.restype = i64

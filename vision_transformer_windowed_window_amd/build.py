@@ -50,6 +50,7 @@ def build(verbose: bool = False) -> str:
         gobj = os.path.join(tmp, "wattn_gated.o")
         cobj = os.path.join(tmp, "wattn_cla.o")
         mobj = os.path.join(tmp, "wattn_model.o")
+        nobj = os.path.join(tmp, "wattn_noalloc.o")
         aobj = os.path.join(tmp, "wattn_api.o")
         _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
               os.path.join(CSRC, "wattn_kernels.hip"), "-o", kobj], verbose)
@@ -59,11 +60,13 @@ def build(verbose: bool = False) -> str:
               os.path.join(CSRC, "wattn_cla.hip"), "-o", cobj], verbose)
         _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
               os.path.join(CSRC, "wattn_model.hip"), "-o", mobj], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
+              os.path.join(CSRC, "wattn_noalloc.hip"), "-o", nobj], verbose)
         rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
         _run([hipcc, *COMMON, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-c",
               os.path.join(CSRC, "wattn_api.cpp"), "-o", aobj], verbose)
         out_tmp = os.path.join(tmp, "libwattn.so")
-        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, cobj, mobj, aobj, "-o", out_tmp], verbose)
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, gobj, cobj, mobj, nobj, aobj, "-o", out_tmp], verbose)
         shutil.move(out_tmp, LIB + ".tmp")
         os.replace(LIB + ".tmp", LIB)
         exe_tmp = os.path.join(tmp, "pipe_rates")

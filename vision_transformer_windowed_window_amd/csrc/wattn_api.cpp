@@ -11,6 +11,7 @@
 
 #include "wattn.h"
 #include "wattn_aux_plan.h"
+#include "wattn_noalloc.h"
 #include "wattn_plan.h"
 
 hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out_f32, const void* q,
@@ -272,14 +273,17 @@ namespace {
 // to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32] each.
 int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 32 * rows) * 4 + 16; }
 
-// Backward pass shared by wattn_backward and wattn_backward_gated (gz and dz both NULL or both set).
+// Backward pass shared by wattn_backward, wattn_backward_gated (gz and dz both NULL or both
+// set) and wattn_backward_noalloc (library_scratch: scratch is NULL on entry and the
+// library-held array of wattn_noalloc.hip is used instead).
 int backward_impl(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
                   const void* gz, float* scratch, float* dq, float* dk, float* dv, float* dtheta, float* dz, int B,
                   int H, int Hgrid, int Wgrid, int M, int shift, int d, const float* theta, const void* bias_u,
-                  const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype, void* stream) {
+                  const void* bias_v, int r, float* dbias_u, float* dbias_v, int dtype, void* stream,
+                  bool library_scratch = false) {
   // ---- argument checks (no HIP call before this block ends)
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
-      scratch == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+      (scratch == nullptr && !library_scratch) || dq == nullptr || dk == nullptr || dv == nullptr)
     return WATTN_ERR_NULL;
   if ((theta == nullptr) != (dtheta == nullptr)) return WATTN_ERR_NULL;
   if ((gz == nullptr) != (dz == nullptr)) return WATTN_ERR_NULL;
@@ -300,6 +304,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   const size_t fbytes = (size_t)elems * 4;                                    // dq, dk, dv
   const size_t rbytes = (size_t)(elems / d) * 4;                              // lse
   const size_t sbytes = (size_t)backward_scratch_bytes(elems / d);            // scratch
+  if (library_scratch && sbytes > (size_t)WATTN_NOALLOC_SCRATCH_BYTES) return WATTN_ERR_SCRATCH;
   const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
   const size_t b_bytes = (size_t)H * M * M * r * 2;   // bias factors (bf16)
   const size_t db_bytes = (size_t)H * M * M * r * 4;  // their gradients (float32)
@@ -333,8 +338,16 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   const size_t sizes[18] = {tbytes, tbytes, tbytes, gbytes, gbytes, rbytes, sbytes, fbytes, fbytes,
                             fbytes, th_bytes, th_bytes, b_bytes, b_bytes, db_bytes, db_bytes, tbytes, fbytes};
   for (int i = 0; i < 18; ++i) {
-    st = pointer_ok(ptrs[i], sizes[i]);
+    st = pointer_ok(ptrs[i], sizes[i]);  // (a NULL library scratch is skipped)
     if (st != WATTN_OK) return st;
+  }
+  if (library_scratch) {
+    void* p = nullptr;
+    if (wattn_noalloc_scratch(static_cast<hipStream_t>(stream), &p) != hipSuccess) {
+      (void)hipGetLastError();
+      return WATTN_ERR_HIP;
+    }
+    scratch = static_cast<float*>(p);
   }
   const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
                                         lse, scratch, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v, gz,
@@ -356,6 +369,15 @@ extern "C" int wattn_backward(const void* q, const void* k, const void* v, const
                               int dtype, void* stream) {
   return backward_impl(q, k, v, out, dout, lse, nullptr, scratch, dq, dk, dv, dtheta, nullptr, B, H, Hgrid, Wgrid, M,
                        shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream);
+}
+
+extern "C" int wattn_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                      const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                                      float* dtheta, int B, int H, int Hgrid, int Wgrid, int M, int shift, int d,
+                                      const float* theta, const void* bias_u, const void* bias_v, int r,
+                                      float* dbias_u, float* dbias_v, int dtype, void* stream) {
+  return backward_impl(q, k, v, out, dout, lse, nullptr, nullptr, dq, dk, dv, dtheta, nullptr, B, H, Hgrid, Wgrid,
+                       M, shift, d, theta, bias_u, bias_v, r, dbias_u, dbias_v, dtype, stream, true);
 }
 
 extern "C" int wattn_backward_gated(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -732,6 +754,7 @@ extern "C" const char* wattn_status_string(int status) {
     case WATTN_ERR_HIP: return "HIP runtime error (no device or launch failure)";
     case WATTN_ERR_POINTER: return "buffer is not device-accessible memory of the required size";
     case WATTN_ERR_VALUE: return "scalar parameter out of range (eps must be finite and >= 0)";
+    case WATTN_ERR_SCRATCH: return "problem needs more scratch than the library holds (wattn_backward_noalloc)";
     default: return "unknown status";
   }
 }

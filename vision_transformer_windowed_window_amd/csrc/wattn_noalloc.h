@@ -1,0 +1,11 @@
+// wattn_noalloc.h -- the library-held backward scratch (wattn_noalloc.hip), shared with the
+// host API.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+// Size of the library-held scratch on each device: 64 MiB, room for the backward pass of up to
+// (64 MiB - 16) / 132 = 508400 query rows (B * Hgrid * Wgrid * H).
+#define WATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+hipError_t wattn_noalloc_scratch(hipStream_t stream, void** out);
