@@ -44,11 +44,13 @@
 extern "C" {
 #endif
 
-#define WATTN_ABI_VERSION 4
+#define WATTN_ABI_VERSION 5
 
-/* Element types.  The bf16 modes run QK^T and PV on bf16 matrix cores with fp32 RoPE,
- * fp32 softmax and fp32 accumulation; they differ only in the type of `out`.  A bf16
- * `out` adds its own rounding (up to 2^-9 relative) on top of the kernel's error. */
+/* Element types.  The bf16 modes take bf16 q, k, v and run both products on the matrix
+ * cores with fp32 RoPE, fp32 softmax and fp32 accumulation: QK^T on fp16 operands (the
+ * rotated q and k rounded once to fp16, see wattn_forward) and PV on bf16 operands.  They
+ * differ only in the type of `out`.  A bf16 `out` adds its own rounding (up to 2^-9
+ * relative) on top of the kernel's error. */
 typedef enum {
   WATTN_BF16 = 0,          /* q, k, v, bias_u, bias_v and out in bfloat16 */
   WATTN_FP32 = 1,          /* everything in float32 (plain fp32 arithmetic, no matrix cores) */
@@ -311,7 +313,10 @@ int wattn_select_blocks(const float* gate, int nblocks, float tau, int* list, in
  *           (WATTN_BF16_OUT_FP32); read and written.  Must not overlap q, k, v, list or count.
  * list, count : the block list and its length on the device (as written by
  *           wattn_select_blocks, capacity B * (Hgrid/w) * (Wgrid/w)).  The count is clamped to
- *           [0, number of blocks] and list entries outside the grid are skipped.
+ *           [0, number of blocks] and list entries outside the grid are skipped.  The entries
+ *           must be distinct (wattn_select_blocks writes them ascending): each listed block is
+ *           updated in place by its own workgroups with no atomics, so a block listed twice is
+ *           updated by two racing sets of workgroups and its result is undefined.
  * w       : block side, one of 4, 8, 12, 16; Hgrid and Wgrid multiples of w.
  * d       : 32.   eps : finite, >= 0 (WATTN_ERR_VALUE otherwise).
  * One workgroup per (block, head) is launched for every block of the grid; those past the

@@ -108,18 +108,15 @@ def test_bf16_output(case):
 
 
 def test_large_query_scale():
-    """Peaked softmax: q scaled by 2.5 beyond the N(0,1) workloads.  The rotated q and k
-    are rounded to bf16 for the matrix cores, so the logit error grows in proportion to
-    the logits; the bounds are the benchmark spec's bounds scaled by the same factor."""
-    from parity_util import errors
-
+    """Peaked softmax: q scaled by 2.5 beyond the N(0,1) workloads, the case that drives the
+    lazy rescale hardest.  The rotated q and k are rounded to fp16 (11-bit significand) for
+    the matrix cores, so the logit error grows with the logits; at this scale it stays within
+    the benchmark spec's bounds."""
     note("start large q scale")
     f = 2.5
     inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=5, qscale=f)
     got = run_gpu(inp, "bf16", 16, 8)
-    max_abs, rel = errors(got, oracle_full(inp, 16, 8))
-    note(f"q_x{f}: max|err| = {max_abs:.3e}, rel-L2 = {rel:.3e}")
-    assert max_abs <= f * 1e-2 and rel <= f * 5e-3
+    check(got, oracle_full(inp, 16, 8), "bf16", f"q_x{f}")
 
 
 # ------------------------------------------------------------ workloads at full size

@@ -83,14 +83,7 @@ AxisSplit split_axis(int G, int M, int s) {
 // Returns false if the task count would not fit the launch limits.
 // Waves per workgroup of the bf16 path: wide workgroups amortise each staged K/V tile over
 // more queries; narrow ones keep waves busy when windows (and their wrap regions) are small.
-int waves_for_window(int M) {
-#ifdef WATTN_FORCE_NW
-  (void)M;
-  return WATTN_FORCE_NW;
-#else
-  return M >= 24 ? 8 : (M >= 12 ? 4 : 2);
-#endif
-}
+int waves_for_window(int M) { return M >= 24 ? 8 : (M >= 12 ? 4 : 2); }
 
 bool build_plan(int B, int H, int Hg, int Wg, int M, int s, WattnPlan& P, int nw) {
   P = WattnPlan{};

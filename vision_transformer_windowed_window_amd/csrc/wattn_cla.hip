@@ -212,7 +212,10 @@ __global__ __launch_bounds__(2 * C) void wattn_cla_logits_kernel(const uint16_t*
     // Two stores that the hardware drops (a resource of zero bytes) follow each prefetch, so
     // that the row loop is entered with the same memory operations in flight as on later
     // iterations (a row's loads, then its two z stores): the compiler's count of younger
-    // operations at each wait is then exact on every path.
+    // operations at each wait is then exact on every path.  They only make the compiler's
+    // waits tight, not correct: every load here goes to registers, which the compiler tracks,
+    // so an added or removed memory operation can lengthen a wait but never shorten it below
+    // what the data needs.
     fetch_row(y0 + 2, preA, okA);
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rnone, 0, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rnone, 64, 0, 0);

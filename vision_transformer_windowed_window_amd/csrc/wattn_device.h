@@ -36,6 +36,11 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// The MFMA wrappers below are all the 16x16x32 shape.  Products are chained through srcC (an
+// accumulator fed back as the next product's srcC); such chains must keep one shape: the
+// compiler inserts no wait states between MFMAs of different shapes whose srcC is exactly
+// the previous destination, which the hardware only forwards between identical instructions.
+
 // score product: fp16 operands (k = 32 channels in one instruction), fp32 accumulate
 __device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,

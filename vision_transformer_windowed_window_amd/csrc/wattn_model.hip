@@ -59,6 +59,12 @@ __device__ __forceinline__ float gelu_erf(float x) {
 constexpr int LT = 128;     // tile rows (tokens) and columns (outputs)
 constexpr int LSTAGE = 3;   // k slices in flight
 constexpr int LSL = LT * 32;  // bf16 elements of one operand's slice
+// Direct-to-LDS loads per k slice and wave: LT / 64 = 2 instructions (64 rows of 16-byte
+// chunks each) for each of the two operands.  The main loop's hand-written wait leaves exactly
+// one slice's loads in flight, so it counts these and nothing else: the loop must issue no
+// other vector-memory instruction (the epilogue's loads and stores come after it).
+constexpr int LIN_LOAD_HALVES = LT / 64;
+constexpr int LIN_SLICE_LOADS = 2 * LIN_LOAD_HALVES;
 
 __device__ __forceinline__ int lswz(int row) { return (row >> 2) & 3; }
 
@@ -83,17 +89,17 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
   // loads: instruction h of wave w fills LDS chunks 256 h + 64 w + lane of a slice, i.e. row
   // 64 h + 16 w + lane / 4, slot lane % 4, from the chunk that the swizzle puts there; rows
   // past M (N) reload the last row, whose products are never stored
-  const uint16_t* xs[2];
-  const uint16_t* ws[2];
+  const uint16_t* xs[LIN_LOAD_HALVES];
+  const uint16_t* ws[LIN_LOAD_HALVES];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < LIN_LOAD_HALVES; ++h) {
     const int row = 64 * h + 16 * wave + (lane >> 2), chunk = (lane & 3) ^ lswz(row);
     xs[h] = x + (int64_t)min(m0 + row, P.M - 1) * P.K + 8 * chunk;
     ws[h] = W + (int64_t)min(n0 + row, P.N - 1) * P.K + 8 * chunk;
   }
-  auto issue = [&](int ks, int stage) {
+  auto issue = [&](int ks, int stage) {  // LIN_SLICE_LOADS vector-memory instructions, no more
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < LIN_LOAD_HALVES; ++h) {
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(xs[h] + 32 * ks),
                                        (__attribute__((address_space(3))) void*)(&sS[stage][0][(256 * h + 64 * wave) * 8]),
                                        16, 0, 0);
@@ -121,7 +127,7 @@ __global__ __launch_bounds__(256) void wattn_linear_kernel(const uint16_t* __res
     // this wave's loads of slice ks are done when at most slice ks + 1's four loads are still in
     // flight; the barrier then covers every wave's loads (and, on the first step, sBias)
     if (ks + 1 < nk)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LIN_SLICE_LOADS) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // slice ks + 2 goes into the stage slice ks - 1 used, which every wave finished reading
