@@ -94,7 +94,10 @@ typedef enum {
  * bias_u,
  * bias_v       : device pointers, [H][M*M][r] of q's element type, indexed by the
  *                window-local token index n = r*M + c; both NULL when r == 0.
- * r            : bias rank, 0 or 16.
+ * r            : bias rank, 0, 16 or 32 (d + r a multiple of 16 that one or two k = 32
+ *                matrix-core products carry: a rank-16 bias is zero-padded to the second
+ *                product, which on this GPU costs the same as a k = 16 product, and a
+ *                rank-32 bias fills it).
  * dtype        : a wattn_dtype_t value.
  * stream       : hipStream_t to launch on; NULL = the default stream.
  *
@@ -169,7 +172,8 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *   dbias_u, dbias_v : float32 [H][M*M][r], the gradients of the bias factors (summed over
  *             every window and image, which share them; zeroed, then accumulated with atomic
  *             adds); required iff r == 16.
- * bias_u, bias_v, r : the forward pass's bias factors (bfloat16 [H][M*M][r]) and rank: NULL,
+ * bias_u, bias_v, r : the forward pass's bias factors (bfloat16 [H][M*M][r]) and rank (the
+ *             backward pass takes rank 16 only; the forward pass also takes 32): NULL,
  *             NULL, 0 or both set with r == 16 (WATTN_ERR_RANK otherwise, also when the
  *             dbias pointers do not match).
  * Sizes, shift and d follow wattn_forward.  No output may overlap an input or another

@@ -65,11 +65,11 @@ def test_status_enum_matches_header_and_strings():
         (dict(s=-1), 3), (dict(s=8), 3), (dict(s=9), 3),
         (dict(d=64), 4), (dict(d=16), 4), (dict(d=33), 4),
         (dict(r=8, bu=BU, bv=BV), 5), (dict(r=16), 5), (dict(r=16, bu=BU), 5), (dict(r=0, bu=BU, bv=BV), 5),
-        (dict(r=-1), 5),
+        (dict(r=-1), 5), (dict(r=48, bu=BU, bv=BV), 5), (dict(r=24, bu=BU, bv=BV), 5), (dict(r=32, bu=BU), 5),
         (dict(dtype=3), 6), (dict(dtype=-1), 6),
         (dict(dtype=2, out=P1 - 16 * 16 * 2 * 32 * 4 + 8), 7),
         (dict(out=P1), 7), (dict(out=P1 + 100), 7), (dict(out=P2 - 10), 7), (dict(out=TH, theta=TH), 7),
-        (dict(r=16, bu=BU, bv=BV, out=BV + 64), 7),
+        (dict(r=16, bu=BU, bv=BV, out=BV + 64), 7), (dict(r=32, bu=BU, bv=BV, out=BV + 64), 7),
     ],
 )
 def test_invalid_arguments_are_rejected_on_the_host(kw, status):
@@ -147,6 +147,7 @@ def _call_bwd(**kw):
         (dict(B=0), 2), (dict(Hg=20), 2), (dict(s=-1), 3), (dict(d=64), 4),
         (dict(dtype=1), 6), (dict(dtype=3), 6),
         (dict(r=16, bu=BU, bv=BV), 5), (dict(dbu=0xE00000), 5), (dict(r=8, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5),
+        (dict(r=32, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5),  # the backward pass takes rank 16 only
         (dict(r=16, bu=BU, bv=BV, dbu=0xE00000), 5), (dict(r=16, bu=BU, dbu=0xE00000, dbv=0xF00000), 5),
         (dict(r=16, bu=BU, bv=BV, dbu=G1, dbv=0xF00000), 7), (dict(r=16, bu=BU, bv=BV, dbu=0xE00000, dbv=BV), 7),
         (dict(dq=P1), 7), (dict(dk=G1 + 64), 7), (dict(dv=LS), 7), (dict(delta=G3 + 4), 7),

@@ -44,6 +44,12 @@ SMALL = [
     ("bf16_m1", 1, 3, 5, 2, 1, 0, "bf16", True, 0),
     ("bf16_m40_s13_bias", 1, 40, 80, 1, 40, 13, "bf16", True, 16),
     ("bf16_norope_nobias", 1, 32, 32, 2, 16, 8, "bf16", False, 0),
+    # rank-32 bias: one full k = 32 product of bias channels
+    ("fp32_m8_s3_bias32", 1, 16, 24, 2, 8, 3, "fp32", True, 32),
+    ("bf16_m8_s3_rope_bias32", 2, 24, 32, 2, 8, 3, "bf16", True, 32),
+    ("bf16_m16_s5_rope_bias32_ragged", 1, 48, 32, 2, 16, 5, "bf16", True, 32),
+    ("bf16_m32_s16_rope_bias32", 1, 64, 64, 2, 32, 16, "bf16", True, 32),
+    ("bf16_m48_bias32_norope", 1, 48, 96, 1, 48, 0, "bf16", False, 32),
 ]
 
 

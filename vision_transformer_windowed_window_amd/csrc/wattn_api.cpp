@@ -157,7 +157,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
   if (st != WATTN_OK) return st;
   if (d != 32) return WATTN_ERR_HEAD_DIM;
   if (dtype != WATTN_BF16 && dtype != WATTN_FP32 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
-  if (r != 0 && r != 16) return WATTN_ERR_RANK;
+  if (r != 0 && r != 16 && r != 32) return WATTN_ERR_RANK;
   if (r == 0 && (bias_u != nullptr || bias_v != nullptr)) return WATTN_ERR_RANK;
   if (r > 0 && (bias_u == nullptr || bias_v == nullptr)) return WATTN_ERR_RANK;
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
@@ -227,7 +227,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype != WATTN_FP32)
-    e = wattn_launch_bf16(plan, r > 0 ? 3 : 2, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, theta,
+    e = wattn_launch_bf16(plan, 2 + r / 16, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, theta,
                           bias_u, bias_v, lse, gz, s);
   else
     e = wattn_launch_f32(fplan, r, q, k, v, out, theta, bias_u, bias_v, s);

@@ -181,8 +181,10 @@ __device__ __forceinline__ void split_idx(const TaskCtx& X, uint32_t i, int& qt,
 __host__ __device__ constexpr int table_stride(int NW) { return NW == 2 ? 18 : (NW == 4 ? 26 : 130); }
 
 // NW waves per workgroup (2, 4 or 8): 32 NW queries, key tiles of 16 NW keys.
+// NKS: 16-channel groups of the score product's contraction: 2 (d = 32, no bias), 3 (a rank-16
+// bias, zero-padded to a second k = 32 product) or 4 (a rank-32 bias, one full k = 32 product).
 template <int NW, int NKS, bool ROPE, bool OUTF32, bool GATE>
-__global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               void* __restrict__ out,
@@ -192,13 +194,15 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
                                                               float* __restrict__ lse,
                                                               const uint16_t* __restrict__ gz,
                                                               const WattnPlan P) {
-  constexpr bool BIAS = (NKS == 3);
+  constexpr bool BIAS = (NKS >= 3);
+  constexpr int BR = (NKS - 2) * 16;          // bias channels (0, 16 or 32)
+  constexpr int BCH = BIAS ? BR / 8 : 1;      // 16-byte chunks of a key's bias-factor row
   constexpr int NTHR = 64 * NW;  // threads
   constexpr int QT = 32 * NW;    // queries (two 16-query blocks per wave)
   constexpr int KT = 16 * NW;    // keys per LDS tile: each thread stages one 16-byte chunk of K and of V
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
-  __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];
+  __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * BR : 8];
   constexpr int TSTR = table_stride(NW);
   extern __shared__ float2 sTab[];  // 16 rows of TSTR cos/sin entries of the head, pair-major (dynamic size)
 
@@ -237,9 +241,9 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
         const int off = Y.regbase + li * rowstride + lj * colstride;
         qraw[a] = *reinterpret_cast<const u32x4*>(q + Y.img + off + 8 * g);
         qpos[a] = (g < 2) ? (Y.t.r0 + li) : (Y.t.c0 + lj);  // channels 0..15 carry y, 16..31 x
-        if (BIAS && g < 2) {
+        if (BIAS && 8 * g < BR) {
           const int nl = (Y.t.r0 + li) * M + (Y.t.c0 + lj);
-          braw[a] = *reinterpret_cast<const u32x4*>(bu + ((int64_t)Y.t.h * M * M + nl) * 16 + 8 * g);
+          braw[a] = *reinterpret_cast<const u32x4*>(bu + ((int64_t)Y.t.h * M * M + nl) * BR + 8 * g);
         }
       }
     }
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
   //      past the region end load the region's last key (finite data; their scores are
   //      masked, so their probabilities are exactly 0).
   const int lk = tid >> 2, lch = tid & 3;
-  const int bk = (tid % (2 * KT)) >> 1, bch = tid & 1;
-  const bool bthread = BIAS && tid < 2 * KT;
+  const int bk = (tid % (BCH * KT)) / BCH, bch = tid % BCH;
+  const bool bthread = BIAS && tid < BCH * KT;
   int ci, cj, bi, bj, koff, klast;
   u32x4 pk, pv, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
     if (BIAS && bthread) {
       const bool bvalid = tile * KT + bk < Y.n;
       const int key = bvalid ? (Y.t.r0 + bi) * M + (Y.t.c0 + bj) : 0;
-      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)Y.t.h * M * M + key) * 16 + 8 * bch);
+      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)Y.t.h * M * M + key) * BR + 8 * bch);
     }
   };
   auto store = [&](int buf) {
@@ -363,7 +367,8 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
       u32x4 br;
 #pragma unroll
       for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
-      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = br;
+      const int sw = BR == 16 ? bswz(bk) : kswz(bk);  // rank 32: the row layout of K
+      *reinterpret_cast<u32x4*>(&sKb[buf][bk * BR + 8 * (bch ^ sw)]) = br;
     }
   };
 
@@ -412,7 +417,8 @@ __global__ __launch_bounds__(64 * NW, NKS == 3 ? 2 : 4) void wattn_fwd_bf16_kern
     for (int b = 0; b < 2; ++b) {
       const int key = kb + krow + 4 * b;
       F.Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
-      if (BIAS) F.Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+      if (BIAS && BR == 16) F.Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+      if (BIAS && BR == 32) F.Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 32 + 8 * (g ^ kswz(key))]);
     }
   };
   // value operand A (V^T): dims 16 db + c, keys kb + 8g .. 8g+7
@@ -1467,7 +1473,7 @@ static hipError_t launch_bf16_nw(const WattnPlan& plan, int nks, bool rope, bool
                                  const void* k, const void* v, void* out, const float* theta, const void* bu,
                                  const void* bv, float* lse, const void* gz, hipStream_t stream) {
 #define WATTN_FWD_ARGS plan, q, k, v, out, theta, bu, bv, lse, gz, stream
-  const int sel = (nks == 3 ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+  const int sel = (nks - 2) * 4 + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
     case 0: return launch_bf16_inst<NW, 2, false, false, GATE>(WATTN_FWD_ARGS);
     case 1: return launch_bf16_inst<NW, 2, false, true, GATE>(WATTN_FWD_ARGS);
@@ -1476,7 +1482,12 @@ static hipError_t launch_bf16_nw(const WattnPlan& plan, int nks, bool rope, bool
     case 4: return launch_bf16_inst<NW, 3, false, false, GATE>(WATTN_FWD_ARGS);
     case 5: return launch_bf16_inst<NW, 3, false, true, GATE>(WATTN_FWD_ARGS);
     case 6: return launch_bf16_inst<NW, 3, true, false, GATE>(WATTN_FWD_ARGS);
-    default: return launch_bf16_inst<NW, 3, true, true, GATE>(WATTN_FWD_ARGS);
+    case 7: return launch_bf16_inst<NW, 3, true, true, GATE>(WATTN_FWD_ARGS);
+    case 8: return launch_bf16_inst<NW, 4, false, false, GATE>(WATTN_FWD_ARGS);
+    case 9: return launch_bf16_inst<NW, 4, false, true, GATE>(WATTN_FWD_ARGS);
+    case 10: return launch_bf16_inst<NW, 4, true, false, GATE>(WATTN_FWD_ARGS);
+    case 11: return launch_bf16_inst<NW, 4, true, true, GATE>(WATTN_FWD_ARGS);
+    default: return hipErrorInvalidValue;
   }
 #undef WATTN_FWD_ARGS
 }
@@ -1511,6 +1522,8 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
   auto W = static_cast<const float*>(bv);
   if (r == 16)
     hipLaunchKernelGGL((wattn_fwd_f32_kernel<16>), grid, block, 0, stream, Q, K, V, O, theta, U, W, plan);
+  else if (r == 32)
+    hipLaunchKernelGGL((wattn_fwd_f32_kernel<32>), grid, block, 0, stream, Q, K, V, O, theta, U, W, plan);
   else
     hipLaunchKernelGGL((wattn_fwd_f32_kernel<0>), grid, block, 0, stream, Q, K, V, O, theta, U, W, plan);
   return hipGetLastError();
