@@ -196,7 +196,6 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
                                                               const WattnPlan P) {
   constexpr bool BIAS = (NKS >= 3);
   constexpr int BR = (NKS - 2) * 16;          // bias channels (0, 16 or 32)
-  constexpr int BCH = BIAS ? BR / 8 : 1;      // 16-byte chunks of a key's bias-factor row
   constexpr int NTHR = 64 * NW;  // threads
   constexpr int QT = 32 * NW;    // queries (two 16-query blocks per wave)
   constexpr int KT = 16 * NW;    // keys per LDS tile: each thread stages one 16-byte chunk of K and of V
@@ -297,20 +296,17 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
   };
 
   // ---- loader: thread t owns the 16-byte chunk lch = t % 4 of key lk = t / 4 of a tile in
-  //      both K and V (same element offset); threads 0 .. 2 KT - 1 also own the 16-byte
-  //      half bch = t % 2 of the bias-factor row of key bk = t / 2.  The key index advances by
-  //      KT per tile; region coordinates and the element offset are carried along.  Keys
-  //      past the region end load the region's last key (finite data; their scores are
-  //      masked, so their probabilities are exactly 0).
+  //      both K and V (same element offset) and the quarter lch of the key's bias-factor row
+  //      (8 bytes at rank 16, 16 bytes at rank 32).  The key index advances by KT per tile;
+  //      region coordinates and the element offset are carried along.  Keys past the region
+  //      end load the region's last key (bias: the window's first position) -- finite data
+  //      whose scores are masked, so their probabilities are exactly 0.
   const int lk = tid >> 2, lch = tid & 3;
-  const int bk = (tid % (BCH * KT)) / BCH, bch = tid % BCH;
-  const bool bthread = BIAS && tid < BCH * KT;
-  int ci, cj, bi, bj, koff, klast;
+  int ci, cj, koff, klast;
   u32x4 pk, pv, pb = {0u, 0u, 0u, 0u};
   int lpos = 0;
   auto loader_init = [&](const TaskCtx& Y) {
     split_idx(Y, (uint32_t)lk, ci, cj);
-    split_idx(Y, (uint32_t)bk, bi, bj);
     koff = Y.regbase + ci * rowstride + cj * colstride + 8 * lch;
     int li, lj;
     split_idx(Y, (uint32_t)(Y.n - 1), li, lj);
@@ -325,14 +321,6 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
       ci += 1;
       koff += Y.carry_off;
     }
-    if (BIAS) {
-      bi += Y.step_i;
-      bj += Y.step_j;
-      if (bj >= Y.t.rw) {
-        bj -= Y.t.rw;
-        bi += 1;
-      }
-    }
   };
   auto fetch = [&](const TaskCtx& Y, int tile) {
     const bool valid = tile * KT + lk < Y.n;
@@ -341,10 +329,15 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
     pk = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(k + Y.img) + off);
     pv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(v + Y.img) + off);
     lpos = (lch < 2) ? (Y.t.r0 + ci) : (Y.t.c0 + cj);
-    if (BIAS && bthread) {
-      const bool bvalid = tile * KT + bk < Y.n;
-      const int key = bvalid ? (Y.t.r0 + bi) * M + (Y.t.c0 + bj) : 0;
-      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)Y.t.h * M * M + key) * BR + 8 * bch);
+    if (BIAS) {
+      const int key = valid ? (Y.t.r0 + ci) * M + (Y.t.c0 + cj) : 0;
+      const uint16_t* src = bv + ((int64_t)Y.t.h * M * M + key) * BR + (BR / 4) * lch;
+      if (BR == 16) {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(src);
+        pb = u32x4{h[0], h[1], 0u, 0u};
+      } else {
+        pb = *reinterpret_cast<const u32x4*>(src);
+      }
     }
   };
   auto store = [&](int buf) {
@@ -363,12 +356,15 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
     }
     *reinterpret_cast<u32x4*>(&sK[buf][lk * D + ((lch ^ kswz(lk)) * 8)]) = kr;
     *reinterpret_cast<u32x4*>(&sV[buf][lk * D + ((lch ^ vswz(lk)) * 8)]) = pv;
-    if (BIAS && bthread) {
+    if (BIAS && BR == 16) {  // 32-byte rows: quarter lch is half lch / 2 (swizzled), offset 4 (lch % 2)
+      const u32x2 br = {pack_f16(bf_lo(pb[0]), bf_hi(pb[0])), pack_f16(bf_lo(pb[1]), bf_hi(pb[1]))};
+      *reinterpret_cast<u32x2*>(&sKb[buf][lk * 16 + 8 * ((lch >> 1) ^ bswz(lk)) + 4 * (lch & 1)]) = br;
+    }
+    if (BIAS && BR == 32) {  // 64-byte rows: the row layout of K
       u32x4 br;
 #pragma unroll
       for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
-      const int sw = BR == 16 ? bswz(bk) : kswz(bk);  // rank 32: the row layout of K
-      *reinterpret_cast<u32x4*>(&sKb[buf][bk * BR + 8 * (bch ^ sw)]) = br;
+      *reinterpret_cast<u32x4*>(&sKb[buf][lk * 32 + 8 * (lch ^ kswz(lk))]) = br;
     }
   };
 
