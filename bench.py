@@ -53,6 +53,7 @@ KERNEL_SRCS = {
 }
 PIPE_RATES = os.path.join(ROOT, "vision_transformer_windowed_window_amd", "pipe_rates")
 MFMA_FLOPS = 16 * 16 * 32 * 2  # one v_mfma_f32_16x16x32_bf16 / _f16
+COPY_BYTES = 256 << 20      # the calibration copy of --pass copy
 
 
 def parse():
@@ -69,10 +70,11 @@ def parse():
                     help="time only the named workload (by default the forward pass also times the other "
                          "bf16 workloads for a few seconds each, reported under 'configs')")
     ap.add_argument("--sweep-steps", type=int, default=30, help="timed steps of each swept workload")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack", "model"],
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "gated", "stack", "model", "copy"],
                     help="fwd: wattn_forward (the headline); bwd: wattn_backward; gated: the gated local path; "
                          "stack: six layers with cyclic windows and the convolutional gate; "
-                         "model: the FlashSwin-T forward pass (--workload flashswin_t_p4_m32 or _p2_m32)")
+                         "model: the FlashSwin-T forward pass (--workload flashswin_t_p4_m32 or _p2_m32); "
+                         "copy: a plain 256 MiB device copy, the scale for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -633,6 +635,33 @@ def make_fwd_sets(cfg, args, torch, dev):
     return sets, params
 
 
+def main_copy(args):
+    """A plain device copy of known size, the scale for the HBM counters.
+
+    One step reads COPY_BYTES and writes COPY_BYTES (an element-wise negation of fp32 data, one
+    kernel).  Under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, the counters' reading for this
+    kernel divided by COPY_BYTES gives the factor that turns the same counters into bytes for
+    the attention kernels."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = COPY_BYTES // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+
+    def step(i):
+        torch.neg(src, out=dst)
+
+    wall_s, avg_kern_s, _ = time_steps(step, args.steps, args.warmup, torch)
+    print(json.dumps({
+        "metric": "device copy GB/s (read + write)", "value": 2 * COPY_BYTES / avg_kern_s / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "copy", "bytes_read_per_step": COPY_BYTES, "bytes_written_per_step": COPY_BYTES},
+        "kernel_ms_avg": avg_kern_s * 1e3}), flush=True)
+
+
 def time_steps(step, steps: int, warmup: int, torch, warmup_min_s: float = WARMUP_MIN_S):
     """Untimed warm-up, then `steps` back-to-back steps bracketed by events on the stream the
     kernels run on.  Returns (wall seconds per step, kernel seconds per step, peak extra bytes)."""
@@ -725,7 +754,7 @@ def sweep_record(cfg, args, wattn, torch, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the operator needs no collective: batch and window sharding are communication-free)",
               file=sys.stderr)
         sys.exit(2)
@@ -737,6 +766,9 @@ def main():
         return
     if args.which == "model":
         main_model(args)
+        return
+    if args.which == "copy":
+        main_copy(args)
         return
 
     import torch

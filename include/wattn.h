@@ -171,14 +171,13 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *             depend on the order of the additions); required iff theta is not NULL.
  *   dbias_u, dbias_v : float32 [H][M*M][r], the gradients of the bias factors (summed over
  *             every window and image, which share them; zeroed, then accumulated with atomic
- *             adds); required iff r == 16.
- * bias_u, bias_v, r : the forward pass's bias factors (bfloat16 [H][M*M][r]) and rank (the
- *             backward pass takes rank 16 only; the forward pass also takes 32): NULL,
- *             NULL, 0 or both set with r == 16 (WATTN_ERR_RANK otherwise, also when the
- *             dbias pointers do not match).
+ *             adds); required iff r > 0.
+ * bias_u, bias_v, r : the forward pass's bias factors (bfloat16 [H][M*M][r]) and rank, as in
+ *             wattn_forward: NULL, NULL, 0 or both set with r == 16 or r == 32
+ *             (WATTN_ERR_RANK otherwise, also when the dbias pointers do not match).
  * Sizes, shift and d follow wattn_forward.  No output may overlap an input or another
  * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: fill kernels for the accumulated
- * outputs and two attention kernels (one per query tile: delta, dq, the q part of dtheta,
+ * outputs (one launch) and two attention kernels (one per query tile: delta, dq, the q part of dtheta,
  * dbias_u; one per key tile: dk, dv, the k part of dtheta, dbias_v).
  *
  * Numerics: the scores are recomputed as in the forward pass (fp16 operands, P =

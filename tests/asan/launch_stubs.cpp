@@ -14,7 +14,7 @@ hipError_t wattn_launch_bf16(const WattnPlan&, int, bool, bool, const void*, con
 }
 hipError_t wattn_launch_bwd(const WattnPlan&, bool, bool, const void*, const void*, const void*, const void*,
                             const void*, const float*, float*, float*, float*, float*, float*, const float*,
-                            const void*, const void*, float*, float*, const void*, float*, hipStream_t) {
+                            const void*, const void*, int, float*, float*, const void*, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t wattn_launch_select(const float*, int, float, int*, int*, hipStream_t) { return hipErrorNoDevice; }

@@ -147,9 +147,10 @@ def _call_bwd(**kw):
         (dict(B=0), 2), (dict(Hg=20), 2), (dict(s=-1), 3), (dict(d=64), 4),
         (dict(dtype=1), 6), (dict(dtype=3), 6),
         (dict(r=16, bu=BU, bv=BV), 5), (dict(dbu=0xE00000), 5), (dict(r=8, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5),
-        (dict(r=32, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5),  # the backward pass takes rank 16 only
+        (dict(r=48, bu=BU, bv=BV, dbu=0xE00000, dbv=0xF00000), 5), (dict(r=32, bu=BU, bv=BV, dbu=0xE00000), 5),
         (dict(r=16, bu=BU, bv=BV, dbu=0xE00000), 5), (dict(r=16, bu=BU, dbu=0xE00000, dbv=0xF00000), 5),
         (dict(r=16, bu=BU, bv=BV, dbu=G1, dbv=0xF00000), 7), (dict(r=16, bu=BU, bv=BV, dbu=0xE00000, dbv=BV), 7),
+        (dict(r=32, bu=BU, bv=BV, dbu=0xE00000, dbv=BV), 7),
         (dict(dq=P1), 7), (dict(dk=G1 + 64), 7), (dict(dv=LS), 7), (dict(delta=G3 + 4), 7),
         (dict(theta=TH, dtheta=TH), 7), (dict(theta=TH, dtheta=G1), 7),
         (dict(dq=DL + 0x10000), 7), (dict(delta=DL + 8), 9),

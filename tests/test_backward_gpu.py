@@ -76,6 +76,11 @@ CASES = [
     ("m24_s0_bias_norope", 2, 48, 48, 1, 24, 0, False, True, 16),
     ("m40_s13_bias", 1, 40, 80, 1, 40, 13, True, True, 16),
     ("m128_s64", 1, 128, 128, 1, 128, 64, True, True),  # the largest window, four wrap regions
+    # rank-32 bias factors: a full k = 32 bias operand, two 16-channel blocks of dbias
+    ("m8_s3_rank32", 2, 16, 24, 2, 8, 3, True, True, 32),
+    ("m16_s8_rank32_bf16_out", 1, 32, 32, 2, 16, 8, True, False, 32),
+    ("m32_s16_rank32_norope", 1, 64, 64, 2, 32, 16, False, True, 32),
+    ("m40_s13_rank32", 1, 40, 80, 1, 40, 13, True, True, 32),
 ]
 
 
@@ -122,6 +127,7 @@ SCALE_CASES = [
     ("m32_s16_x1e-6", 1e-6, ("m32_s16", 1, 64, 64, 2, 32, 16, True, True)),
     ("m32_s16_x1e3", 1e3, ("m32_s16", 1, 64, 64, 2, 32, 16, True, True)),
     ("m16_s8_bias_x1e-8", 1e-8, ("m16_s8_bias", 1, 32, 32, 2, 16, 8, True, True, 16)),
+    ("m16_s8_rank32_x1e-6", 1e-6, ("m16_s8_rank32", 1, 32, 32, 2, 16, 8, True, True, 32)),
     ("m32_s16_bf16_out_x1e-5", 1e-5, ("m32_s16_bf16_out", 1, 64, 64, 1, 32, 16, True, False)),
 ]
 

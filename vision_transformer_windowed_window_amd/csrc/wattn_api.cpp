@@ -20,7 +20,8 @@ hipError_t wattn_launch_bf16(const WattnPlan& plan, int nks, bool rope, bool out
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* scratch,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
-                            const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream);
+                            const void* bv, int r, float* dbu, float* dbv, const void* gz, float* dz,
+                            hipStream_t stream);
 hipError_t wattn_launch_select(const float* gate, int n, float tau, int* list, int* count, hipStream_t stream);
 hipError_t wattn_launch_local(const LocalPlan& P, bool out_f32, const void* q, const void* k, const void* v,
                               void* out, const int* list, const int* count, hipStream_t stream);
@@ -284,10 +285,10 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   if (st != WATTN_OK) return st;
   if (d != 32) return WATTN_ERR_HEAD_DIM;
   if (dtype != WATTN_BF16 && dtype != WATTN_BF16_OUT_FP32) return WATTN_ERR_DTYPE;
-  if (r != 0 && r != 16) return WATTN_ERR_RANK;
+  if (r != 0 && r != 16 && r != 32) return WATTN_ERR_RANK;
   if (r == 0 && (bias_u != nullptr || bias_v != nullptr || dbias_u != nullptr || dbias_v != nullptr))
     return WATTN_ERR_RANK;
-  if (r == 16 && (bias_u == nullptr || bias_v == nullptr || dbias_u == nullptr || dbias_v == nullptr))
+  if (r > 0 && (bias_u == nullptr || bias_v == nullptr || dbias_u == nullptr || dbias_v == nullptr))
     return WATTN_ERR_RANK;
   const int64_t elems = (int64_t)B * Hgrid * Wgrid * H * d;
   if (elems >= kMaxElems) return WATTN_ERR_SHAPE;
@@ -343,7 +344,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
     scratch = static_cast<float*>(p);
   }
   const hipError_t e = wattn_launch_bwd(plan, theta != nullptr, dtype == WATTN_BF16_OUT_FP32, q, k, v, out, dout,
-                                        lse, scratch, dq, dk, dv, dtheta, theta, bias_u, bias_v, dbias_u, dbias_v, gz,
+                                        lse, scratch, dq, dk, dv, dtheta, theta, bias_u, bias_v, r, dbias_u, dbias_v, gz,
                                         dz, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? WATTN_OK : WATTN_ERR_HIP;
 }

@@ -837,9 +837,10 @@ __device__ __forceinline__ int grad_scale_exp(float gmax) {
   return max(-GRAD_EXP_LIMIT, min(GRAD_EXP_LIMIT, e));    // 0 and non-finite gmax give e = 3
 }
 
-// ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.
-template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
-__global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
+// ---- Kernel A: dq (and D) per query tile; K/V streamed like the forward pass.  BR is the
+//      bias rank (0, 16 or 32): the bias factors enter the scores as BR extra channels.
+template <int NW, bool ROPE, bool OUTF32, int BR, bool GATE>
+__global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
@@ -848,9 +849,12 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     uint16_t* __restrict__ dot, uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
+  constexpr bool BIAS = BR > 0;
+  constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
+  static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
-  __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * 16 : 8];  // bias factor v of the keys (fp16)
+  __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * BR : 8];  // bias factor v of the keys (fp16)
   __shared__ float sDth[D / 2];
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
@@ -866,8 +870,8 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
   if (tid < D / 2) sDth[tid] = 0.f;
 
   // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
-  //      (preset with the row's gradient-scale exponent);
-  //      with a bias, u * log2(e) in channels 0..15 of a zero-padded k = 32 operand
+  //      (preset with the row's gradient-scale exponent); with a bias, u * log2(e) as a k = 32
+  //      operand (rank 16: channels 0..15, zero-padded; rank 32: all of it)
   u32x4 qraw[2], dOf[2], Qb[2];
   f32x4 CnL[2], CnD[2];
   int qpos_r[2], qpos_c[2];
@@ -891,10 +895,10 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     load8<OUTF32>(out, qoff[a] + 8 * g, o[a]);
     lraw[a] = lse[qoff[a] / D];
     if (GATE) zraw[a] = *reinterpret_cast<const u32x4*>(gz + qoff[a] + 8 * g);
-    // lanes g = 2, 3 reload the first half of the 16 bias channels and ignore it
+    // rank 16: lanes g = 2, 3 reload the first half of the 16 bias channels and ignore it
     if (BIAS)
       braw[a] = *reinterpret_cast<const u32x4*>(
-          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 8 * (g & 1));
+          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * BR + 8 * (BR == 32 ? g : (g & 1)));
   }
   int gexp[2];     // gradient-scale exponent of each query row
   float wgmax = 0.f;
@@ -936,7 +940,7 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     gexp[a] = grad_scale_exp(gm);
     L2 -= (float)gexp[a];     // P becomes 2^e P
     Qb[a] = u32x4{0u, 0u, 0u, 0u};
-    if (BIAS && qvalid[a] && g < 2) {
+    if (BIAS && qvalid[a] && (BR == 32 || g < 2)) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(braw[a][p]) * LOG2E, bf_hi(braw[a][p]) * LOG2E);
     }
@@ -946,11 +950,12 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
   }
 
-  // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V; threads 0 .. 2 KT - 1
-  //      also the 16-byte half t % 2 of the bias factor v of key t / 2)
+  // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V; with a rank-32 bias
+  //      the same chunk of the key's bias factor v; with rank 16, threads 0 .. 2 KT - 1 the
+  //      16-byte half t % 2 of the bias factor v of key t / 2)
   const int lk = tid >> 2, lch = tid & 3;
-  const int bk = (tid % (2 * KT)) >> 1, bch = tid & 1;
-  const bool bthread = BIAS && tid < 2 * KT;
+  const int bk = BR == 32 ? lk : (tid % (2 * KT)) >> 1, bch = BR == 32 ? lch : tid & 1;
+  const bool bthread = BIAS && (BR == 32 || tid < 2 * KT);
   Walker W, Wb;
   walker_init(W, X, lk, 8 * lch, rowstride, colstride);
   walker_init(Wb, X, bk, 0, rowstride, colstride);
@@ -964,7 +969,7 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
     lpos = (lch < 2) ? (X.t.r0 + W.ci) : (X.t.c0 + W.cj);
     if (bthread) {
       const int key = (tile * KT + bk < n) ? (X.t.r0 + Wb.ci) * M + (X.t.c0 + Wb.cj) : 0;
-      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)X.t.h * M * M + key) * 16 + 8 * bch);
+      pb = *reinterpret_cast<const u32x4*>(bv + ((int64_t)X.t.h * M * M + key) * BR + 8 * bch);
     }
   };
   auto store = [&](int buf) {
@@ -986,7 +991,10 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
       u32x4 br;
 #pragma unroll
       for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[p]), bf_hi(pb[p]));
-      *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = br;
+      if (BR == 32)  // rows of 32 channels swizzled like K
+        *reinterpret_cast<u32x4*>(&sKb[buf][bk * 32 + 8 * (bch ^ kswz(bk))]) = br;
+      else
+        *reinterpret_cast<u32x4*>(&sKb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = br;
     }
   };
 
@@ -1037,13 +1045,14 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
   const int krow = 8 * (c >> 2) + (c & 3);
   const int vrow = 8 * g + (c >> 2);
   const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
-  f32x4 dQ[2][2];  // [channel block][query block]: channels 16 cb + 4 g + e of query 16 a + c
-  f32x4 dU[2];     // [query block]: bias channels 4 g + e of query 16 a + c
+  f32x4 dQ[2][2];    // [channel block][query block]: channels 16 cb + 4 g + e of query 16 a + c
+  f32x4 dU[NBB][2];  // [bias channel block][query block]: bias channels 16 cb + 4 g + e of query 16 a + c
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     dQ[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
     dQ[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dU[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < NBB; ++cb) dU[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const bool wave_live = X.t.q0 + wave * 32 < n;
 
@@ -1055,22 +1064,27 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
       // one 32-key block; MASK: the region's last, partial block, whose padded keys get -inf
       auto kblock = [&](int kb, int kg, auto mask_tag) {
           constexpr bool MASK = decltype(mask_tag)::value;
-          u32x4 Kf[2], Vr[2], KTf[2], Kb[2], VbT;
+          u32x4 Kf[2], Vr[2], KTf[2], Kb[2], VbT[NBB];
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int key = kb + krow + 4 * b;
             Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][key * D + ((g ^ kswz(key)) * 8)]);
             Vr[b] = *reinterpret_cast<const u32x4*>(&sV[buf][key * D + ((g ^ vswz(key)) * 8)]);
-            if (BIAS) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+            if (BR == 16) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+            if (BR == 32) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[buf][key * 32 + 8 * (g ^ kswz(key))]);
           }
-          if (BIAS) {  // bias factor v^T: channel c, keys kb + 8 g .. 8 g + 7
-            u32x2 h[2];
+          if (BIAS) {  // bias factor v^T: channel 16 cb + c, keys kb + 8 g .. 8 g + 7
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int row = kb + vrow + 4 * hh;
-              h[hh] = lds_read_tr16(&sKb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+            for (int cb = 0; cb < NBB; ++cb) {
+              u32x2 h[2];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const int row = kb + vrow + 4 * hh;
+                h[hh] = BR == 32 ? lds_read_tr16(&sKb[buf][row * 32 + (((2 * cb + vch) ^ kswz(row)) * 8) + vsub])
+                                 : lds_read_tr16(&sKb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+              }
+              VbT[cb] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
             }
-            VbT = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
           }
 #pragma unroll
           for (int cb = 0; cb < 2; ++cb) {
@@ -1106,7 +1120,9 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
             const u32x4 dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
 #pragma unroll
             for (int cb = 0; cb < 2; ++cb) dQ[cb][a] = mfma16_f16(KTf[cb], dSa, dQ[cb][a]);
-            if (BIAS) dU[a] = mfma16_f16(VbT, dSa, dU[a]);
+#pragma unroll
+            for (int cb = 0; cb < NBB; ++cb)
+              if (BIAS) dU[cb][a] = mfma16_f16(VbT[cb], dSa, dU[cb][a]);
           }
       };
 #pragma unroll
@@ -1132,10 +1148,12 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!qvalid[a]) continue;
-      float* dst = dbu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * 16 + 4 * g;
+      float* dst = dbu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * BR + 4 * g;
       const float us = __builtin_ldexpf(1.0f, -gexp[a]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dU[a][e] * us);
+      for (int cb = 0; cb < NBB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(dst + 16 * cb + e, dU[cb][a][e] * us);
     }
   }
   // the raw q channels of the dtheta sums, all loads issued before the first use
@@ -1166,7 +1184,7 @@ __global__ __launch_bounds__(64 * NW, BIAS ? 2 : 4) void wattn_bwd_dq_kernel(
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
-template <int NW, bool ROPE, bool BIAS>
+template <int NW, bool ROPE, int BR>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ delta,
@@ -1175,9 +1193,12 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
+  constexpr bool BIAS = BR > 0;
+  constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
+  static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
   __shared__ __align__(16) uint16_t sQ[2][QTT * D];
   __shared__ __align__(16) uint16_t sO[2][QTT * D];
-  __shared__ __align__(16) uint16_t sUb[BIAS ? 2 : 1][BIAS ? QTT * 16 : 8];  // u * log2(e) of the queries (fp16)
+  __shared__ __align__(16) uint16_t sUb[BIAS ? 2 : 1][BIAS ? QTT * BR : 8];  // u * log2(e) of the queries (fp16)
   __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
   __shared__ float sDth[D / 2];
@@ -1198,7 +1219,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const float gshift = (float)gexp;
 
   // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands; with a bias, the
-  //      factor v_b in channels 0..15 of a zero-padded k = 32 operand
+  //      factor v_b as a k = 32 operand (rank 16: channels 0..15, zero-padded)
   u32x4 kraw[2], Vf[2], Vbf[2];
   int kpos_r[2], kpos_c[2];
   int64_t koffs[2];
@@ -1220,19 +1241,20 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       Vf[a] = u32x4{0u, 0u, 0u, 0u};
     }
     Vbf[a] = u32x4{0u, 0u, 0u, 0u};
-    if (BIAS && kvalid[a] && g < 2) {
+    if (BIAS && kvalid[a] && (BR == 32 || g < 2)) {
       const u32x4 raw = *reinterpret_cast<const u32x4*>(
-          bv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * 16 + 8 * g);
+          bv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * BR + 8 * g);
 #pragma unroll
       for (int p = 0; p < 4; ++p) Vbf[a][p] = pack_f16(bf_lo(raw[p]), bf_hi(raw[p]));
     }
   }
 
-  // ---- query tile loader: thread t owns chunk t % 4 of query t / 4 in q and dO; threads
-  //      0 .. QTT - 1 also stage query t's statistics
+  // ---- query tile loader: thread t owns chunk t % 4 of query t / 4 in q and dO (and, with a
+  //      rank-32 bias, in the query's factor u); threads 0 .. QTT - 1 also stage query t's
+  //      statistics; with rank 16, threads 0 .. 2 QTT - 1 the half t % 2 of the u of query t / 2
   const int lk = tid >> 2, lch = tid & 3;
-  const int bk = (tid % (2 * QTT)) >> 1, bch = tid & 1;
-  const bool bthread = BIAS && tid < 2 * QTT;
+  const int bk = BR == 32 ? lk : (tid % (2 * QTT)) >> 1, bch = BR == 32 ? lch : tid & 1;
+  const bool bthread = BIAS && (BR == 32 || tid < 2 * QTT);
   Walker W, Ws, Wb;
   walker_init(W, X, lk, 8 * lch, rowstride, colstride);
   walker_init(Ws, X, tid < QTT ? tid : 0, 0, rowstride, colstride);
@@ -1256,7 +1278,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     pd = delta[X.img / D + so];
     if (BIAS) {
       const int qn = (tile * QTT + bk < n) ? (X.t.r0 + Wb.ci) * M + (X.t.c0 + Wb.cj) : 0;
-      pu = *reinterpret_cast<const u32x4*>(bu + ((int64_t)X.t.h * M * M + qn) * 16 + 8 * bch);
+      pu = *reinterpret_cast<const u32x4*>(bu + ((int64_t)X.t.h * M * M + qn) * BR + 8 * bch);
     }
   };
   auto store = [&](int buf) {
@@ -1271,7 +1293,10 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       u32x4 ur;
 #pragma unroll
       for (int p = 0; p < 4; ++p) ur[p] = pack_f16(bf_lo(pu[p]) * LOG2E, bf_hi(pu[p]) * LOG2E);
-      *reinterpret_cast<u32x4*>(&sUb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = ur;
+      if (BR == 32)  // rows of 32 channels swizzled like Q
+        *reinterpret_cast<u32x4*>(&sUb[buf][bk * 32 + 8 * (bch ^ kswz(bk))]) = ur;
+      else
+        *reinterpret_cast<u32x4*>(&sUb[buf][bk * 16 + 8 * (bch ^ bswz(bk))]) = ur;
     }
   };
 
@@ -1304,10 +1329,11 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int vrow = 8 * g + (c >> 2);
   const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
   f32x4 dV[2][2], dK[2][2];  // [dim / channel block][key block]
-  f32x4 dVb[2];              // [key block]: bias channels 4 g + e of key 16 a + c (times log2(e))
+  f32x4 dVb[NBB][2];         // [bias channel block][key block]: channels 16 x + 4 g + e of key 16 a + c (times log2(e))
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    dVb[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < NBB; ++x) dVb[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       dV[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1326,23 +1352,28 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       for (int st = 0; st < QTT / 32; ++st) {
         if (st < nst) {
           const int qb = st * 32;
-          u32x4 Qr[2], Or[2], OT[2], QTf[2], Ur[2], UT;
+          u32x4 Qr[2], Or[2], OT[2], QTf[2], Ur[2], UT[NBB];
           f32x4 CL[2], CD[2];
-          if (BIAS) {  // bias factor (u log2 e)^T: channel c, queries qb + 8 g .. 8 g + 7
-            u32x2 h[2];
+          if (BIAS) {  // bias factor (u log2 e)^T: channel 16 x + c, queries qb + 8 g .. 8 g + 7
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int row = qb + vrow + 4 * hh;
-              h[hh] = lds_read_tr16(&sUb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+            for (int x = 0; x < NBB; ++x) {
+              u32x2 h[2];
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                const int row = qb + vrow + 4 * hh;
+                h[hh] = BR == 32 ? lds_read_tr16(&sUb[buf][row * 32 + (((2 * x + vch) ^ kswz(row)) * 8) + vsub])
+                                 : lds_read_tr16(&sUb[buf][row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+              }
+              UT[x] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
             }
-            UT = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
           }
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int row = qb + krow + 4 * b;
             Qr[b] = *reinterpret_cast<const u32x4*>(&sQ[buf][row * D + ((g ^ kswz(row)) * 8)]);
             Or[b] = *reinterpret_cast<const u32x4*>(&sO[buf][row * D + ((g ^ vswz(row)) * 8)]);
-            if (BIAS) Ur[b] = *reinterpret_cast<const u32x4*>(&sUb[buf][row * 16 + 8 * ((g & 1) ^ bswz(row))]);
+            if (BR == 16) Ur[b] = *reinterpret_cast<const u32x4*>(&sUb[buf][row * 16 + 8 * ((g & 1) ^ bswz(row))]);
+            if (BR == 32) Ur[b] = *reinterpret_cast<const u32x4*>(&sUb[buf][row * 32 + 8 * (g ^ kswz(row))]);
             // statistics of the accumulator rows of this lane: queries qb + 8 g + 4 b + e
             CL[b] = *reinterpret_cast<const f32x4*>(&sL[buf][qb + 8 * g + 4 * b]);
             CD[b] = *reinterpret_cast<const f32x4*>(&sDl[buf][qb + 8 * g + 4 * b]);
@@ -1383,7 +1414,9 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
               dV[x][a] = mfma16_bf16(OT[x], Pa, dV[x][a]);
               dK[x][a] = mfma16_f16(QTf[x], dSa, dK[x][a]);
             }
-            if (BIAS) dVb[a] = mfma16_f16(UT, dSa, dVb[a]);
+#pragma unroll
+            for (int x = 0; x < NBB; ++x)
+              if (BIAS) dVb[x][a] = mfma16_f16(UT[x], dSa, dVb[x][a]);
           }
         }
       }
@@ -1404,9 +1437,11 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!kvalid[a]) continue;
-      float* dst = dbv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * 16 + 4 * g;
+      float* dst = dbv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * BR + 4 * g;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(dst + e, dVb[a][e] * gunscale_ln2);
+      for (int x = 0; x < NBB; ++x)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(dst + 16 * x + e, dVb[x][a][e] * gunscale_ln2);
     }
   }
 
@@ -1440,9 +1475,17 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   }
 }
 
-__global__ void wattn_fill_zero_kernel(float* __restrict__ p, int n) {
+// zeroes up to four float arrays in one launch (the backward pass's atomic targets), so that
+// the clearing costs one dispatch however many of them a call has
+struct ZeroList {
+  float* p[4];
+  int n[4];
+};
+__global__ void wattn_fill_zero_kernel(const ZeroList z) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (i < z.n[j]) z.p[j][i] = 0.f;
 }
 
 }  // namespace
@@ -1526,7 +1569,7 @@ hipError_t wattn_launch_f32(const WattnF32Plan& plan, int r, const void* q, cons
 }
 
 // ---- backward launchers
-template <int NW, bool ROPE, bool OUTF32, bool BIAS, bool GATE>
+template <int NW, bool ROPE, bool OUTF32, int BR, bool GATE>
 static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const void* k, const void* v, const void* out,
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
@@ -1540,12 +1583,12 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   auto BU = static_cast<const uint16_t*>(bu);
   auto BV = static_cast<const uint16_t*>(bv);
   auto GZ = static_cast<const uint16_t*>(gz);
-  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BIAS, GATE>), dim3(plan.grid), dim3(64 * NW),
+  hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BR, GATE>), dim3(plan.grid), dim3(64 * NW),
                      table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz, qt,
                      dot, gmax, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, BIAS>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
+  hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, BR>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
                      static_cast<const uint16_t*>(qt), K, V, static_cast<const uint16_t*>(dot), lse,
                      static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv,
                      static_cast<const uint32_t*>(gmax), plan);
@@ -1553,23 +1596,28 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
 }
 
 template <int NW, bool GATE>
-static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, bool bias, const void* q,
+static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, int br, const void* q,
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
                                 float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
                                 const void* bu, const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
                                 uint16_t* qt, uint16_t* dot, uint32_t* gmax, hipStream_t stream) {
 #define WATTN_BWD_ARGS \
   plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, gmax, stream
-  const int sel = (bias ? 4 : 0) + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+  const int sel = (br / 16) * 4 + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
-    case 0: return launch_bwd_inst<NW, false, false, false, GATE>(WATTN_BWD_ARGS);
-    case 1: return launch_bwd_inst<NW, false, true, false, GATE>(WATTN_BWD_ARGS);
-    case 2: return launch_bwd_inst<NW, true, false, false, GATE>(WATTN_BWD_ARGS);
-    case 3: return launch_bwd_inst<NW, true, true, false, GATE>(WATTN_BWD_ARGS);
-    case 4: return launch_bwd_inst<NW, false, false, true, GATE>(WATTN_BWD_ARGS);
-    case 5: return launch_bwd_inst<NW, false, true, true, GATE>(WATTN_BWD_ARGS);
-    case 6: return launch_bwd_inst<NW, true, false, true, GATE>(WATTN_BWD_ARGS);
-    default: return launch_bwd_inst<NW, true, true, true, GATE>(WATTN_BWD_ARGS);
+    case 0: return launch_bwd_inst<NW, false, false, 0, GATE>(WATTN_BWD_ARGS);
+    case 1: return launch_bwd_inst<NW, false, true, 0, GATE>(WATTN_BWD_ARGS);
+    case 2: return launch_bwd_inst<NW, true, false, 0, GATE>(WATTN_BWD_ARGS);
+    case 3: return launch_bwd_inst<NW, true, true, 0, GATE>(WATTN_BWD_ARGS);
+    case 4: return launch_bwd_inst<NW, false, false, 16, GATE>(WATTN_BWD_ARGS);
+    case 5: return launch_bwd_inst<NW, false, true, 16, GATE>(WATTN_BWD_ARGS);
+    case 6: return launch_bwd_inst<NW, true, false, 16, GATE>(WATTN_BWD_ARGS);
+    case 7: return launch_bwd_inst<NW, true, true, 16, GATE>(WATTN_BWD_ARGS);
+    case 8: return launch_bwd_inst<NW, false, false, 32, GATE>(WATTN_BWD_ARGS);
+    case 9: return launch_bwd_inst<NW, false, true, 32, GATE>(WATTN_BWD_ARGS);
+    case 10: return launch_bwd_inst<NW, true, false, 32, GATE>(WATTN_BWD_ARGS);
+    case 11: return launch_bwd_inst<NW, true, true, 32, GATE>(WATTN_BWD_ARGS);
+    default: return hipErrorInvalidValue;
   }
 #undef WATTN_BWD_ARGS
 }
@@ -1577,19 +1625,10 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
 hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, const void* q, const void* k,
                             const void* v, const void* out, const void* dout, const float* lse, float* scratch,
                             float* dq, float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
-                            const void* bv, float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream) {
-  const bool bias = bu != nullptr;
-  auto fill = [&](float* p, int64_t cnt) {
-    hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream, p,
-                       (int)cnt);
-    return hipGetLastError();
-  };
-  hipError_t e = hipSuccess;
-  if (rope && (e = fill(dtheta, (int64_t)plan.H * (D / 2))) != hipSuccess) return e;
-  if (bias) {
-    const int64_t cnt = (int64_t)plan.H * plan.M * plan.M * 16;
-    if ((e = fill(dbu, cnt)) != hipSuccess || (e = fill(dbv, cnt)) != hipSuccess) return e;
-  }
+                            const void* bv, int r, float* dbu, float* dbv, const void* gz, float* dz,
+                            hipStream_t stream) {
+  const int br = bu != nullptr ? r : 0;
+  if (br != 0 && br != 16 && br != 32) return hipErrorInvalidValue;
   // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32],
   // then 16 bytes holding the largest output-gradient entry (as float bits, zeroed first)
   const int64_t th = (int64_t)plan.B * plan.Hg * plan.Wg * plan.H;
@@ -1597,9 +1636,17 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
   uint16_t* qt = reinterpret_cast<uint16_t*>(scratch + ((th + 3) & ~int64_t(3)));
   uint16_t* dot = qt + th * D;
   float* gmax_slot = reinterpret_cast<float*>(dot + th * D);
-  if ((e = fill(gmax_slot, 4)) != hipSuccess) return e;
   uint32_t* gmax = reinterpret_cast<uint32_t*>(gmax_slot);
-#define WATTN_BWD_ARGS plan, rope, out_f32, bias, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
+  // one launch clears every atomic target: the gmax slot, dtheta and the bias-factor gradients
+  const int64_t nb64 = (int64_t)plan.H * plan.M * plan.M * br;
+  if (nb64 > 0x7fffff00LL) return hipErrorInvalidValue;  // one grid-stride-free launch covers them
+  const int nb = (int)nb64;
+  const ZeroList z = {{gmax_slot, dtheta, dbu, dbv}, {4, rope ? plan.H * (D / 2) : 0, nb, nb}};
+  const int zmax = std::max(std::max(z.n[0], z.n[1]), nb);
+  hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((zmax + 255) / 256)), dim3(256), 0, stream, z);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define WATTN_BWD_ARGS plan, rope, out_f32, br, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
                        dbu, dbv, gz, dz, qt, dot, gmax, stream
   const bool gate = gz != nullptr;
   switch (plan.nw) {
