@@ -142,7 +142,7 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
 
 /*
  * wattn_backward_scratch_bytes -- bytes of the scratch buffer wattn_backward and
- * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 32 T) + 16 with T = B Hgrid Wgrid H
+ * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 33 T) with T = B Hgrid Wgrid H
  * query rows.  -1 for a size <= 0 or d != 32.
  */
 int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
@@ -184,9 +184,11 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  * exp2(s log2(e) - lse log2(e)) in fp32); P is rounded to bf16 for dv, dS = P (dP - delta)
  * to fp16 for dq and dk; everything accumulates in fp32.  dS is rounded with a power-of-two
  * scale 2^e that puts the largest output-gradient entry in [4, 8) (per query row for dq and
- * dbias_u, over the whole call for dk, dv and dbias_v; |e| <= 96), and the fp32 products
- * are divided by 2^e, so the relative accuracy of every gradient does not depend on the
- * magnitude of dout (gradients scale exactly with a power-of-two factor on dout).
+ * dbias_u, per wrap region -- the queries a key attends with -- for dk, dv and dbias_v;
+ * |e| <= 96), and the fp32 products are divided by 2^e, so the relative accuracy of every
+ * gradient does not depend on the magnitude of dout, also where it differs between regions
+ * (gradients scale exactly with a power-of-two factor on dout).  No atomic operation takes
+ * part in dq, dk or dv, so they are bitwise reproducible.
  */
 int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
                    const float* lse, float* scratch, float* dq, float* dk, float* dv, float* dtheta,
@@ -202,7 +204,7 @@ int wattn_backward(const void* q, const void* k, const void* v, const void* out,
  * The scratch comes from a file-scope device array of the library (64 MiB on every GPU the
  * library runs on, held until the process ends), so the call allocates nothing: no hipMalloc,
  * hipFree or allocating library routine.  Calls that need more than that, i.e. more than
- * 508400 query rows B * Hgrid * Wgrid * H (wattn_backward_scratch_bytes > 64 MiB), return
+ * 493447 query rows B * Hgrid * Wgrid * H (wattn_backward_scratch_bytes > 64 MiB), return
  * WATTN_ERR_SCRATCH before any HIP call.  The first call on a device looks the array's address
  * up on that device (the device of `stream`; the current one for the null stream).
  *

@@ -172,7 +172,7 @@ def test_backward_noalloc_rejects_before_any_hip_call():
     """The no-allocation backward pass refuses a problem whose scratch would exceed the 64 MiB it
     holds (WATTN_ERR_SCRATCH = 11), and the usual argument errors, on the host."""
     lib = _lib()
-    rows_max = ((64 << 20) - 16) // 132
+    rows_max = (64 << 20) // 136
     assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max, 32) <= 64 << 20
     assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max + 1, 32) > 64 << 20
     # 16 x 128 x 128 x 3 heads = 786432 query rows: too many
@@ -189,9 +189,9 @@ def test_backward_noalloc_rejects_before_any_hip_call():
 def test_backward_scratch_bytes():
     # 512 query rows: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32 bf16
     # gradients, then 16 bytes for the largest output-gradient entry
-    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32 + 16
+    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32 + 4 * 512
     # 3 rows: the statistics are padded to 4 floats so the rows after them start 16-byte aligned
-    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32 + 16
+    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32 + 4 * 3
     assert _lib().wattn_backward_scratch_bytes(0, 2, 16, 16, 32) == -1
     assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 64) == -1
 

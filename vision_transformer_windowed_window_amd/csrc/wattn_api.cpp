@@ -264,8 +264,9 @@ extern "C" int wattn_forward_gated(const void* q, const void* k, const void* v, 
 namespace {
 
 // Backward scratch for `rows` query rows (T * H): the rowsum statistic as float32 [rows], padded
-// to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32] each.
-int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 32 * rows) * 4 + 16; }
+// to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32]
+// each, then one float per task (a task holds at least one query row, so at most `rows`).
+int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 33 * rows) * 4; }
 
 // Backward pass shared by wattn_backward, wattn_backward_gated (gz and dz both NULL or both
 // set) and wattn_backward_noalloc (library_scratch: scratch is NULL on entry and the

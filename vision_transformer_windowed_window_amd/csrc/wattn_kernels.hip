@@ -78,6 +78,7 @@ constexpr float REF_HEADROOM = 16.0f;  // the forward reference sits this far (b
 
 struct Task {
   int b, h, q0;
+  int qt, nqt;         // tile index within the region-head and its tile count (tasks qt - .. are consecutive)
   int r0, rh, c0, rw;  // region in window-local coordinates
   int y0, x0;          // region origin in the original grid (the region does not wrap)
   int step_i, step_j;  // one key tile as region rows and columns
@@ -130,6 +131,8 @@ __device__ __forceinline__ bool decode_task(const WattnPlan& P, int task, int QT
   t.c0 = S.c0;
   t.rw = S.rw;
   t.q0 = (int)qt * QT;
+  t.qt = (int)qt;
+  t.nqt = S.nqt;
   int y = wy * P.M + S.r0 + P.s;
   if (y >= P.Hg) y -= P.Hg;
   int x = wx * P.M + S.c0 + P.s;
@@ -829,8 +832,10 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 // largest output-gradient entry g_max so that 2^e g_max lies in [4, 8), and divide the
 // accumulated products by 2^e in fp32.  The factor is folded into the score preset (P
 // becomes 2^e P), so it costs no instruction per score.  The query-tile kernel takes e per
-// query row (its products sum over keys only); the key-tile kernel sums over the queries of
-// a region, so it takes one e for the call, from the largest entry over all rows.
+// query row (its products sum over keys only) and leaves the largest entry of its tile in
+// one float per task; the key-tile kernel sums over the queries of its wrap region, so it
+// takes one e per region from the largest of the region's tile entries (the tasks of a
+// region and head are consecutive).
 constexpr int GRAD_EXP_LIMIT = 96;
 __device__ __forceinline__ int grad_scale_exp(float gmax) {
   const int e = 3 - __builtin_amdgcn_frexp_expf(gmax);  // gmax in [2^(x-1), 2^x): 2^e gmax in [4, 8)
@@ -846,7 +851,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu,
     const uint16_t* __restrict__ gz, float* __restrict__ dz, uint16_t* __restrict__ qt,
-    uint16_t* __restrict__ dot, uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
+    uint16_t* __restrict__ dot, float* __restrict__ tmax, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
   constexpr int TSTR = bwd_table_stride(NW);
   constexpr bool BIAS = BR > 0;
@@ -861,7 +866,8 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
 
   const int tid = threadIdx.x;
   Task T0;
-  if (!decode_task(P, task_of_block(P, blockIdx.x), QT, T0)) return;
+  const int task = task_of_block(P, blockIdx.x);
+  if (!decode_task(P, task, QT, T0)) return;
   const TaskCtx X = make_ctx(P, T0, KT);
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -998,7 +1004,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     }
   };
 
-  // largest output-gradient entry of the workgroup, for the key-tile kernel's scale
+  // largest output-gradient entry of the tile, for the key-tile kernel's scale
   {
     float wm = wgmax;
 #pragma unroll
@@ -1012,7 +1018,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     float wm = sGmax[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) wm = fmaxf(wm, sGmax[w]);
-    atomicMax(gmax_bits, __float_as_uint(wm));  // non-negative floats order as their bits
+    tmax[task] = wm;  // every task of the launch writes its own slot
   }
   // queries: rotate (fp32), scale by log2(e) / sqrt(d), round to fp16
   u32x4 Qf[2];
@@ -1190,7 +1196,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ delta,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
-    const uint32_t* __restrict__ gmax_bits, const WattnPlan P) {
+    const float* __restrict__ tmax, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
   constexpr int TSTR = bwd_table_stride(NW);
   constexpr bool BIAS = BR > 0;
@@ -1202,21 +1208,26 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
   __shared__ float sDth[D / 2];
+  __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
   const int tid = threadIdx.x;
   Task T0;
-  if (!decode_task(P, task_of_block(P, blockIdx.x), KTW, T0)) return;
+  const int task = task_of_block(P, blockIdx.x);
+  if (!decode_task(P, task, KTW, T0)) return;
   const TaskCtx X = make_ctx(P, T0, QTT);
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   if (tid < D / 2) sDth[tid] = 0.f;
-  // one gradient-scale exponent for the call, from the largest output-gradient entry that
-  // the query-tile kernel found over all rows (see grad_scale_exp)
-  const int gexp = grad_scale_exp(__uint_as_float(__builtin_nontemporal_load(gmax_bits)));
-  const float gshift = (float)gexp;
+  // the largest output-gradient entry of the region: the query-tile kernel's entries of the
+  // region's tiles (tasks task - qt .. task - qt + nqt - 1, which hold the same region and
+  // head), reduced after the first barrier (see grad_scale_exp)
+  float rmax = 0.f;
+  for (int i = tid; i < X.t.nqt; i += NTHR) rmax = fmaxf(rmax, tmax[task - X.t.qt + i]);
+  int gexp = 0;        // the region's gradient-scale exponent, set after the first barrier
+  float gshift = 0.f;  // (float) gexp, added to the staged statistics
 
   // ---- this lane's keys: k (rotated, fp16) and v (bf16) as B operands; with a bias, the
   //      factor v_b as a k = 32 operand (rank 16: channels 0..15, zero-padded)
@@ -1300,9 +1311,18 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     }
   };
 
+  rmax = xmax32(xmax16(rmax));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
+  if (lane == 0) sGmax[wave] = rmax;
   fetch(0);
   if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
   __syncthreads();
+  float gm = sGmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) gm = fmaxf(gm, sGmax[w]);
+  gexp = grad_scale_exp(gm);  // one exponent for the region
+  gshift = (float)gexp;
   u32x4 Kf[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -1475,16 +1495,16 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   }
 }
 
-// zeroes up to four float arrays in one launch (the backward pass's atomic targets), so that
+// zeroes up to three float arrays in one launch (the backward pass's atomic targets), so that
 // the clearing costs one dispatch however many of them a call has
 struct ZeroList {
-  float* p[4];
-  int n[4];
+  float* p[3];
+  int n[3];
 };
 __global__ void wattn_fill_zero_kernel(const ZeroList z) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 3; ++j)
     if (i < z.n[j]) z.p[j][i] = 0.f;
 }
 
@@ -1574,7 +1594,7 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
                                   const void* dout, const float* lse, float* delta, float* dq, float* dk, float* dv,
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
                                   float* dbv, const void* gz, float* dz, uint16_t* qt, uint16_t* dot,
-                                  uint32_t* gmax, hipStream_t stream) {
+                                  float* tmax, hipStream_t stream) {
   if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
   const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
@@ -1585,13 +1605,13 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   auto GZ = static_cast<const uint16_t*>(gz);
   hipLaunchKernelGGL((wattn_bwd_dq_kernel<NW, ROPE, OUTF32, BR, GATE>), dim3(plan.grid), dim3(64 * NW),
                      table_bytes, stream, Q, K, V, out, dout, lse, delta, dq, dtheta, theta, BU, BV, dbu, GZ, dz, qt,
-                     dot, gmax, plan);
+                     dot, tmax, plan);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((wattn_bwd_dkdv_kernel<NW, ROPE, BR>), dim3(plan.grid), dim3(64 * NW), table_bytes, stream,
                      static_cast<const uint16_t*>(qt), K, V, static_cast<const uint16_t*>(dot), lse,
                      static_cast<const float*>(delta), dk, dv, dtheta, theta, BU, BV, dbv,
-                     static_cast<const uint32_t*>(gmax), plan);
+                     static_cast<const float*>(tmax), plan);
   return hipGetLastError();
 }
 
@@ -1600,9 +1620,9 @@ static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, 
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
                                 float* delta, float* dq, float* dk, float* dv, float* dtheta, const float* theta,
                                 const void* bu, const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
-                                uint16_t* qt, uint16_t* dot, uint32_t* gmax, hipStream_t stream) {
+                                uint16_t* qt, uint16_t* dot, float* tmax, hipStream_t stream) {
 #define WATTN_BWD_ARGS \
-  plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, gmax, stream
+  plan, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, qt, dot, tmax, stream
   const int sel = (br / 16) * 4 + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
   switch (sel) {
     case 0: return launch_bwd_inst<NW, false, false, 0, GATE>(WATTN_BWD_ARGS);
@@ -1630,24 +1650,27 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
   const int br = bu != nullptr ? r : 0;
   if (br != 0 && br != 16 && br != 32) return hipErrorInvalidValue;
   // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32],
-  // then 16 bytes holding the largest output-gradient entry (as float bits, zeroed first)
+  // then one float per task (at most TH: every task holds at least one query row), the
+  // largest output-gradient entry of the task's query tile
   const int64_t th = (int64_t)plan.B * plan.Hg * plan.Wg * plan.H;
+  if (plan.ntasks > th) return hipErrorInvalidValue;
   float* delta = scratch;
   uint16_t* qt = reinterpret_cast<uint16_t*>(scratch + ((th + 3) & ~int64_t(3)));
   uint16_t* dot = qt + th * D;
-  float* gmax_slot = reinterpret_cast<float*>(dot + th * D);
-  uint32_t* gmax = reinterpret_cast<uint32_t*>(gmax_slot);
-  // one launch clears every atomic target: the gmax slot, dtheta and the bias-factor gradients
+  float* tmax = reinterpret_cast<float*>(dot + th * D);
+  // one launch clears every atomic target: dtheta and the bias-factor gradients
   const int64_t nb64 = (int64_t)plan.H * plan.M * plan.M * br;
   if (nb64 > 0x7fffff00LL) return hipErrorInvalidValue;  // one grid-stride-free launch covers them
   const int nb = (int)nb64;
-  const ZeroList z = {{gmax_slot, dtheta, dbu, dbv}, {4, rope ? plan.H * (D / 2) : 0, nb, nb}};
-  const int zmax = std::max(std::max(z.n[0], z.n[1]), nb);
-  hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((zmax + 255) / 256)), dim3(256), 0, stream, z);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const ZeroList z = {{dtheta, dbu, dbv}, {rope ? plan.H * (D / 2) : 0, nb, nb}};
+  const int zmax = std::max(z.n[0], nb);
+  if (zmax > 0) {
+    hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((zmax + 255) / 256)), dim3(256), 0, stream, z);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define WATTN_BWD_ARGS plan, rope, out_f32, br, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
-                       dbu, dbv, gz, dz, qt, dot, gmax, stream
+                       dbu, dbv, gz, dz, qt, dot, tmax, stream
   const bool gate = gz != nullptr;
   switch (plan.nw) {
     case 2: return gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS);

@@ -5,7 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 // Size of the library-held scratch on each device: 64 MiB, room for the backward pass of up to
-// (64 MiB - 16) / 132 = 508400 query rows (B * Hgrid * Wgrid * H).
+// 64 MiB / 136 = 493447 query rows (B * Hgrid * Wgrid * H).
 #define WATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 hipError_t wattn_noalloc_scratch(hipStream_t stream, void** out);
