@@ -149,7 +149,7 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
 
 /*
  * wattn_backward -- gradients of loss = sum(dout * out) of the shifted-window attention
- * (the FLASHSWIN page's memory claims cover the scores "and their gradient": the backward
+ * (the FLASHSWIN page's memory claims cover the scores and their gradient: the backward
  * pass recomputes P per tile from q, k and lse and never stores an N x N matrix).
  *
  * Inputs (device pointers, caller-owned, read only):

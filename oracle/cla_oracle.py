@@ -20,8 +20,8 @@ Readings where the page leaves a step open (each also used by the device library
   * the depth-wise convolution has a 3 x 3 kernel per channel, stride 1, zero padding 1 (the
     output has the input's size) and a bias per channel; the point-wise convolution is a
     C x C matrix plus a bias; there is no activation between them;
-  * "modulates" is an elementwise product: out = sigmoid(z) * attention output, channel by
-    channel, with z the point-wise output (the gate logits);
+  * the gate acts on the attention output as an elementwise product: out = sigmoid(z) *
+    attention output, channel by channel, with z the point-wise output (the gate logits);
   * a cyclic schedule runs the layers in order, layer l with window side M_l and shift 0 or
     M_l / 2 (alternating, as Swin does); each layer has its own q, k, v and parameters.
 """
