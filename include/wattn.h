@@ -142,8 +142,9 @@ int wattn_forward_lse(const void* q, const void* k, const void* v, void* out, fl
 
 /*
  * wattn_backward_scratch_bytes -- bytes of the scratch buffer wattn_backward and
- * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 33 T) with T = B Hgrid Wgrid H
- * query rows.  -1 for a size <= 0 or d != 32.
+ * wattn_backward_gated take for these sizes: 4 * (ceil4(T) + 33 T + 4096 H) with T = B Hgrid
+ * Wgrid H query rows (4096 H: 256 copies of the partial angle-gradient sums).  -1 for a size
+ * <= 0 or d != 32.
  */
 int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
 
@@ -164,11 +165,13 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *             16-byte aligned (WATTN_ERR_POINTER otherwise), contents undefined on entry and
  *             on return.  The query-tile kernel writes rowsum(dout * out) per query, the
  *             rotated and scaled queries (fp16), the output gradient (bf16) and the largest
- *             output-gradient entry there once; the key-tile kernel streams them back
- *             instead of redoing that work per tile.
+ *             output-gradient entry of each query tile there once; the key-tile kernel
+ *             streams them back instead of redoing that work per tile.  Every kernel adds its
+ *             angle-gradient sums into the copies at the end of the scratch.
  *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
- *   dtheta  : float32 [H][d/2] (zeroed, then accumulated with atomic adds, so its last bits
- *             depend on the order of the additions); required iff theta is not NULL.
+ *   dtheta  : float32 [H][d/2], written by a last small kernel from partial sums that the
+ *             workgroups add into 256 copies in the scratch with atomic adds, so its last bits
+ *             depend on the order of the additions; required iff theta is not NULL.
  *   dbias_u, dbias_v : float32 [H][M*M][r], the gradients of the bias factors (summed over
  *             every window and image, which share them; zeroed, then accumulated with atomic
  *             adds); required iff r > 0.
@@ -176,9 +179,11 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *             wattn_forward: NULL, NULL, 0 or both set with r == 16 or r == 32
  *             (WATTN_ERR_RANK otherwise, also when the dbias pointers do not match).
  * Sizes, shift and d follow wattn_forward.  No output may overlap an input or another
- * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: fill kernels for the accumulated
- * outputs (one launch) and two attention kernels (one per query tile: delta, dq, the q part of dtheta,
- * dbias_u; one per key tile: dk, dv, the k part of dtheta, dbias_v).
+ * output (WATTN_ERR_ALIAS).  Asynchronous on `stream`: one fill launch for the accumulated
+ * outputs, then for M <= 8 one fused kernel (a workgroup holds a whole wrap region), for
+ * larger windows two (one per query tile: delta, dq, the q part of dtheta, dbias_u; one per
+ * key tile: dk, dv, the k part of dtheta, dbias_v), and with theta the kernel that sums the
+ * angle-gradient copies into dtheta.
  *
  * Numerics: the scores are recomputed as in the forward pass (fp16 operands, P =
  * exp2(s log2(e) - lse log2(e)) in fp32); P is rounded to bf16 for dv, dS = P (dP - delta)
@@ -204,7 +209,7 @@ int wattn_backward(const void* q, const void* k, const void* v, const void* out,
  * The scratch comes from a file-scope device array of the library (64 MiB on every GPU the
  * library runs on, held until the process ends), so the call allocates nothing: no hipMalloc,
  * hipFree or allocating library routine.  Calls that need more than that, i.e. more than
- * 493447 query rows B * Hgrid * Wgrid * H (wattn_backward_scratch_bytes > 64 MiB), return
+ * about 493300 query rows B * Hgrid * Wgrid * H (wattn_backward_scratch_bytes > 64 MiB), return
  * WATTN_ERR_SCRATCH before any HIP call.  The first call on a device looks the array's address
  * up on that device (the device of `stream`; the current one for the null stream).
  *

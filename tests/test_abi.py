@@ -172,7 +172,13 @@ def test_backward_noalloc_rejects_before_any_hip_call():
     """The no-allocation backward pass refuses a problem whose scratch would exceed the 64 MiB it
     holds (WATTN_ERR_SCRATCH = 11), and the usual argument errors, on the host."""
     lib = _lib()
-    rows_max = (64 << 20) // 136
+    def nbytes(rows, H=1):  # the formula of wattn_backward_scratch_bytes
+        return 4 * ((rows + 3) // 4 * 4 + 33 * rows + 4096 * H)
+
+    rows_max = ((64 << 20) // 4 - 4096) // 34
+    while nbytes(rows_max + 1) <= 64 << 20:
+        rows_max += 1
+    assert rows_max == 493327
     assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max, 32) <= 64 << 20
     assert lib.wattn_backward_scratch_bytes(1, 1, 1, rows_max + 1, 32) > 64 << 20
     # 16 x 128 x 128 x 3 heads = 786432 query rows: too many
@@ -187,11 +193,11 @@ def test_backward_noalloc_rejects_before_any_hip_call():
 
 
 def test_backward_scratch_bytes():
-    # 512 query rows: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32 bf16
-    # gradients, then 16 bytes for the largest output-gradient entry
-    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32 + 4 * 512
+    # 512 query rows of 2 heads: 512 float32 statistics, then 512 x 32 fp16 queries and 512 x 32
+    # bf16 gradients, one float per task (at most one per row), 256 copies of 2 x 16 floats
+    assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 32) == 4 * 512 + 2 * 2 * 512 * 32 + 4 * 512 + 4 * 256 * 32
     # 3 rows: the statistics are padded to 4 floats so the rows after them start 16-byte aligned
-    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32 + 4 * 3
+    assert _lib().wattn_backward_scratch_bytes(1, 3, 1, 1, 32) == 16 + 2 * 2 * 3 * 32 + 4 * 3 + 4 * 256 * 48
     assert _lib().wattn_backward_scratch_bytes(0, 2, 16, 16, 32) == -1
     assert _lib().wattn_backward_scratch_bytes(1, 2, 16, 16, 64) == -1
 

@@ -81,6 +81,10 @@ CASES = [
     ("m16_s8_rank32_bf16_out", 1, 32, 32, 2, 16, 8, True, False, 32),
     ("m32_s16_rank32_norope", 1, 64, 64, 2, 32, 16, False, True, 32),
     ("m40_s13_rank32", 1, 40, 80, 1, 40, 13, True, True, 32),
+    # M <= 8: every region fits one workgroup of the fused kernel (as in the M 4 and 8 cases above)
+    ("m8_s0_rank32_norope_bf16_out", 1, 24, 16, 3, 8, 0, False, False, 32),
+    ("m6_s2_bias", 1, 18, 24, 2, 6, 2, True, True, 16),
+    ("m2_s1_bf16_out", 2, 4, 8, 2, 2, 1, True, False),
 ]
 
 
@@ -137,13 +141,15 @@ def test_backward_output_gradient_scale(case):
     _check_case(case[2], dout_scale=case[1])
 
 
-def test_backward_region_scales_differ():
+@pytest.mark.parametrize("M,s", [(16, 8), (8, 4)], ids=["m16_two_kernels", "m8_fused"])
+def test_backward_region_scales_differ(M, s):
     """Output gradients of very different size in different regions: image 0's are scaled by
     1e-7, image 1's are not.  dk and dv sum over the queries of a key's wrap region, and
     each region takes the gradient scale of its own largest output-gradient entry, so both
     images keep the relative accuracy (one scale for the whole call, set by image 1, would
-    round image 0's dS to fp16 zeros and subnormals)."""
-    B, Hg, Wg, H, M, s = 2, 32, 32, 2, 16, 8
+    round image 0's dS to fp16 zeros and subnormals).  M = 8 runs the fused kernel of small
+    regions, M = 16 the query-tile and key-tile kernels."""
+    B, Hg, Wg, H = 2, 32, 32, 2
     note(f"backward two scales: B={B} grid={Hg}x{Wg} H={H} M={M} shift={s}")
     q, k, v, th, dout, _, _ = _setup(B, Hg, Wg, H, M, 931)
     dout[0] *= 1e-7
@@ -156,6 +162,25 @@ def test_backward_region_scales_differ():
             note(f"  image {b} {name}: max|err| {mx:.3e} (max|ref| {scale:.3e}), rel-L2 {rel:.3e}")
             assert rel <= GRAD_REL_L2, (b, name)
             assert mx <= GRAD_MAX_REL * scale, (b, name)
+
+
+def test_backward_single_token_windows():
+    """M = 1: every window holds one token, so P = 1, out = v and dS = P (dP - D) = 0 exactly:
+    dq, dk and dtheta are zero and dv is dout.  The kernels compute D from the same bf16 dO as
+    dP, so dS vanishes up to the fp32 rounding of the two sums."""
+    B, Hg, Wg, H, M, s = 1, 4, 6, 2, 1, 0
+    note(f"backward single-token windows: B={B} grid={Hg}x{Wg} H={H} M={M}")
+    q, k, v, th, dout, _, _ = _setup(B, Hg, Wg, H, M, 955)
+    got = _gpu(q, k, v, th, dout, M, s, True)
+    ref = oracle.window_attention_backward(q, k, v, dout, M, s, th)
+    for name in ("dq", "dk", "dtheta"):
+        assert float(np.max(np.abs(ref[name]))) < 1e-12, name
+        mx = float(np.max(np.abs(got[name])))
+        note(f"  {name}: max|got| {mx:.3e}")
+        assert mx <= 1e-4, name
+    mx, rel = errors(got["dv"], ref["dv"])
+    note(f"  dv: max|err| {mx:.3e}, rel-L2 {rel:.3e}")
+    assert rel <= GRAD_REL_L2
 
 
 def test_backward_scratch_contract():
@@ -180,7 +205,7 @@ def test_backward_scratch_contract():
     lib = wattn.load_library()
     nbytes = lib.wattn_backward_scratch_bytes(B, H, Hg, Wg, 32)
     rows = B * Hg * Wg * H
-    assert nbytes == 4 * ((rows + 3) // 4 * 4 + 33 * rows)
+    assert nbytes == 4 * ((rows + 3) // 4 * 4 + 33 * rows + 256 * 16 * H)
     scratch = torch.full((nbytes + 64,), 0xFF, dtype=torch.uint8, device=dev)  # NaN bytes
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
     dth = torch.empty((H, 16), dtype=torch.float32, device=dev)

@@ -263,10 +263,13 @@ extern "C" int wattn_forward_gated(const void* q, const void* k, const void* v, 
 
 namespace {
 
-// Backward scratch for `rows` query rows (T * H): the rowsum statistic as float32 [rows], padded
-// to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output gradient, [rows][32]
-// each, then one float per task (a task holds at least one query row, so at most `rows`).
-int64_t backward_scratch_bytes(int64_t rows) { return (((rows + 3) & ~int64_t(3)) + 33 * rows) * 4; }
+// Backward scratch for `rows` query rows (T * H) and H heads: the rowsum statistic as float32
+// [rows], padded to 16 bytes, then the rotated, scaled fp16 queries and the bf16 output
+// gradient, [rows][32] each, then one float per task (a task holds at least one query row, so
+// at most `rows`), then WATTN_DTHETA_COPIES copies of the partial angle-gradient sums [H][16].
+int64_t backward_scratch_bytes(int64_t rows, int64_t H) {
+  return (((rows + 3) & ~int64_t(3)) + 33 * rows + (int64_t)WATTN_DTHETA_COPIES * H * 16) * 4;
+}
 
 // Backward pass shared by wattn_backward, wattn_backward_gated (gz and dz both NULL or both
 // set) and wattn_backward_noalloc (library_scratch: scratch is NULL on entry and the
@@ -298,7 +301,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
   const size_t gbytes = (size_t)elems * (dtype == WATTN_BF16 ? 2 : 4);        // out, dout
   const size_t fbytes = (size_t)elems * 4;                                    // dq, dk, dv
   const size_t rbytes = (size_t)(elems / d) * 4;                              // lse
-  const size_t sbytes = (size_t)backward_scratch_bytes(elems / d);            // scratch
+  const size_t sbytes = (size_t)backward_scratch_bytes(elems / d, H);         // scratch
   if (library_scratch && sbytes > (size_t)WATTN_NOALLOC_SCRATCH_BYTES) return WATTN_ERR_SCRATCH;
   const size_t th_bytes = (size_t)H * (d / 2) * sizeof(float);
   const size_t b_bytes = (size_t)H * M * M * r * 2;   // bias factors (bf16)
@@ -354,7 +357,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* out, 
 
 extern "C" int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d) {
   if (B <= 0 || H <= 0 || Hgrid <= 0 || Wgrid <= 0 || d != 32) return -1;
-  return backward_scratch_bytes((int64_t)B * Hgrid * Wgrid * H);
+  return backward_scratch_bytes((int64_t)B * Hgrid * Wgrid * H, H);
 }
 
 extern "C" int wattn_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,

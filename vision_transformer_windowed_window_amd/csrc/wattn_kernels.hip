@@ -801,10 +801,10 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float x[8])
 }
 
 // un-rotate the gradient of four channels 4t' .. 4t'+3 (two rotation pairs j0, j0 + 1) at a
-// window position and add the pairs' angle-gradient terms pos * (g . J x) to sDth
+// window position and add the pairs' angle-gradient terms pos * (g . J x) to dth[0], dth[1]
 template <bool ROPE, int TSTR>
 __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j0, int pos, const float2* sTab,
-                                             const u32x2 raw, float* sDth, float out[4]) {
+                                             const u32x2 raw, float dth[2], float out[4]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float a = acc[2 * t] * scale, b = acc[2 * t + 1] * scale;
@@ -821,8 +821,35 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const float x0 = bf_lo(raw[t]), x1 = bf_hi(raw[t]);
-      atomicAdd(&sDth[j0 + t], (float)pos * (out[2 * t + 1] * x0 - out[2 * t] * x1));
+      dth[t] += (float)pos * (out[2 * t + 1] * x0 - out[2 * t] * x1);
     }
+  }
+}
+
+// The angle gradient: each lane holds the terms of pairs 8 cb + 2 g + t (cb, t in {0, 1}) of its
+// rows.  They are summed over the 16 lanes of a row group, then over the workgroup's waves in
+// LDS, and each workgroup adds its 16 sums into copy blockIdx % WATTN_DTHETA_COPIES of the
+// head's partial sums (so that thousands of workgroups do not queue on the same 16 addresses);
+// wattn_dtheta_reduce_kernel adds the copies up.
+template <int NW>
+__device__ __forceinline__ void dtheta_flush(float (&acc)[2][2], float (*sDthw)[D / 2], float* __restrict__ dth_part,
+                                             int h, int H, int tid) {
+  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float v = acc[cb][t];
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) v += __shfl_xor(v, s);
+      if (c == 0) sDthw[wave][8 * cb + 2 * g + t] = v;
+    }
+  __syncthreads();
+  if (tid < D / 2) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += sDthw[w][tid];
+    atomicAdd(dth_part + ((int64_t)(blockIdx.x % WATTN_DTHETA_COPIES) * H + h) * (D / 2) + tid, sum);
   }
 }
 
@@ -848,7 +875,7 @@ template <int NW, bool ROPE, bool OUTF32, int BR, bool GATE>
 __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dtheta, const float* __restrict__ theta,
+    float* __restrict__ delta, float* __restrict__ dq, float* __restrict__ dth_part, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbu,
     const uint16_t* __restrict__ gz, float* __restrict__ dz, uint16_t* __restrict__ qt,
     uint16_t* __restrict__ dot, float* __restrict__ tmax, const WattnPlan P) {
@@ -860,7 +887,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * BR : 8];  // bias factor v of the keys (fp16)
-  __shared__ float sDth[D / 2];
+  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
@@ -873,7 +900,6 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
-  if (tid < D / 2) sDth[tid] = 0.f;
 
   // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
   //      (preset with the row's gradient-scale exponent); with a bias, u * log2(e) as a k = 32
@@ -912,12 +938,12 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   for (int a = 0; a < 2; ++a) {
     float Dp = 0.f, L2 = 0.f;
     if (qvalid[a]) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Dp += go[a][e] * o[a][e];
       L2 = lraw[a] * LOG2E;
       if (GATE) {
         // out is sigmoid(z) * attention: the attention's output gradient is dout * sigmoid(z),
         // dz = dout * out * (1 - sigmoid(z)), and D = rowsum(dout * out) is unchanged
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Dp += go[a][e] * o[a][e];
         float gzv[8];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -936,6 +962,14 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) go[a][e] = 0.f;
     }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
+    // D from the same bf16 dO that dP uses, so that the row's dS = P (dP - D) sums to zero up
+    // to the rounding of P, as it does exactly (with a gate: the given dout and out)
+    if (!GATE && qvalid[a]) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Dp += bf_lo(dOf[a][p]) * o[a][2 * p] + bf_hi(dOf[a][p]) * o[a][2 * p + 1];
+    }
     const float Dn = xsum32(xsum16(Dp));  // the four lanes of query c hold 8 dims each
     if (qvalid[a] && g == 0) delta[qoff[a] / D] = Dn;
     float gm = 0.f;
@@ -952,8 +986,6 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     }
     CnL[a] = f32x4{-L2, -L2, -L2, -L2};
     CnD[a] = f32x4{-Dn, -Dn, -Dn, -Dn};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
   }
 
   // ---- K/V tile loader (thread t: chunk t % 4 of key t / 4, in K and V; with a rank-32 bias
@@ -1171,6 +1203,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
       for (int cb = 0; cb < 2; ++cb)
         if (qvalid[a]) qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
   }
+  float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [channel block][pair]: this lane's angle-gradient terms
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (!qvalid[a]) continue;
@@ -1179,14 +1212,11 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
       float r4[4];
       const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];  // channels 0..15 rotate with the row
       finish_grad4<ROPE, TSTR>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos,
-                               sTab, qr2[a][cb], sDth, r4);
+                               sTab, qr2[a][cb], dth[cb], r4);
       *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
-  if (ROPE) {
-    __syncthreads();
-    if (tid < D / 2) atomicAdd(&dtheta[X.t.h * (D / 2) + tid], sDth[tid]);
-  }
+  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
@@ -1194,7 +1224,7 @@ template <int NW, bool ROPE, int BR>
 __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dot, const float* __restrict__ lse, const float* __restrict__ delta,
-    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dtheta, const float* __restrict__ theta,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dth_part, const float* __restrict__ theta,
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
     const float* __restrict__ tmax, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
@@ -1207,7 +1237,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   __shared__ __align__(16) uint16_t sUb[BIAS ? 2 : 1][BIAS ? QTT * BR : 8];  // u * log2(e) of the queries (fp16)
   __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
-  __shared__ float sDth[D / 2];
+  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
@@ -1220,7 +1250,6 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
-  if (tid < D / 2) sDth[tid] = 0.f;
   // the largest output-gradient entry of the region: the query-tile kernel's entries of the
   // region's tiles (tasks task - qt .. task - qt + nqt - 1, which hold the same region and
   // head), reduced after the first barrier (see grad_scale_exp)
@@ -1475,6 +1504,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
       for (int x = 0; x < 2; ++x)
         if (kvalid[a]) kr2[a][x] = *reinterpret_cast<const u32x2*>(k + koffs[a] + 16 * x + 4 * g);
   }
+  float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [channel block][pair]: this lane's angle-gradient terms
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (!kvalid[a]) continue;
@@ -1485,14 +1515,471 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
                       dV[x][a][3] * gunscale);
       float r4[4];
       const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
-      finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], sDth, r4);
+      finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], dth[x], r4);
       *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
-  if (ROPE) {
-    __syncthreads();
-    if (tid < D / 2) atomicAdd(&dtheta[X.t.h * (D / 2) + tid], sDth[tid]);
+  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
+}
+
+// ---- Kernel C: the whole backward pass of one wrap region of at most 64 tokens (window side
+//      M <= 8) and one head, in a workgroup of two waves.  The region's K, V, Q~ and dO~ sit
+//      in LDS at once.  Phase A does the query-tile kernel's work for the region's queries
+//      (wave w: queries 32 w .. 32 w + 31) against every key and leaves P and dS of each pair
+//      in LDS, [query][key]; phase B does the key-tile kernel's products (wave w: keys
+//      32 w .. 32 w + 31) with P and dS read back transposed.  The scores, dP and the
+//      exponentials are computed once per pair, nothing is staged in memory, and every sum
+//      (dq over the region's keys; dk, dv over its queries) is complete inside the workgroup.
+//      The gradient scale: per query row for dq and dU, as in kernel A; one per region (the
+//      workgroup's largest output-gradient entry) for the P and dS that phase B consumes.
+constexpr int SMALL_REGION = 64;  // tokens of a region the fused kernel holds (every region at M <= 8)
+// 16-byte chunk swizzle of the [query][key] P and dS tiles (rows of 64 entries, 8 chunks)
+__device__ __forceinline__ int pswz(int row) { return row & 7; }
+
+template <bool ROPE, bool OUTF32, int BR, bool GATE>
+__global__ __launch_bounds__(128, BR ? 2 : 4) void wattn_bwd_small_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dth_part,
+    const float* __restrict__ theta, const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv,
+    float* __restrict__ dbu, float* __restrict__ dbv, const uint16_t* __restrict__ gz, float* __restrict__ dz,
+    const WattnPlan P) {
+  constexpr int NW = 2, NTHR = 64 * NW, NR = SMALL_REGION;
+  constexpr int TSTR = bwd_table_stride(NW);
+  constexpr bool BIAS = BR > 0;
+  constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
+  static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
+  static_assert(NR == 32 * NW, "one query and one key block of 32 per wave");
+  __shared__ __align__(16) uint16_t sK[NR * D];   // rotated k, fp16
+  __shared__ __align__(16) uint16_t sV[NR * D];   // v, bf16
+  __shared__ __align__(16) uint16_t sQ[NR * D];   // rotated q times log2(e) / sqrt(d), fp16
+  __shared__ __align__(16) uint16_t sO[NR * D];   // dO (times the gate), bf16
+  __shared__ __align__(16) uint16_t sP[NR * NR];  // 2^e P, bf16, [query][key]
+  __shared__ __align__(16) uint16_t sS[NR * NR];  // 2^e dS, fp16, [query][key]
+  __shared__ __align__(16) uint16_t sKb[BIAS ? NR * BR : 8];  // bias factor v of the keys (fp16)
+  __shared__ __align__(16) uint16_t sUb[BIAS ? NR * BR : 8];  // u log2(e) of the queries (fp16)
+  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
+  __shared__ float sGmax[NW];
+  extern __shared__ float2 sTab[];
+
+  const int tid = threadIdx.x;
+  Task T0;
+  if (!decode_task(P, task_of_block(P, blockIdx.x), NR, T0)) return;
+  const TaskCtx X = make_ctx(P, T0, NR);
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int M = P.M, n = X.n;  // n <= NR
+  const int colstride = P.H * D, rowstride = P.Wg * colstride;
+  float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this lane's angle-gradient terms, both phases
+
+  // ---- this lane's queries 32 wave + 16 a + c, channels 8 g .. 8 g + 7 (as in kernel A); all
+  //      loads first, from valid addresses
+  u32x4 qraw[2], dOf[2], Qb[2];
+  f32x4 CnL[2], CnD[2];
+  int qpos_r[2], qpos_c[2];
+  int64_t qoff[2];
+  bool qvalid[2];
+  float go[2][8], o[2][8], lraw[2];
+  u32x4 zraw[2], braw[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int iq = wave * 32 + 16 * a + c;
+    qvalid[a] = iq < n;
+    int li = 0, lj = 0;
+    if (qvalid[a]) split_idx(X, (uint32_t)iq, li, lj);
+    qpos_r[a] = X.t.r0 + li;
+    qpos_c[a] = X.t.c0 + lj;
+    qoff[a] = X.img + X.regbase + li * rowstride + lj * colstride;
+    qraw[a] = *reinterpret_cast<const u32x4*>(q + qoff[a] + 8 * g);
+    load8<OUTF32>(dout, qoff[a] + 8 * g, go[a]);
+    load8<OUTF32>(out, qoff[a] + 8 * g, o[a]);
+    lraw[a] = lse[qoff[a] / D];
+    if (GATE) zraw[a] = *reinterpret_cast<const u32x4*>(gz + qoff[a] + 8 * g);
+    if (BIAS)
+      braw[a] = *reinterpret_cast<const u32x4*>(
+          bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * BR + 8 * (BR == 32 ? g : (g & 1)));
   }
+  // ---- the region's keys: thread t stages chunk t % 4 of keys t / 4 and t / 4 + 32 (keys past
+  //      the region end repeat its last key: finite data whose scores are masked), and the same
+  //      quarter of their bias-factor rows
+  const int lk = tid >> 2, lch = tid & 3;
+  u32x4 pk[2], pv[2], pb[2];
+  int lpos[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int key = lk + 32 * j;
+    int li, lj;
+    split_idx(X, (uint32_t)min(key, n - 1), li, lj);
+    const uint32_t off = (uint32_t)(X.regbase + li * rowstride + lj * colstride + 8 * lch) * 2u;
+    pk[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(k + X.img) + off);
+    pv[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(v + X.img) + off);
+    lpos[j] = (lch < 2) ? (X.t.r0 + li) : (X.t.c0 + lj);
+    pb[j] = u32x4{0u, 0u, 0u, 0u};
+    if (BIAS) {
+      const uint16_t* src = bv + ((int64_t)X.t.h * M * M + (X.t.r0 + li) * M + (X.t.c0 + lj)) * BR + (BR / 4) * lch;
+      if (BR == 16) {
+        const u32x2 h = *reinterpret_cast<const u32x2*>(src);
+        pb[j] = u32x4{h[0], h[1], 0u, 0u};
+      } else {
+        pb[j] = *reinterpret_cast<const u32x4*>(src);
+      }
+    }
+  }
+
+  // ---- per query row: D, the gate, the row's scale exponent, the operands
+  int gexp[2];
+  float wgmax = 0.f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    float Dp = 0.f, L2 = 0.f;
+    if (qvalid[a]) {
+      L2 = lraw[a] * LOG2E;
+      if (GATE) {  // as in kernel A: dO becomes dout * sigmoid(z), dz = dout * out * (1 - sigmoid(z))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Dp += go[a][e] * o[a][e];
+        float gzv[8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float s0 = sigmoidf_fast(bf_lo(zraw[a][p])), s1 = sigmoidf_fast(bf_hi(zraw[a][p]));
+          gzv[2 * p] = go[a][2 * p] * o[a][2 * p] * (1.0f - s0);
+          gzv[2 * p + 1] = go[a][2 * p + 1] * o[a][2 * p + 1] * (1.0f - s1);
+          go[a][2 * p] *= s0;
+          go[a][2 * p + 1] *= s1;
+        }
+        float* dst = dz + qoff[a] + 8 * g;
+        *reinterpret_cast<float4*>(dst) = make_float4(gzv[0], gzv[1], gzv[2], gzv[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(gzv[4], gzv[5], gzv[6], gzv[7]);
+      }
+    } else {
+      qraw[a] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) go[a][e] = 0.f;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
+    if (!GATE && qvalid[a]) {  // D from the bf16 dO that dP uses (as in kernel A)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Dp += bf_lo(dOf[a][p]) * o[a][2 * p] + bf_hi(dOf[a][p]) * o[a][2 * p + 1];
+    }
+    const float Dn = xsum32(xsum16(Dp));
+    float gm = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gm = fmaxf(gm, fabsf(go[a][e]));
+    gm = xmax32(xmax16(gm));
+    wgmax = fmaxf(wgmax, gm);
+    gexp[a] = grad_scale_exp(gm);
+    // a padded query gets -inf: its P and dS are exactly 0, in LDS too
+    const float cl = qvalid[a] ? (float)gexp[a] - L2 : -INFINITY;
+    Qb[a] = u32x4{0u, 0u, 0u, 0u};
+    if (BIAS && qvalid[a] && (BR == 32 || g < 2)) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Qb[a][p] = pack_f16(bf_lo(braw[a][p]) * LOG2E, bf_hi(braw[a][p]) * LOG2E);
+    }
+    CnL[a] = f32x4{cl, cl, cl, cl};
+    CnD[a] = f32x4{-Dn, -Dn, -Dn, -Dn};
+  }
+  {
+    float wm = wgmax;
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) wm = fmaxf(wm, __shfl_xor(wm, s));
+    if (lane == 0) sGmax[wave] = wm;
+  }
+  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  __syncthreads();
+  const int ereg = grad_scale_exp(fmaxf(sGmax[0], sGmax[1]));  // the region's exponent
+
+  // ---- LDS: rotated keys (fp16), values, bias factors of the keys; the lane's rotated, scaled
+  //      queries (fp16), dO~ (bf16) and u log2(e) (fp16) for phase B
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int key = lk + 32 * j;
+    u32x4 kr;
+    const int lp = min(lpos[j], M - 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf_lo(pk[j][p]), x1 = bf_hi(pk[j][p]);
+      if (ROPE) {
+        const float2 t = sTab[(4 * lch + p) * TSTR + lp];
+        kr[p] = pack_f16(x0 * t.x - x1 * t.y, x0 * t.y + x1 * t.x);
+      } else {
+        kr[p] = pack_f16(x0, x1);
+      }
+    }
+    *reinterpret_cast<u32x4*>(&sK[key * D + ((lch ^ kswz(key)) * 8)]) = kr;
+    *reinterpret_cast<u32x4*>(&sV[key * D + ((lch ^ vswz(key)) * 8)]) = pv[j];
+    if (BR == 16) {
+      const u32x2 br = {pack_f16(bf_lo(pb[j][0]), bf_hi(pb[j][0])), pack_f16(bf_lo(pb[j][1]), bf_hi(pb[j][1]))};
+      *reinterpret_cast<u32x2*>(&sKb[key * 16 + 8 * ((lch >> 1) ^ bswz(key)) + 4 * (lch & 1)]) = br;
+    }
+    if (BR == 32) {
+      u32x4 br;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) br[p] = pack_f16(bf_lo(pb[j][p]), bf_hi(pb[j][p]));
+      *reinterpret_cast<u32x4*>(&sKb[key * 32 + 8 * (lch ^ kswz(key))]) = br;
+    }
+  }
+  u32x4 Qf[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const float qscale = LOG2E * 0.17677669529663687f;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x0 = bf_lo(qraw[a][p]), x1 = bf_hi(qraw[a][p]);
+      if (ROPE) {
+        const int j = 4 * g + p;
+        const float2 t = sTab[j * TSTR + (j < D / 4 ? qpos_r[a] : qpos_c[a])];
+        const float r0 = x0 * t.x - x1 * t.y, r1 = x0 * t.y + x1 * t.x;
+        x0 = r0;
+        x1 = r1;
+      }
+      Qf[a][p] = pack_f16(x0 * qscale, x1 * qscale);
+    }
+    const int qi = wave * 32 + 16 * a + c;  // padded queries store zeros
+    *reinterpret_cast<u32x4*>(&sQ[qi * D + ((g ^ kswz(qi)) * 8)]) = Qf[a];
+    *reinterpret_cast<u32x4*>(&sO[qi * D + ((g ^ vswz(qi)) * 8)]) = dOf[a];
+    if (BR == 16 && g < 2) *reinterpret_cast<u32x4*>(&sUb[qi * 16 + 8 * (g ^ bswz(qi))]) = Qb[a];
+    if (BR == 32) *reinterpret_cast<u32x4*>(&sUb[qi * 32 + 8 * (g ^ kswz(qi))]) = Qb[a];
+  }
+  __syncthreads();
+
+  const int krow = 8 * (c >> 2) + (c & 3);
+  const int vrow = 8 * g + (c >> 2);
+  const int vch = (c & 3) >> 1, vsub = 4 * (c & 1);
+  const bool wave_live = wave * 32 < n;
+
+  // ---- phase A: dq (and dU) of the wave's queries over all keys; P and dS to LDS
+  if (wave_live) {
+    f32x4 dQ[2][2], dU[NBB][2];
+    float fscale[2];  // 2^(ereg - gexp): from the row's scale to the region's
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      dQ[0][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dQ[1][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < NBB; ++cb) dU[cb][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      fscale[a] = __builtin_ldexpf(1.0f, ereg - gexp[a]);
+    }
+    auto kblock = [&](int kb, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      u32x4 Kf[2], Vr[2], KTf[2], Kb[2], VbT[NBB];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int key = kb + krow + 4 * b;
+        Kf[b] = *reinterpret_cast<const u32x4*>(&sK[key * D + ((g ^ kswz(key)) * 8)]);
+        Vr[b] = *reinterpret_cast<const u32x4*>(&sV[key * D + ((g ^ vswz(key)) * 8)]);
+        if (BR == 16) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[key * 16 + 8 * ((g & 1) ^ bswz(key))]);
+        if (BR == 32) Kb[b] = *reinterpret_cast<const u32x4*>(&sKb[key * 32 + 8 * (g ^ kswz(key))]);
+      }
+      if (BIAS) {
+#pragma unroll
+        for (int cb = 0; cb < NBB; ++cb) {
+          u32x2 h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = kb + vrow + 4 * hh;
+            h[hh] = BR == 32 ? lds_read_tr16(&sKb[row * 32 + (((2 * cb + vch) ^ kswz(row)) * 8) + vsub])
+                             : lds_read_tr16(&sKb[row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+          }
+          VbT[cb] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        u32x2 h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = kb + vrow + 4 * hh;
+          h[hh] = lds_read_tr16(&sK[row * D + (((2 * cb + vch) ^ kswz(row)) * 8) + vsub]);
+        }
+        KTf[cb] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        f32x4 S[2], G[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          S[b] = BIAS ? mfma16_f16(Kb[b], Qb[a], CnL[a]) : CnL[a];
+          S[b] = mfma16_f16(Kf[b], Qf[a], S[b]);
+          G[b] = mfma16_bf16(Vr[b], dOf[a], CnD[a]);  // dP - D
+        }
+        uint32_t dS16[4], Pr[4], Sr[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int b = t >> 1, e0 = 2 * (t & 1);
+          float s0 = S[b][e0], s1 = S[b][e0 + 1];
+          if (MASK) {
+            if (kb + 8 * g + 4 * b + e0 >= n) s0 = -INFINITY;
+            if (kb + 8 * g + 4 * b + e0 + 1 >= n) s1 = -INFINITY;
+          }
+          const float p0 = __builtin_amdgcn_exp2f(s0), p1 = __builtin_amdgcn_exp2f(s1);
+          const float d0 = p0 * G[b][e0], d1 = p1 * G[b][e0 + 1];
+          dS16[t] = pack_f16(d0, d1);
+          Pr[t] = pack_bf16(p0 * fscale[a], p1 * fscale[a]);
+          Sr[t] = pack_f16(d0 * fscale[a], d1 * fscale[a]);
+        }
+        const u32x4 dSa = {dS16[0], dS16[1], dS16[2], dS16[3]};
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) dQ[cb][a] = mfma16_f16(KTf[cb], dSa, dQ[cb][a]);
+#pragma unroll
+        for (int cb = 0; cb < NBB; ++cb)
+          if (BIAS) dU[cb][a] = mfma16_f16(VbT[cb], dSa, dU[cb][a]);
+        // keys kb + 8 g .. kb + 8 g + 7 of query qi: one 16-byte chunk of its P and dS rows
+        const int qi = wave * 32 + 16 * a + c;
+        const int ch = ((kb >> 3) + g) ^ pswz(qi);
+        *reinterpret_cast<u32x4*>(&sP[qi * NR + 8 * ch]) = u32x4{Pr[0], Pr[1], Pr[2], Pr[3]};
+        *reinterpret_cast<u32x4*>(&sS[qi * NR + 8 * ch]) = u32x4{Sr[0], Sr[1], Sr[2], Sr[3]};
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < NR / 32; ++st) {
+      const int kb = st * 32;
+      if (kb + 32 <= n)
+        kblock(kb, std::false_type{});
+      else if (kb < n)
+        kblock(kb, std::true_type{});
+    }
+    // epilogue of phase A: dU, dq and the q part of dtheta (as in kernel A)
+    u32x2 qr2[2][2] = {};
+    if (ROPE) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          if (qvalid[a]) qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (!qvalid[a]) continue;
+      if (BIAS) {
+        float* dst = dbu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * BR + 4 * g;
+        const float us = __builtin_ldexpf(1.0f, -gexp[a]);
+#pragma unroll
+        for (int cb = 0; cb < NBB; ++cb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(dst + 16 * cb + e, dU[cb][a][e] * us);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float r4[4];
+        const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];
+        finish_grad4<ROPE, TSTR>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos,
+                                 sTab, qr2[a][cb], dth[cb], r4);
+        *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase B: dv, dk (and dV_b) of the wave's keys 32 wave + 16 a + c over all queries
+  if (wave_live) {
+    f32x4 dV[2][2], dK[2][2], dVb[NBB][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        dV[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dK[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int x = 0; x < NBB; ++x) dVb[x][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int st = 0; st < NR / 32; ++st) {
+      const int qb = st * 32;
+      if (qb < n) {
+        u32x4 OT[2], QTf[2], UT[NBB];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          u32x2 h[2], hq[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = qb + vrow + 4 * hh;
+            h[hh] = lds_read_tr16(&sO[row * D + (((2 * x + vch) ^ vswz(row)) * 8) + vsub]);
+            hq[hh] = lds_read_tr16(&sQ[row * D + (((2 * x + vch) ^ kswz(row)) * 8) + vsub]);
+          }
+          OT[x] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+          QTf[x] = u32x4{hq[0][0], hq[0][1], hq[1][0], hq[1][1]};
+        }
+        if (BIAS) {
+#pragma unroll
+          for (int x = 0; x < NBB; ++x) {
+            u32x2 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int row = qb + vrow + 4 * hh;
+              h[hh] = BR == 32 ? lds_read_tr16(&sUb[row * 32 + (((2 * x + vch) ^ kswz(row)) * 8) + vsub])
+                               : lds_read_tr16(&sUb[row * 16 + ((vch ^ bswz(row)) * 8) + vsub]);
+            }
+            UT[x] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
+          }
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          // B operands: key column 32 wave + 16 a + c, queries qb + 8 g .. qb + 8 g + 7
+          const int kch = 2 * (2 * wave + a) + vch;  // 8-key chunk of the column
+          u32x2 hp[2], hs[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = qb + vrow + 4 * hh;
+            hp[hh] = lds_read_tr16(&sP[row * NR + ((kch ^ pswz(row)) * 8) + vsub]);
+            hs[hh] = lds_read_tr16(&sS[row * NR + ((kch ^ pswz(row)) * 8) + vsub]);
+          }
+          const u32x4 Pa = {hp[0][0], hp[0][1], hp[1][0], hp[1][1]};
+          const u32x4 dSa = {hs[0][0], hs[0][1], hs[1][0], hs[1][1]};
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            dV[x][a] = mfma16_bf16(OT[x], Pa, dV[x][a]);
+            dK[x][a] = mfma16_f16(QTf[x], dSa, dK[x][a]);
+          }
+#pragma unroll
+          for (int x = 0; x < NBB; ++x)
+            if (BIAS) dVb[x][a] = mfma16_f16(UT[x], dSa, dVb[x][a]);
+        }
+      }
+    }
+    // epilogue of phase B: dV_b, dv, dk and the k part of dtheta (as in kernel B)
+    const float gunscale = __builtin_ldexpf(1.0f, -ereg), gunscale_ln2 = gunscale * LN2;
+    int kpos_r[2], kpos_c[2];
+    int64_t koffs[2];
+    bool kvalid[2];
+    u32x2 kr2[2][2] = {};
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int ik = wave * 32 + 16 * a + c;
+      kvalid[a] = ik < n;
+      int li = 0, lj = 0;
+      if (kvalid[a]) split_idx(X, (uint32_t)ik, li, lj);
+      kpos_r[a] = X.t.r0 + li;
+      kpos_c[a] = X.t.c0 + lj;
+      koffs[a] = X.img + X.regbase + li * rowstride + lj * colstride;
+      if (ROPE && kvalid[a]) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) kr2[a][x] = *reinterpret_cast<const u32x2*>(k + koffs[a] + 16 * x + 4 * g);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      if (!kvalid[a]) continue;
+      if (BIAS) {
+        float* dst = dbv + ((int64_t)X.t.h * M * M + kpos_r[a] * M + kpos_c[a]) * BR + 4 * g;
+#pragma unroll
+        for (int x = 0; x < NBB; ++x)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) atomicAdd(dst + 16 * x + e, dVb[x][a][e] * gunscale_ln2);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        *reinterpret_cast<float4*>(dv + koffs[a] + 16 * x + 4 * g) =
+            make_float4(dV[x][a][0] * gunscale, dV[x][a][1] * gunscale, dV[x][a][2] * gunscale,
+                        dV[x][a][3] * gunscale);
+        float r4[4];
+        const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
+        finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], dth[x], r4);
+        *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
+      }
+    }
+  }
+  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
 }
 
 // zeroes up to three float arrays in one launch (the backward pass's atomic targets), so that
@@ -1506,6 +1993,16 @@ __global__ void wattn_fill_zero_kernel(const ZeroList z) {
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (i < z.n[j]) z.p[j][i] = 0.f;
+}
+
+// dtheta[i] = the sum of the WATTN_DTHETA_COPIES partial sums of entry i (n = H * d / 2 entries)
+__global__ void wattn_dtheta_reduce_kernel(const float* __restrict__ part, float* __restrict__ dtheta, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < WATTN_DTHETA_COPIES; ++c) s += part[(int64_t)c * n + i];
+  dtheta[i] = s;
 }
 
 }  // namespace
@@ -1615,6 +2112,48 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
   return hipGetLastError();
 }
 
+// the fused kernel of regions of at most 64 tokens (window side M <= 8)
+template <bool ROPE, bool OUTF32, int BR, bool GATE>
+static hipError_t launch_small_inst(const WattnPlan& plan, const void* q, const void* k, const void* v,
+                                    const void* out, const void* dout, const float* lse, float* dq, float* dk,
+                                    float* dv, float* dtheta, const float* theta, const void* bu, const void* bv,
+                                    float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream) {
+  if (plan.nw != 2 || plan.M * plan.M > SMALL_REGION) return hipErrorInvalidValue;
+  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(2) * (D / 2) * sizeof(float2) : 0;
+  hipLaunchKernelGGL((wattn_bwd_small_kernel<ROPE, OUTF32, BR, GATE>), dim3(plan.grid), dim3(128), table_bytes,
+                     stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), out, dout, lse, dq, dk, dv, dtheta, theta,
+                     static_cast<const uint16_t*>(bu), static_cast<const uint16_t*>(bv), dbu, dbv,
+                     static_cast<const uint16_t*>(gz), dz, plan);
+  return hipGetLastError();
+}
+
+template <bool GATE>
+static hipError_t launch_small(const WattnPlan& plan, bool rope, bool out_f32, int br, const void* q, const void* k,
+                               const void* v, const void* out, const void* dout, const float* lse, float* dq,
+                               float* dk, float* dv, float* dtheta, const float* theta, const void* bu,
+                               const void* bv, float* dbu, float* dbv, const void* gz, float* dz,
+                               hipStream_t stream) {
+#define WATTN_SMALL_ARGS plan, q, k, v, out, dout, lse, dq, dk, dv, dtheta, theta, bu, bv, dbu, dbv, gz, dz, stream
+  const int sel = (br / 16) * 4 + (rope ? 2 : 0) + (out_f32 ? 1 : 0);
+  switch (sel) {
+    case 0: return launch_small_inst<false, false, 0, GATE>(WATTN_SMALL_ARGS);
+    case 1: return launch_small_inst<false, true, 0, GATE>(WATTN_SMALL_ARGS);
+    case 2: return launch_small_inst<true, false, 0, GATE>(WATTN_SMALL_ARGS);
+    case 3: return launch_small_inst<true, true, 0, GATE>(WATTN_SMALL_ARGS);
+    case 4: return launch_small_inst<false, false, 16, GATE>(WATTN_SMALL_ARGS);
+    case 5: return launch_small_inst<false, true, 16, GATE>(WATTN_SMALL_ARGS);
+    case 6: return launch_small_inst<true, false, 16, GATE>(WATTN_SMALL_ARGS);
+    case 7: return launch_small_inst<true, true, 16, GATE>(WATTN_SMALL_ARGS);
+    case 8: return launch_small_inst<false, false, 32, GATE>(WATTN_SMALL_ARGS);
+    case 9: return launch_small_inst<false, true, 32, GATE>(WATTN_SMALL_ARGS);
+    case 10: return launch_small_inst<true, false, 32, GATE>(WATTN_SMALL_ARGS);
+    case 11: return launch_small_inst<true, true, 32, GATE>(WATTN_SMALL_ARGS);
+    default: return hipErrorInvalidValue;
+  }
+#undef WATTN_SMALL_ARGS
+}
+
 template <int NW, bool GATE>
 static hipError_t launch_bwd_nw(const WattnPlan& plan, bool rope, bool out_f32, int br, const void* q,
                                 const void* k, const void* v, const void* out, const void* dout, const float* lse,
@@ -1651,31 +2190,48 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
   if (br != 0 && br != 16 && br != 32) return hipErrorInvalidValue;
   // scratch: delta [TH] floats, then (16-byte aligned) the fp16 q~ and bf16 dO~ rows [TH][32],
   // then one float per task (at most TH: every task holds at least one query row), the
-  // largest output-gradient entry of the task's query tile
+  // largest output-gradient entry of the task's query tile, then the WATTN_DTHETA_COPIES
+  // copies of the partial angle-gradient sums [copy][H][d/2]
   const int64_t th = (int64_t)plan.B * plan.Hg * plan.Wg * plan.H;
   if (plan.ntasks > th) return hipErrorInvalidValue;
   float* delta = scratch;
   uint16_t* qt = reinterpret_cast<uint16_t*>(scratch + ((th + 3) & ~int64_t(3)));
   uint16_t* dot = qt + th * D;
   float* tmax = reinterpret_cast<float*>(dot + th * D);
-  // one launch clears every atomic target: dtheta and the bias-factor gradients
+  float* dth_part = tmax + th;
+  const int nth = plan.H * (D / 2);
+  // one launch clears every atomic target: the angle-gradient copies and the bias-factor gradients
   const int64_t nb64 = (int64_t)plan.H * plan.M * plan.M * br;
-  if (nb64 > 0x7fffff00LL) return hipErrorInvalidValue;  // one grid-stride-free launch covers them
+  const int64_t nd64 = rope ? (int64_t)WATTN_DTHETA_COPIES * nth : 0;
+  if (nb64 > 0x7fffff00LL || nd64 > 0x7fffff00LL) return hipErrorInvalidValue;  // one launch covers them
   const int nb = (int)nb64;
-  const ZeroList z = {{dtheta, dbu, dbv}, {rope ? plan.H * (D / 2) : 0, nb, nb}};
+  const ZeroList z = {{dth_part, dbu, dbv}, {(int)nd64, nb, nb}};
   const int zmax = std::max(z.n[0], nb);
   if (zmax > 0) {
     hipLaunchKernelGGL(wattn_fill_zero_kernel, dim3((unsigned)((zmax + 255) / 256)), dim3(256), 0, stream, z);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#define WATTN_BWD_ARGS plan, rope, out_f32, br, q, k, v, out, dout, lse, delta, dq, dk, dv, dtheta, theta, bu, bv, \
-                       dbu, dbv, gz, dz, qt, dot, tmax, stream
   const bool gate = gz != nullptr;
-  switch (plan.nw) {
-    case 2: return gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS);
-    case 4: return gate ? launch_bwd_nw<4, true>(WATTN_BWD_ARGS) : launch_bwd_nw<4, false>(WATTN_BWD_ARGS);
-    default: return hipErrorInvalidValue;
-  }
+  hipError_t e;
+  if (plan.nw == 2 && plan.M * plan.M <= SMALL_REGION) {
+    // every region of a window of at most 8 x 8 fits one workgroup: one fused kernel
+    e = gate ? launch_small<true>(plan, rope, out_f32, br, q, k, v, out, dout, lse, dq, dk, dv, dth_part, theta, bu,
+                                  bv, dbu, dbv, gz, dz, stream)
+             : launch_small<false>(plan, rope, out_f32, br, q, k, v, out, dout, lse, dq, dk, dv, dth_part, theta,
+                                   bu, bv, dbu, dbv, gz, dz, stream);
+  } else {
+#define WATTN_BWD_ARGS plan, rope, out_f32, br, q, k, v, out, dout, lse, delta, dq, dk, dv, dth_part, theta, bu, bv, \
+                       dbu, dbv, gz, dz, qt, dot, tmax, stream
+    switch (plan.nw) {
+      case 2: e = gate ? launch_bwd_nw<2, true>(WATTN_BWD_ARGS) : launch_bwd_nw<2, false>(WATTN_BWD_ARGS); break;
+      case 4: e = gate ? launch_bwd_nw<4, true>(WATTN_BWD_ARGS) : launch_bwd_nw<4, false>(WATTN_BWD_ARGS); break;
+      default: return hipErrorInvalidValue;
+    }
 #undef WATTN_BWD_ARGS
+  }
+  if (e != hipSuccess || !rope) return e;
+  hipLaunchKernelGGL(wattn_dtheta_reduce_kernel, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const float*>(dth_part), dtheta, nth);
+  return hipGetLastError();
 }

@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #define WATTN_MAX_SEG 9
+#define WATTN_DTHETA_COPIES 256  // copies of the backward pass's partial angle-gradient sums
 #define WATTN_F32_QTILE 256   // queries per workgroup of the fp32 path (one per thread)
 
 // Divisors the kernel needs come with recip(d) = min(floor(2^32 / d), 2^32 - 1), computed on the
