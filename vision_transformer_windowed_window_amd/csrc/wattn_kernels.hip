@@ -1536,8 +1536,9 @@ constexpr int SMALL_REGION = 64;  // tokens of a region the fused kernel holds (
 // 16-byte chunk swizzle of the [query][key] P and dS tiles (rows of 64 entries, 8 chunks)
 __device__ __forceinline__ int pswz(int row) { return row & 7; }
 
+// Two waves per SIMD: its 34-42 KB of LDS allow four workgroups per CU.
 template <bool ROPE, bool OUTF32, int BR, bool GATE>
-__global__ __launch_bounds__(128, BR ? 2 : 4) void wattn_bwd_small_kernel(
+__global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ out, const void* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dth_part,
