@@ -1996,14 +1996,20 @@ __global__ void wattn_fill_zero_kernel(const ZeroList z) {
     if (i < z.n[j]) z.p[j][i] = 0.f;
 }
 
-// dtheta[i] = the sum of the WATTN_DTHETA_COPIES partial sums of entry i (n = H * d / 2 entries)
-__global__ void wattn_dtheta_reduce_kernel(const float* __restrict__ part, float* __restrict__ dtheta, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < WATTN_DTHETA_COPIES; ++c) s += part[(int64_t)c * n + i];
-  dtheta[i] = s;
+// dtheta[i] = the sum of the WATTN_DTHETA_COPIES partial sums of entry i (n = H * d / 2 entries):
+// one workgroup of WATTN_DTHETA_COPIES threads per entry, thread c loads copy c, a fixed-order
+// tree sum (shuffles within the waves, then over the waves)
+static_assert(WATTN_DTHETA_COPIES == 256, "one 256-thread workgroup per dtheta entry");
+__global__ __launch_bounds__(WATTN_DTHETA_COPIES) void wattn_dtheta_reduce_kernel(const float* __restrict__ part,
+                                                                                float* __restrict__ dtheta, int n) {
+  __shared__ float sw[WATTN_DTHETA_COPIES / 64];
+  const int i = blockIdx.x, t = threadIdx.x;
+  float v = part[(int64_t)t * n + i];
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s);
+  if ((t & 63) == 0) sw[t >> 6] = v;
+  __syncthreads();
+  if (t == 0) dtheta[i] = (sw[0] + sw[1]) + (sw[2] + sw[3]);
 }
 
 }  // namespace
@@ -2232,7 +2238,7 @@ hipError_t wattn_launch_bwd(const WattnPlan& plan, bool rope, bool out_f32, cons
 #undef WATTN_BWD_ARGS
   }
   if (e != hipSuccess || !rope) return e;
-  hipLaunchKernelGGL(wattn_dtheta_reduce_kernel, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(wattn_dtheta_reduce_kernel, dim3((unsigned)nth), dim3(WATTN_DTHETA_COPIES), 0, stream,
                      static_cast<const float*>(dth_part), dtheta, nth);
   return hipGetLastError();
 }
