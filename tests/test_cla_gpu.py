@@ -64,6 +64,7 @@ def _gated_inputs(B, Hg, Wg, H, M, seed, rope=True, r=0):
 CASES = [
     # label, B, Hg, Wg, H, M, shift, rope, r, fp32 out
     ("m8_s4", 2, 16, 24, 3, 8, 4, True, 0, True),
+    ("m8_s3_bias_bf16_out", 1, 24, 16, 2, 8, 3, True, 16, False),  # the fused small-region backward
     ("m32_s16", 1, 64, 64, 2, 32, 16, True, 0, True),
     ("m16_bias_norope", 1, 32, 48, 2, 16, 0, False, 16, True),
     ("m16_s5_bf16_out", 1, 48, 32, 2, 16, 5, True, 0, False),

@@ -72,3 +72,10 @@ def test_noalloc_matches_caller_scratch_twice():
     _case(2, 64, 64, 3, 32, 16, 1401, 0)
     note("no-alloc backward: 1 x 32 x 48, 2 heads, M = 16, shift 5, rank-16 bias (3072 query rows)")
     _case(1, 32, 48, 2, 16, 5, 1402, 16)
+
+
+def test_noalloc_fused_small_windows():
+    """M = 8: the fused small-region kernel, which takes only the angle-gradient copies from the
+    scratch, with the library-held array left as the calls above (or a first call) left it."""
+    note("no-alloc backward: 2 x 32 x 32, 3 heads, M = 8, shift 4, rank-32 bias (6144 query rows)")
+    _case(2, 32, 32, 3, 8, 4, 1403, 32)

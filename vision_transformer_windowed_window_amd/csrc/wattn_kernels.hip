@@ -887,6 +887,8 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   __shared__ __align__(16) uint16_t sK[2][KT * D];
   __shared__ __align__(16) uint16_t sV[2][KT * D];
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * BR : 8];  // bias factor v of the keys (fp16)
+  // the tile's raw q rows, for the dtheta terms of the epilogue (written and read by the same wave)
+  __shared__ __align__(16) uint16_t sQraw[ROPE ? QT * D : 8];
   __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
@@ -962,6 +964,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) go[a][e] = 0.f;
     }
+    if (ROPE) *reinterpret_cast<u32x4*>(&sQraw[(wave * 32 + 16 * a + c) * D + 8 * g]) = qraw[a];
 #pragma unroll
     for (int p = 0; p < 4; ++p) dOf[a][p] = pack_bf16(go[a][2 * p], go[a][2 * p + 1]);
     // D from the same bf16 dO that dP uses, so that the row's dS = P (dP - D) sums to zero up
@@ -1194,14 +1197,14 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
         for (int e = 0; e < 4; ++e) atomicAdd(dst + 16 * cb + e, dU[cb][a][e] * us);
     }
   }
-  // the raw q channels of the dtheta sums, all loads issued before the first use
+  // the raw q channels of the dtheta sums (the prologue left the rows in LDS)
   u32x2 qr2[2][2] = {};
   if (ROPE) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
-        if (qvalid[a]) qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
+        qr2[a][cb] = *reinterpret_cast<const u32x2*>(&sQraw[(wave * 32 + 16 * a + c) * D + 16 * cb + 4 * g]);
   }
   float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [channel block][pair]: this lane's angle-gradient terms
 #pragma unroll
@@ -1237,6 +1240,8 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   __shared__ __align__(16) uint16_t sUb[BIAS ? 2 : 1][BIAS ? QTT * BR : 8];  // u * log2(e) of the queries (fp16)
   __shared__ __align__(16) float sL[2][QTT];  // -lse * log2(e) of the tile's queries
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
+  // the task's raw k rows, for the dtheta terms of the epilogue (written and read by the same wave)
+  __shared__ __align__(16) uint16_t sKraw[ROPE ? KTW * D : 8];
   __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
@@ -1355,6 +1360,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   u32x4 Kf[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (ROPE) *reinterpret_cast<u32x4*>(&sKraw[(wave * 32 + 16 * a + c) * D + 8 * g]) = kraw[a];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float x0 = bf_lo(kraw[a][p]), x1 = bf_hi(kraw[a][p]);
@@ -1495,14 +1501,14 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   }
 
   // ---- epilogue: dv, dk = R^T (dS^T Q~) ln 2, and the k part of dtheta (the raw k channels
-  //      of the dtheta sums loaded first, all before the first use)
+  //      of the dtheta sums from LDS, where the prologue left them)
   u32x2 kr2[2][2] = {};
   if (ROPE) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int x = 0; x < 2; ++x)
-        if (kvalid[a]) kr2[a][x] = *reinterpret_cast<const u32x2*>(k + koffs[a] + 16 * x + 4 * g);
+        kr2[a][x] = *reinterpret_cast<const u32x2*>(&sKraw[(wave * 32 + 16 * a + c) * D + 16 * x + 4 * g]);
   }
   float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // [channel block][pair]: this lane's angle-gradient terms
 #pragma unroll
@@ -1582,6 +1588,9 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
   bool qvalid[2];
   float go[2][8], o[2][8], lraw[2];
   u32x4 zraw[2], braw[2];
+  // raw q and k channels 16 cb + 4 g .. + 3 of the lane's rows, for the dtheta terms of the two
+  // epilogues (the wave's keys are its queries' tokens); loaded with the rest, kept in registers
+  u32x2 qr2[2][2] = {}, kr2[2][2] = {};
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int iq = wave * 32 + 16 * a + c;
@@ -1599,6 +1608,13 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     if (BIAS)
       braw[a] = *reinterpret_cast<const u32x4*>(
           bu + ((int64_t)X.t.h * M * M + qpos_r[a] * M + qpos_c[a]) * BR + 8 * (BR == 32 ? g : (g & 1)));
+    if (ROPE) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
+        kr2[a][cb] = *reinterpret_cast<const u32x2*>(k + qoff[a] + 16 * cb + 4 * g);
+      }
+    }
   }
   // ---- the region's keys: thread t stages chunk t % 4 of keys t / 4 and t / 4 + 32 (keys past
   //      the region end repeat its last key: finite data whose scores are masked), and the same
@@ -1840,14 +1856,6 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
         kblock(kb, std::true_type{});
     }
     // epilogue of phase A: dU, dq and the q part of dtheta (as in kernel A)
-    u32x2 qr2[2][2] = {};
-    if (ROPE) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          if (qvalid[a]) qr2[a][cb] = *reinterpret_cast<const u32x2*>(q + qoff[a] + 16 * cb + 4 * g);
-    }
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!qvalid[a]) continue;
@@ -1940,24 +1948,11 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     }
     // epilogue of phase B: dV_b, dv, dk and the k part of dtheta (as in kernel B)
     const float gunscale = __builtin_ldexpf(1.0f, -ereg), gunscale_ln2 = gunscale * LN2;
-    int kpos_r[2], kpos_c[2];
-    int64_t koffs[2];
-    bool kvalid[2];
-    u32x2 kr2[2][2] = {};
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int ik = wave * 32 + 16 * a + c;
-      kvalid[a] = ik < n;
-      int li = 0, lj = 0;
-      if (kvalid[a]) split_idx(X, (uint32_t)ik, li, lj);
-      kpos_r[a] = X.t.r0 + li;
-      kpos_c[a] = X.t.c0 + lj;
-      koffs[a] = X.img + X.regbase + li * rowstride + lj * colstride;
-      if (ROPE && kvalid[a]) {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) kr2[a][x] = *reinterpret_cast<const u32x2*>(k + koffs[a] + 16 * x + 4 * g);
-      }
-    }
+    // the wave's keys are the tokens of its queries: the same offsets, positions and validity
+    const int64_t* koffs = qoff;
+    const int* kpos_r = qpos_r;
+    const int* kpos_c = qpos_c;
+    const bool* kvalid = qvalid;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       if (!kvalid[a]) continue;
