@@ -741,9 +741,12 @@ __global__ __launch_bounds__(256) void wattn_fwd_f32_kernel(const float* __restr
 // part of dtheta.  Both use the same 16x16x32 MFMAs and LDS layouts as the forward pass.
 // ------------------------------------------------------------------------------------
 
-// The backward kernels run 2 waves per workgroup for windows below 12 and 4 waves above, so
-// the 4-wave table serves every window side up to 128.
-__host__ __device__ constexpr int bwd_table_stride(int NW) { return NW == 2 ? 18 : 130; }
+// Row stride (entries) of the backward kernels' cos/sin table for window side M: the
+// smallest stride >= M that is 2 mod 8, so that 32 * stride bytes is 64 mod 256 and the four
+// chunks of a row read distinct banks.  Sizing the table for the launch's own window (4.4 KB
+// at M = 32 rather than 16.6 KB for the largest window) lets the query-tile kernel keep four
+// workgroups on a CU.
+__host__ __device__ constexpr int bwd_table_stride(int M) { return M + ((2 - M) & 7); }
 
 // Region walk of one thread's row of a tile: region coordinates (ci, cj) and the element
 // offset of key / query idx + tile * KT, advanced by one tile at a time.
@@ -772,9 +775,9 @@ __device__ __forceinline__ void walker_advance(Walker& w, const TaskCtx& Y) {
 }
 
 // window-local cos/sin table of head h (pair-major rows of TSTR entries), fp32 angles
-template <int NTHR, int TSTR>
-__device__ __forceinline__ void build_rope_table(float2* sTab, const float* __restrict__ theta, int h, int M,
-                                                 int tid) {
+template <int NTHR>
+__device__ __forceinline__ void build_rope_table(float2* sTab, int TSTR, const float* __restrict__ theta, int h,
+                                                 int M, int tid) {
   for (int i = tid; i < M * (D / 2); i += NTHR) {
     const int pos = i >> 4, j = i & 15;
     float sn, cs;
@@ -802,9 +805,9 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, float x[8])
 
 // un-rotate the gradient of four channels 4t' .. 4t'+3 (two rotation pairs j0, j0 + 1) at a
 // window position and add the pairs' angle-gradient terms pos * (g . J x) to dth[0], dth[1]
-template <bool ROPE, int TSTR>
+template <bool ROPE>
 __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j0, int pos, const float2* sTab,
-                                             const u32x2 raw, float dth[2], float out[4]) {
+                                             int TSTR, const u32x2 raw, float dth[2], float out[4]) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float a = acc[2 * t] * scale, b = acc[2 * t + 1] * scale;
@@ -827,30 +830,30 @@ __device__ __forceinline__ void finish_grad4(const f32x4 acc, float scale, int j
 }
 
 // The angle gradient: each lane holds the terms of pairs 8 cb + 2 g + t (cb, t in {0, 1}) of its
-// rows.  They are summed over the 16 lanes of a row group, then over the workgroup's waves in
-// LDS, and each workgroup adds its 16 sums into copy blockIdx % WATTN_DTHETA_COPIES of the
-// head's partial sums (so that thousands of workgroups do not queue on the same 16 addresses);
-// wattn_dtheta_reduce_kernel adds the copies up.
+// rows.  They are summed over the 16 lanes of a row group (DPP row, no LDS round trip), and each
+// wave adds its 16 sums into copy (workgroup * NW + wave) % WATTN_DTHETA_COPIES of the head's
+// partial sums, so that tens of thousands of waves do not queue on the same 16 addresses and no
+// wave waits for the others of its workgroup; wattn_dtheta_reduce_kernel adds the copies up.
+__device__ __forceinline__ float rowsum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror 4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror 8
+  return x;
+}
 template <int NW>
-__device__ __forceinline__ void dtheta_flush(float (&acc)[2][2], float (*sDthw)[D / 2], float* __restrict__ dth_part,
-                                             int h, int H, int tid) {
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+__device__ __forceinline__ void dtheta_flush(float (&acc)[2][2], float* __restrict__ dth_part, int h, int H,
+                                             int tid) {
+  const int lane = tid & 63, g = lane >> 4, c = lane & 15;
+  float* dst =
+      dth_part + ((int64_t)(((int)blockIdx.x * NW + (tid >> 6)) % WATTN_DTHETA_COPIES) * H + h) * (D / 2);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float v = acc[cb][t];
-#pragma unroll
-      for (int s = 1; s < 16; s <<= 1) v += __shfl_xor(v, s);
-      if (c == 0) sDthw[wave][8 * cb + 2 * g + t] = v;
+      const float v = rowsum16(acc[cb][t]);
+      if (c == 0) atomicAdd(dst + 8 * cb + 2 * g + t, v);
     }
-  __syncthreads();
-  if (tid < D / 2) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) sum += sDthw[w][tid];
-    atomicAdd(dth_part + ((int64_t)(blockIdx.x % WATTN_DTHETA_COPIES) * H + h) * (D / 2) + tid, sum);
-  }
 }
 
 // dS = P (dP - D) is rounded to fp16 for the products of dq and dk: its size follows dout,
@@ -880,7 +883,6 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     const uint16_t* __restrict__ gz, float* __restrict__ dz, uint16_t* __restrict__ qt,
     uint16_t* __restrict__ dot, float* __restrict__ tmax, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, QT = 32 * NW, KT = 16 * NW;
-  constexpr int TSTR = bwd_table_stride(NW);
   constexpr bool BIAS = BR > 0;
   constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
   static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
@@ -889,7 +891,6 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   __shared__ __align__(16) uint16_t sKb[BIAS ? 2 : 1][BIAS ? KT * BR : 8];  // bias factor v of the keys (fp16)
   // the tile's raw q rows, for the dtheta terms of the epilogue (written and read by the same wave)
   __shared__ __align__(16) uint16_t sQraw[ROPE ? QT * D : 8];
-  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
@@ -901,6 +902,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
+  const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
 
   // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     if (lane == 0) sGmax[wave] = wm;                                      // xmax32/16 covered g
   }
   fetch(0);
-  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
   __syncthreads();
   if (tid == 0) {
     float wm = sGmax[0];
@@ -1183,6 +1185,23 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     __syncthreads();
   }
 
+  // the query rows' addresses and window positions again: recomputed from an opaque copy of
+  // the lane index, so that they are not held in registers across the key loop
+  {
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int ce = lane_e & 15;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int iq = X.t.q0 + wave * 32 + 16 * a + ce;
+      qvalid[a] = iq < n;
+      int li = 0, lj = 0;
+      if (qvalid[a]) split_idx(X, (uint32_t)iq, li, lj);
+      qpos_r[a] = X.t.r0 + li;
+      qpos_c[a] = X.t.c0 + lj;
+      qoff[a] = X.img + X.regbase + li * rowstride + lj * colstride;
+    }
+  }
   // ---- epilogue: the gradient of the bias factor u (shared by every window and image: added
   //      into its window position with atomics), dq = R^T (dS K) / sqrt(d), the q part of dtheta
   if (BIAS) {
@@ -1214,12 +1233,12 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     for (int cb = 0; cb < 2; ++cb) {
       float r4[4];
       const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];  // channels 0..15 rotate with the row
-      finish_grad4<ROPE, TSTR>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos,
-                               sTab, qr2[a][cb], dth[cb], r4);
+      finish_grad4<ROPE>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos, sTab,
+                         TSTR, qr2[a][cb], dth[cb], r4);
       *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
-  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
+  if (ROPE) dtheta_flush<NW>(dth, dth_part, X.t.h, P.H, tid);
 }
 
 // ---- Kernel B: dk, dv per key tile; rotated queries, dO and the per-query statistics streamed.
@@ -1231,7 +1250,6 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ bu, const uint16_t* __restrict__ bv, float* __restrict__ dbv,
     const float* __restrict__ tmax, const WattnPlan P) {
   constexpr int NTHR = 64 * NW, KTW = 32 * NW, QTT = 16 * NW;  // keys per task, queries per tile
-  constexpr int TSTR = bwd_table_stride(NW);
   constexpr bool BIAS = BR > 0;
   constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
   static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
@@ -1242,7 +1260,6 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   __shared__ __align__(16) float sDl[2][QTT];  // -D of the tile's queries
   // the task's raw k rows, for the dtheta terms of the epilogue (written and read by the same wave)
   __shared__ __align__(16) uint16_t sKraw[ROPE ? KTW * D : 8];
-  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
@@ -1254,6 +1271,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
+  const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   // the largest output-gradient entry of the region: the query-tile kernel's entries of the
   // region's tiles (tasks task - qt .. task - qt + nqt - 1, which hold the same region and
@@ -1350,7 +1368,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
   if (lane == 0) sGmax[wave] = rmax;
   fetch(0);
-  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
   __syncthreads();
   float gm = sGmax[0];
 #pragma unroll
@@ -1521,11 +1539,11 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
                       dV[x][a][3] * gunscale);
       float r4[4];
       const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
-      finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], dth[x], r4);
+      finish_grad4<ROPE>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, TSTR, kr2[a][x], dth[x], r4);
       *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
     }
   }
-  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
+  if (ROPE) dtheta_flush<NW>(dth, dth_part, X.t.h, P.H, tid);
 }
 
 // ---- Kernel C: the whole backward pass of one wrap region of at most 64 tokens (window side
@@ -1552,7 +1570,6 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     float* __restrict__ dbu, float* __restrict__ dbv, const uint16_t* __restrict__ gz, float* __restrict__ dz,
     const WattnPlan P) {
   constexpr int NW = 2, NTHR = 64 * NW, NR = SMALL_REGION;
-  constexpr int TSTR = bwd_table_stride(NW);
   constexpr bool BIAS = BR > 0;
   constexpr int NBB = BR == 32 ? 2 : 1;  // 16-channel blocks of the bias gradient
   static_assert(BR == 0 || BR == 16 || BR == 32, "bias rank 0, 16 or 32");
@@ -1565,7 +1582,6 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
   __shared__ __align__(16) uint16_t sS[NR * NR];  // 2^e dS, fp16, [query][key]
   __shared__ __align__(16) uint16_t sKb[BIAS ? NR * BR : 8];  // bias factor v of the keys (fp16)
   __shared__ __align__(16) uint16_t sUb[BIAS ? NR * BR : 8];  // u log2(e) of the queries (fp16)
-  __shared__ float sDthw[NW][D / 2];  // per-wave angle-gradient sums
   __shared__ float sGmax[NW];
   extern __shared__ float2 sTab[];
 
@@ -1576,6 +1592,7 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;  // n <= NR
+  const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this lane's angle-gradient terms, both phases
 
@@ -1701,7 +1718,7 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     for (int s = 1; s < 16; s <<= 1) wm = fmaxf(wm, __shfl_xor(wm, s));
     if (lane == 0) sGmax[wave] = wm;
   }
-  if (ROPE) build_rope_table<NTHR, TSTR>(sTab, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
   __syncthreads();
   const int ereg = grad_scale_exp(fmaxf(sGmax[0], sGmax[1]));  // the region's exponent
 
@@ -1871,8 +1888,8 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
       for (int cb = 0; cb < 2; ++cb) {
         float r4[4];
         const int pos = cb == 0 ? qpos_r[a] : qpos_c[a];
-        finish_grad4<ROPE, TSTR>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos,
-                                 sTab, qr2[a][cb], dth[cb], r4);
+        finish_grad4<ROPE>(dQ[cb][a], __builtin_ldexpf(0.17677669529663687f, -gexp[a]), 8 * cb + 2 * g, pos, sTab,
+                           TSTR, qr2[a][cb], dth[cb], r4);
         *reinterpret_cast<float4*>(dq + qoff[a] + 16 * cb + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
       }
     }
@@ -1970,12 +1987,12 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
                         dV[x][a][3] * gunscale);
         float r4[4];
         const int pos = x == 0 ? kpos_r[a] : kpos_c[a];
-        finish_grad4<ROPE, TSTR>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, kr2[a][x], dth[x], r4);
+        finish_grad4<ROPE>(dK[x][a], gunscale_ln2, 8 * x + 2 * g, pos, sTab, TSTR, kr2[a][x], dth[x], r4);
         *reinterpret_cast<float4*>(dk + koffs[a] + 16 * x + 4 * g) = make_float4(r4[0], r4[1], r4[2], r4[3]);
       }
     }
   }
-  if (ROPE) dtheta_flush<NW>(dth, sDthw, dth_part, X.t.h, P.H, tid);
+  if (ROPE) dtheta_flush<NW>(dth, dth_part, X.t.h, P.H, tid);
 }
 
 // zeroes up to three float arrays in one launch (the backward pass's atomic targets), so that
@@ -2094,8 +2111,7 @@ static hipError_t launch_bwd_inst(const WattnPlan& plan, const void* q, const vo
                                   float* dtheta, const float* theta, const void* bu, const void* bv, float* dbu,
                                   float* dbv, const void* gz, float* dz, uint16_t* qt, uint16_t* dot,
                                   float* tmax, hipStream_t stream) {
-  if (ROPE && plan.M > bwd_table_stride(NW)) return hipErrorInvalidValue;
-  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(NW) * (D / 2) * sizeof(float2) : 0;
+  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(plan.M) * (D / 2) * sizeof(float2) : 0;
   auto Q = static_cast<const uint16_t*>(q);
   auto K = static_cast<const uint16_t*>(k);
   auto V = static_cast<const uint16_t*>(v);
@@ -2121,7 +2137,7 @@ static hipError_t launch_small_inst(const WattnPlan& plan, const void* q, const 
                                     float* dv, float* dtheta, const float* theta, const void* bu, const void* bv,
                                     float* dbu, float* dbv, const void* gz, float* dz, hipStream_t stream) {
   if (plan.nw != 2 || plan.M * plan.M > SMALL_REGION) return hipErrorInvalidValue;
-  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(2) * (D / 2) * sizeof(float2) : 0;
+  const size_t table_bytes = ROPE ? (size_t)bwd_table_stride(plan.M) * (D / 2) * sizeof(float2) : 0;
   hipLaunchKernelGGL((wattn_bwd_small_kernel<ROPE, OUTF32, BR, GATE>), dim3(plan.grid), dim3(128), table_bytes,
                      stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), out, dout, lse, dq, dk, dv, dtheta, theta,
