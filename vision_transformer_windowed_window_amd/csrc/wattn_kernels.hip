@@ -774,15 +774,16 @@ __device__ __forceinline__ void walker_advance(Walker& w, const TaskCtx& Y) {
   }
 }
 
-// window-local cos/sin table of head h (pair-major rows of TSTR entries), fp32 angles
+// window-local cos/sin table (pair-major rows of TSTR entries), fp32 angles.  Every entry a
+// thread writes belongs to pair tid % 16 (NTHR is a multiple of 16), so the caller loads that
+// one angle, th, with its first batch of global loads.
 template <int NTHR>
-__device__ __forceinline__ void build_rope_table(float2* sTab, int TSTR, const float* __restrict__ theta, int h,
-                                                 int M, int tid) {
+__device__ __forceinline__ void build_rope_table(float2* sTab, int TSTR, float th, int M, int tid) {
+  static_assert(NTHR % 16 == 0, "one rotation pair per thread");
   for (int i = tid; i < M * (D / 2); i += NTHR) {
-    const int pos = i >> 4, j = i & 15;
     float sn, cs;
-    __sincosf((float)pos * theta[h * (D / 2) + j], &sn, &cs);
-    sTab[j * TSTR + pos] = make_float2(cs, sn);
+    __sincosf((float)(i >> 4) * th, &sn, &cs);
+    sTab[(i & 15) * TSTR + (i >> 4)] = make_float2(cs, sn);
   }
 }
 
@@ -903,6 +904,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
   const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
+  const float th_tab = ROPE ? theta[X.t.h * (D / 2) + (tid & 15)] : 0.f;  // the angle of this thread's table entries
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
 
   // ---- this lane's queries: q (rotated, scaled, fp16), dO (bf16), D and the row statistic
@@ -1049,7 +1051,7 @@ __global__ __launch_bounds__(64 * NW, BR ? 2 : 4) void wattn_bwd_dq_kernel(
     if (lane == 0) sGmax[wave] = wm;                                      // xmax32/16 covered g
   }
   fetch(0);
-  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, th_tab, M, tid);
   __syncthreads();
   if (tid == 0) {
     float wm = sGmax[0];
@@ -1272,6 +1274,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;
   const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
+  const float th_tab = ROPE ? theta[X.t.h * (D / 2) + (tid & 15)] : 0.f;  // the angle of this thread's table entries
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   // the largest output-gradient entry of the region: the query-tile kernel's entries of the
   // region's tiles (tasks task - qt .. task - qt + nqt - 1, which hold the same region and
@@ -1368,7 +1371,7 @@ __global__ __launch_bounds__(64 * NW, 2) void wattn_bwd_dkdv_kernel(
   for (int o = 1; o < 16; o <<= 1) rmax = fmaxf(rmax, __shfl_xor(rmax, o));
   if (lane == 0) sGmax[wave] = rmax;
   fetch(0);
-  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, th_tab, M, tid);
   __syncthreads();
   float gm = sGmax[0];
 #pragma unroll
@@ -1593,6 +1596,7 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int M = P.M, n = X.n;  // n <= NR
   const int TSTR = bwd_table_stride(M);  // cos/sin table row stride
+  const float th_tab = ROPE ? theta[X.t.h * (D / 2) + (tid & 15)] : 0.f;  // the angle of this thread's table entries
   const int colstride = P.H * D, rowstride = P.Wg * colstride;
   float dth[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // this lane's angle-gradient terms, both phases
 
@@ -1718,7 +1722,7 @@ __global__ __launch_bounds__(128, 2) void wattn_bwd_small_kernel(
     for (int s = 1; s < 16; s <<= 1) wm = fmaxf(wm, __shfl_xor(wm, s));
     if (lane == 0) sGmax[wave] = wm;
   }
-  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, theta, X.t.h, M, tid);
+  if (ROPE) build_rope_table<NTHR>(sTab, TSTR, th_tab, M, tid);
   __syncthreads();
   const int ereg = grad_scale_exp(fmaxf(sGmax[0], sGmax[1]));  // the region's exponent
 
