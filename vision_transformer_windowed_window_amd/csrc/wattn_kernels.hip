@@ -404,7 +404,10 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
   }
   const int n = X.n;
   const bool wave_live = X.t.q0 + wave * 32 < n;  // wave-uniform
-  const u32x4 ONES4 = {ONES, ONES, ONES, ONES};   // bf16 ones: the row-sum operand
+  // bf16 ones: the row-sum operand.  Made opaque to the compiler, so that it stays in four
+  // registers instead of being rebuilt from the constant with two moves in every step.
+  u32x4 ONES4 = {ONES, ONES, ONES, ONES};
+  asm volatile("" : "+v"(ONES4));
 
   // LDS operand fragments of one 32-key step
   struct KFrags {
