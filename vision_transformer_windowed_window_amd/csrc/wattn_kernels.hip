@@ -186,8 +186,10 @@ __host__ __device__ constexpr int table_stride(int NW) { return NW == 2 ? 18 : (
 // NW waves per workgroup (2, 4 or 8): 32 NW queries, key tiles of 16 NW keys.
 // NKS: 16-channel groups of the score product's contraction: 2 (d = 32, no bias), 3 (a rank-16
 // bias, zero-padded to a second k = 32 product) or 4 (a rank-32 bias, one full k = 32 product).
+// Every form runs four waves per SIMD (at most 128 VGPRs) except the 8-wave rank-16 kernel,
+// which needs more registers and runs one workgroup per CU.
 template <int NW, int NKS, bool ROPE, bool OUTF32, bool GATE>
-__global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * NW, (NKS == 3 && NW == 8) ? 2 : 4) void wattn_fwd_bf16_kernel(const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               void* __restrict__ out,
@@ -438,9 +440,9 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
     }
   };
 
-  // One key tile: up to four 32-key steps.  The score fragments of step st + 1 are read from
-  // LDS while step st is computed; the value fragments of a step are read at its start and
-  // land while its exponentials run.
+  // One key tile: up to four 32-key steps.  Without a bias the score fragments of step st + 1
+  // are read from LDS while step st is computed; the value fragments of a step are read at its
+  // start and land while its exponentials run.
   //
   // Lazy reference: p = 2^(s - r) with r at least 16 above every score seen when it was
   // set, so p <= 2^-16 until a score exceeds the running maximum by more than 16.  A step
@@ -451,16 +453,21 @@ __global__ __launch_bounds__(64 * NW, NKS >= 3 ? 2 : 4) void wattn_fwd_bf16_kern
   auto compute_tile = [&](int buf, int tile) {
     if (!wave_live) return;
     const int nst = min(KT / 32, (n - tile * KT + 31) / 32);  // steps holding keys (uniform)
-    KFrags F[2];
+    // Without a bias the score fragments of step st + 1 are read during step st (double
+    // buffer).  With a bias they are read at the start of their own step: the 16 registers
+    // saved bring the 4-wave kernel to 128 VGPRs, four waves per SIMD instead of three.
+    constexpr bool KDB = !BIAS;
+    KFrags F[KDB ? 2 : 1];
     load_kfrags(buf, 0, F[0]);
 #pragma unroll
     for (int st = 0; st < KT / 32; ++st) {
       if (st < nst) {
         const int kg = tile * KT + st * 32;  // first key of the step (uniform)
-        const KFrags& cur = F[st & 1];
+        if (!KDB && st > 0) load_kfrags(buf, st * 32, F[0]);
+        const KFrags& cur = F[KDB ? (st & 1) : 0];
         u32x4 Vf[2];
         load_vfrags(buf, st * 32, Vf);
-        if (st + 1 < nst) load_kfrags(buf, (st + 1) * 32, F[(st + 1) & 1]);
+        if (KDB && st + 1 < nst) load_kfrags(buf, (st + 1) * 32, F[(st + 1) & 1]);
 
         // S^T blocks: S[a][b][e] = score of query 16a + c and key kb + 8g + 4b + e, minus r
         f32x4 S[2][2];
