@@ -1,4 +1,4 @@
-"""Build libwattn.so and the pipe_rates program in-tree with hipcc for gfx950.
+"""Build libwattn.so and the pipe_rates and access_rates programs in-tree with hipcc for gfx950.
 
 Usage: python -m vision_transformer_windowed_window_amd.build
 """
@@ -17,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwattn.so")
 PIPE_RATES = os.path.join(PKG, "pipe_rates")  # instruction-rate probe run by bench.py
+ACCESS_RATES = os.path.join(PKG, "access_rates")  # HBM rate of the small-window access pattern
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -43,7 +44,7 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile csrc/ into libwattn.so and pipe_rates next to this file; return the library path."""
+    """Compile csrc/ into libwattn.so, pipe_rates and access_rates next to this file; return the library path."""
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="wattn_build_") as tmp:
         kobj = os.path.join(tmp, "wattn_kernels.o")
@@ -74,6 +75,11 @@ def build(verbose: bool = False) -> str:
               "-o", exe_tmp], verbose)
         shutil.move(exe_tmp, PIPE_RATES + ".tmp")
         os.replace(PIPE_RATES + ".tmp", PIPE_RATES)
+        acc_tmp = os.path.join(tmp, "access_rates")
+        _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, os.path.join(CSRC, "access_rates.hip"),
+              "-o", acc_tmp], verbose)
+        shutil.move(acc_tmp, ACCESS_RATES + ".tmp")
+        os.replace(ACCESS_RATES + ".tmp", ACCESS_RATES)
     return LIB
 
 
