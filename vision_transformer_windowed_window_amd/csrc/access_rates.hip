@@ -10,6 +10,8 @@
 //                  stride, and the three heads of a token are read by three workgroups;
 //   whole_tokens : one 384-thread workgroup per window: each token's 192 bytes are read as one
 //                  contiguous run by consecutive threads;
+//   per_head_x2  : per_head with two windows of the same head per workgroup: twice the loads in
+//                  flight per thread;
 //   copy         : a plain element-wise copy, 50 MB read and 50 MB written (grid-stride loop).
 // Prints one line per kernel: average microseconds per launch over 100 launches after 300 of
 // warm-up, and the rate against 8 TB/s.
@@ -74,6 +76,22 @@ __global__ __launch_bounds__(384) void gather_whole_tokens(const uint16_t* __res
   for (int r = 0; r < 2; ++r) emit(out + off[r], a[r], b[r], c[r]);
 }
 
+__global__ __launch_bounds__(128) void gather_per_head_x2(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, float* __restrict__ out) {
+  const int w0 = (blockIdx.x / H) * 2, h = blockIdx.x % H, t = threadIdx.x;
+  u32x4 a[4], b[4], c[4];
+  int64_t off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {  // windows w0 and w0 + 1, each as in gather_per_head
+    off[r] = token_offset(w0 + (r >> 1), (t >> 2) + 32 * (r & 1), h * D + (t & 3) * 8);
+    a[r] = *reinterpret_cast<const u32x4*>(q + off[r]);
+    b[r] = *reinterpret_cast<const u32x4*>(k + off[r]);
+    c[r] = *reinterpret_cast<const u32x4*>(v + off[r]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) emit(out + off[r], a[r], b[r], c[r]);
+}
+
 __global__ __launch_bounds__(256) void copy_f4(const float4* __restrict__ s, float4* __restrict__ d, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     d[i] = s[i];
@@ -108,15 +126,17 @@ int main() {
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
-  const char* names[3] = {"per_head", "whole_tokens", "copy"};
+  const char* names[4] = {"per_head", "whole_tokens", "per_head_x2", "copy"};
   int it = 0;
-  for (int which = 0; which < 3; ++which) {
+  for (int which = 0; which < 4; ++which) {
     auto launch = [&]() {
       const int s = (it++) % 3;
       if (which == 0)
         hipLaunchKernelGGL(gather_per_head, dim3(nwin * H), dim3(128), 0, 0, qs[s], ks[s], vs[s], os[s]);
       else if (which == 1)
         hipLaunchKernelGGL(gather_whole_tokens, dim3(nwin), dim3(384), 0, 0, qs[s], ks[s], vs[s], os[s]);
+      else if (which == 2)  // nwin is even
+        hipLaunchKernelGGL(gather_per_head_x2, dim3(nwin / 2 * H), dim3(128), 0, 0, qs[s], ks[s], vs[s], os[s]);
       else  // 50 MB of set s's out copied into its q buffer: 100 MB of traffic
         hipLaunchKernelGGL(copy_f4, dim3(4096), dim3(256), 0, 0, reinterpret_cast<const float4*>(os[s]),
                            reinterpret_cast<float4*>(qs[s]), n * 2 / 16);
@@ -131,7 +151,7 @@ int main() {
     float ms = 0.f;
     CHECK(hipEventElapsedTime(&ms, e0, e1));
     const double us = ms * 1e3 / 100;
-    const double bytes = which == 2 ? 2.0 * n * 2 : 3.0 * n * 2 + 4.0 * n;
+    const double bytes = which == 3 ? 2.0 * n * 2 : 3.0 * n * 2 + 4.0 * n;
     printf("%-13s %8.1f us  %6.0f GB/s  %5.1f%% of 8 TB/s\n", names[which], us, bytes / us * 1e-3,
            bytes / us * 1e-3 / 80.0);
   }
