@@ -170,7 +170,7 @@ int64_t wattn_backward_scratch_bytes(int B, int H, int Hgrid, int Wgrid, int d);
  *             angle-gradient sums into the copies at the end of the scratch.
  *   dq, dk, dv : float32 [B][Hgrid][Wgrid][H][d].
  *   dtheta  : float32 [H][d/2], written by a last small kernel from partial sums that the
- *             workgroups add into 256 copies in the scratch with atomic adds, so its last bits
+ *             waves add into 256 copies in the scratch with atomic adds, so its last bits
  *             depend on the order of the additions; required iff theta is not NULL.
  *   dbias_u, dbias_v : float32 [H][M*M][r], the gradients of the bias factors (summed over
  *             every window and image, which share them; zeroed, then accumulated with atomic
