@@ -10,6 +10,9 @@
 //                  stride, and the three heads of a token are read by three workgroups;
 //   whole_tokens : one 384-thread workgroup per window: each token's 192 bytes are read as one
 //                  contiguous run by consecutive threads;
+//   per_head_xcd : per_head with the workgroups dealt to the XCDs as the attention kernel deals
+//                  its tasks: runs of 16 consecutive (window, head) tasks to one XCD, so the
+//                  three heads of a token meet in one L2;
 //   per_head_x2  : per_head with two windows of the same head per workgroup: twice the loads in
 //                  flight per thread;
 //   copy         : a plain element-wise copy, 50 MB read and 50 MB written (grid-stride loop).
@@ -44,9 +47,14 @@ __device__ __forceinline__ int64_t token_offset(int w, int i, int inner) {
   return ((int64_t)(b * G + y) * G + x) * (H * D) + inner;
 }
 
+template <bool XCD>
 __global__ __launch_bounds__(128) void gather_per_head(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                        const uint16_t* __restrict__ v, float* __restrict__ out) {
-  const int w = blockIdx.x / H, h = blockIdx.x % H, t = threadIdx.x;
+  // workgroups are dealt to the 8 XCDs round-robin; with XCD, slot s of XCD x takes task
+  // (s / 16 * 8 + x) * 16 + s % 16 (the grid is a multiple of 128)
+  const int bid = blockIdx.x;
+  const int task = XCD ? (((bid >> 3) / 16 * 8 + (bid & 7)) * 16 + (bid >> 3) % 16) : bid;
+  const int w = task / H, h = task % H, t = threadIdx.x;
   u32x4 a[2], b[2], c[2];
   int64_t off[2];
 #pragma unroll
@@ -126,13 +134,15 @@ int main() {
   hipEvent_t e0, e1;
   CHECK(hipEventCreate(&e0));
   CHECK(hipEventCreate(&e1));
-  const char* names[4] = {"per_head", "whole_tokens", "per_head_x2", "copy"};
+  const char* names[5] = {"per_head", "whole_tokens", "per_head_x2", "copy", "per_head_xcd"};
   int it = 0;
-  for (int which = 0; which < 4; ++which) {
+  for (int which = 0; which < 5; ++which) {
     auto launch = [&]() {
       const int s = (it++) % 3;
       if (which == 0)
-        hipLaunchKernelGGL(gather_per_head, dim3(nwin * H), dim3(128), 0, 0, qs[s], ks[s], vs[s], os[s]);
+        hipLaunchKernelGGL(gather_per_head<false>, dim3(nwin * H), dim3(128), 0, 0, qs[s], ks[s], vs[s], os[s]);
+      else if (which == 4)  // nwin * H = 12288 is a multiple of 128
+        hipLaunchKernelGGL(gather_per_head<true>, dim3(nwin * H), dim3(128), 0, 0, qs[s], ks[s], vs[s], os[s]);
       else if (which == 1)
         hipLaunchKernelGGL(gather_whole_tokens, dim3(nwin), dim3(384), 0, 0, qs[s], ks[s], vs[s], os[s]);
       else if (which == 2)  // nwin is even
