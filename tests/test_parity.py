@@ -50,6 +50,11 @@ SMALL = [
     ("bf16_m16_s5_rope_bias32_ragged", 1, 48, 32, 2, 16, 5, "bf16", True, 32),
     ("bf16_m32_s16_rope_bias32", 1, 64, 64, 2, 32, 16, "bf16", True, 32),
     ("bf16_m48_bias32_norope", 1, 48, 96, 1, 48, 0, "bf16", False, 32),
+    # the 2-wave kernel (windows below 12) with the rank-16 bias, with and without RoPE
+    ("bf16_m8_s3_rope_bias", 2, 24, 32, 2, 8, 3, "bf16", True, 16),
+    ("bf16_m6_s2_bias_norope_ragged", 1, 18, 30, 3, 6, 2, "bf16", False, 16),
+    # the 4-wave rank-32 kernel without RoPE (windows of 12 to 23)
+    ("bf16_m20_s7_bias32_norope", 1, 40, 60, 2, 20, 7, "bf16", False, 32),
 ]
 
 
