@@ -856,8 +856,9 @@ template <int NW>
 __device__ __forceinline__ void dtheta_flush(float (&acc)[2][2], float* __restrict__ dth_part, int h, int H,
                                              int tid) {
   const int lane = tid & 63, g = lane >> 4, c = lane & 15;
-  float* dst =
-      dth_part + ((int64_t)(((int)blockIdx.x * NW + (tid >> 6)) % WATTN_DTHETA_COPIES) * H + h) * (D / 2);
+  // unsigned: the copy index stays in range for any grid size
+  const uint32_t copy = ((uint32_t)blockIdx.x * NW + (uint32_t)(tid >> 6)) % WATTN_DTHETA_COPIES;
+  float* dst = dth_part + ((int64_t)copy * H + h) * (D / 2);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
