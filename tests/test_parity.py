@@ -122,7 +122,7 @@ def test_large_query_scale():
     """Peaked softmax: q scaled by 2.5 beyond the N(0,1) workloads, the case that drives the
     lazy rescale hardest.  The rotated q and k are rounded to fp16 (11-bit significand) for
     the matrix cores, so the logit error grows with the logits; at this scale it stays within
-    the benchmark spec's bounds."""
+    the parity bounds."""
     note("start large q scale")
     f = 2.5
     inp = _inputs(1, 32, 32, 2, 16, "bf16", seed=5, qscale=f)

@@ -8,7 +8,7 @@ Each case puts large entries into one rotation pair (or one bias channel) of one
 zeroes the matching pair of the other operand, so the large entries contribute nothing to the
 logits: the rest of the logits are the usual N(0, 1) ones and the output is an ordinary,
 non-degenerate attention output.  Just below the limit the HIP path must match the oracle
-within the benchmark spec's bounds (the large entries are representable); just above it every
+within the parity bounds (the large entries are representable); just above it every
 output must be non-finite (an fp16 infinity times zero is NaN in the score product).
 
 A rotated pair keeps its norm, and at least one of its two components reaches norm / sqrt(2)
