@@ -40,6 +40,10 @@ def _bf(shape, seed, scale=1.0):
     (16, 1000, 768, 1000, 0, False, True),    # head: fp32 logits, N not a multiple of 16
     (77, 68, 32, 68, 0, False, False),        # ragged M and N
     (200, 132, 3072, 132, 0, True, False),    # the longest K of the model (96 k slices), residual
+    # large token counts (thousands of workgroups), ragged and in place
+    (131072, 288, 96, 96, 0, False, False),   # qkv projection of a large batch, split
+    (131000, 160, 64, 160, 1, False, False),  # GELU, ragged M and N
+    (131072, 96, 192, 96, 0, True, False),    # residual, in place
 ])
 def test_linear_matches_oracle(M, N, K, split, act, res, f32):
     import torch
