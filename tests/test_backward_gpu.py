@@ -85,6 +85,10 @@ CASES = [
     ("m8_s0_rank32_norope_bf16_out", 1, 24, 16, 3, 8, 0, False, False, 32),
     ("m6_s2_bias", 1, 18, 24, 2, 6, 2, True, True, 16),
     ("m2_s1_bf16_out", 2, 4, 8, 2, 2, 1, True, False),
+    # 8 < M < 12: regions beyond one workgroup, the two-kernel path with 2-wave workgroups
+    ("m10_s3", 1, 20, 30, 2, 10, 3, True, True),
+    ("m11_s5_bias_bf16_out", 1, 22, 22, 2, 11, 5, True, False, 16),
+    ("m9_s0_rank32_norope", 2, 18, 27, 1, 9, 0, False, True, 32),
 ]
 
 

@@ -55,6 +55,9 @@ SMALL = [
     ("bf16_m6_s2_bias_norope_ragged", 1, 18, 30, 3, 6, 2, "bf16", False, 16),
     # the 4-wave rank-32 kernel without RoPE (windows of 12 to 23)
     ("bf16_m20_s7_bias32_norope", 1, 40, 60, 2, 20, 7, "bf16", False, 32),
+    # 8 < M < 12: the 2-wave kernel with regions of several key tiles
+    ("bf16_m10_s3", 1, 20, 30, 2, 10, 3, "bf16", True, 0),
+    ("bf16_m11_s5_bias", 1, 22, 33, 2, 11, 5, "bf16", True, 16),
 ]
 
 
