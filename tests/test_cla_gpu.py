@@ -68,6 +68,7 @@ CASES = [
     ("m32_s16", 1, 64, 64, 2, 32, 16, True, 0, True),
     ("m16_bias_norope", 1, 32, 48, 2, 16, 0, False, 16, True),
     ("m16_s5_bf16_out", 1, 48, 32, 2, 16, 5, True, 0, False),
+    ("m10_s3_bias", 1, 20, 30, 2, 10, 3, True, 16, True),  # the 2-wave two-kernel backward
 ]
 
 
