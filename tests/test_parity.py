@@ -58,6 +58,8 @@ SMALL = [
     # 8 < M < 12: the 2-wave kernel with regions of several key tiles
     ("bf16_m10_s3", 1, 20, 30, 2, 10, 3, "bf16", True, 0),
     ("bf16_m11_s5_bias", 1, 22, 33, 2, 11, 5, "bf16", True, 16),
+    # the 8-wave kernel without RoPE or bias
+    ("bf16_m32_s16_norope", 1, 64, 64, 2, 32, 16, "bf16", False, 0),
 ]
 
 
