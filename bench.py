@@ -133,7 +133,10 @@ def pipe_bound(exps: float, mfma_flops: float, kernel_s: float):
         "kernel_vs_exp_plus_mfma": (t_exp + t_mfma) / (kernel_s * 1e6),
         "mfma_fma_split_vs_serial": rates["split_mfma_fma_ns_per_iteration"] / rates["serial_mfma_fma_ns_per_iteration"],
         "mfma_exp_interleaved_vs_serial": rates["interleaved_4mfma_16exp_ns"] / rates["serial_4mfma_16exp_ns"],
+        "exp_fma_same_wave_vs_serial": (rates["expfma_same_wave_ns_per_iteration"] / rates["serial_exp_fma_ns_per_iteration"]
+                                        if "expfma_same_wave_ns_per_iteration" in rates else None),
         "softmax_step_ns": step_ns,
+        "softmax_step_pipelined_ns": rates.get("softmax_step_pipelined_ns"),
         "steady_state_step_floor_us": t_steps,
         "kernel_vs_step_floor": (t_steps / (kernel_s * 1e6)) if t_steps else None,
         "shader_clock_ghz_mfma_load": rates.get("shader_clock_ghz_mfma_load"),

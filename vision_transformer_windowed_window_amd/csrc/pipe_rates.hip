@@ -11,10 +11,14 @@
 //   split  half the waves of every SIMD run the mfma pattern, half the fma pattern: equal to
 //          the sum of the two when the pipes do not overlap, the larger one when they do
 //   inter  one MFMA followed by four exps, four times, in every wave
+//   expfma sixteen exps and sixteen independent FMAs interleaved in every wave: equal to the
+//          sum of the exp and fma patterns when the two do not overlap
 //   step   the instruction mix of one 32-key step of the attention kernel per wave (two
 //          16-query blocks at d = 32): four fp16 score MFMAs, 16 exps, 8 bf16 packs, the bit
 //          test of the lazy rescale, four bf16 value MFMAs and two row-sum MFMAs, with its
 //          LDS fragment reads; the least time per step of the attention kernel's steady state
+//   pstep  the same step software-pipelined: the score MFMAs of step t+1 are issued before the
+//          exponentials of step t (two score sets live, 16 more registers)
 //   clock  the shader clock while every SIMD runs MFMAs: the shader-cycle counter (s_memtime)
 //          against the 100 MHz real-time counter (s_memrealtime), read by every workgroup
 //
@@ -42,7 +46,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int ITERS = 2048;
 constexpr int THREADS = 512;
 
-enum Pattern { P_MFMA = 0, P_EXP = 1, P_FMA = 2, P_INTER = 3 };
+enum Pattern { P_MFMA = 0, P_EXP = 1, P_FMA = 2, P_INTER = 3, P_EXPFMA = 4 };
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -58,9 +62,12 @@ __global__ __launch_bounds__(THREADS) void rate_kernel(float* out, float seed) {
   const u32x4 a = {0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f003f00u, 0x3f803f80u};
   const u32x4 b = {0x3f803f80u, 0x3f003f00u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u};
   f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0;
-  float x[16];
+  float x[16], y[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = seed * (float)(lane + i);  // in [0, 1): exp2(-x) stays in (0.5, 1]
+  for (int i = 0; i < 16; ++i) {
+    x[i] = seed * (float)(lane + i);  // in [0, 1): exp2(-x) stays in (0.5, 1]
+    y[i] = seed * (float)(lane + 2 * i);
+  }
   if (pattern == P_MFMA) {
     for (int it = 0; it < ITERS; ++it) {
       c0 = mfma(a, b, c0);
@@ -77,6 +84,14 @@ __global__ __launch_bounds__(THREADS) void rate_kernel(float* out, float seed) {
     for (int it = 0; it < ITERS; ++it) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = fmaf(x[i], 0.999f, 0.001f);
+    }
+  } else if (pattern == P_EXPFMA) {
+    for (int it = 0; it < ITERS; ++it) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(-x[i]);
+        y[i] = fmaf(y[i], 0.999f, 0.001f);
+      }
     }
   } else {
     for (int it = 0; it < ITERS; ++it) {
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(THREADS) void rate_kernel(float* out, float seed) {
   }
   float s = c0[0] + c1[1] + c2[2] + c3[3];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s += x[i];
+  for (int i = 0; i < 16; ++i) s += x[i] + y[i];
   out[(size_t)blockIdx.x * THREADS + threadIdx.x] = s;
 }
 
@@ -127,6 +142,7 @@ __global__ __launch_bounds__(THREADS) void clock_kernel(unsigned long long* stam
 // One attention step per iteration (see the header); the probabilities stay below 2^-16, so
 // the rescale branch is never taken, as in the kernel's steady state.
 constexpr int STEP_ITERS = 512;
+template <bool PIPE>
 __global__ __launch_bounds__(THREADS) void step_kernel(float* out, float seed) {
   __shared__ __align__(16) uint16_t sK[2][128 * 32];
   __shared__ __align__(16) uint16_t sV[2][128 * 32];
@@ -143,12 +159,43 @@ __global__ __launch_bounds__(THREADS) void step_kernel(float* out, float seed) {
   const f32x4 Cn = {-r, -r, -r, -r};
   f32x4 O[2][2] = {}, L[2] = {};
   int flag = 0;
-  for (int t = 0; t < STEP_ITERS; ++t) {
+  // K fragments of step t (rows kb .. kb + 31 of buffer t % 2, kb = 32 (t % 4): inside the tile)
+  auto kfrags = [&](int t, u32x4 (&Kf)[2]) {
     const int buf = t & 1, kb = (t & 3) * 32;
-    u32x4 Kf[2], Vf[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
       Kf[b] = *reinterpret_cast<const u32x4*>(&sK[buf][(kb + 8 * (c >> 2) + (c & 3) + 4 * b) * 32 + g * 8]);
+  };
+  auto scores = [&](const u32x4 (&Kf)[2], f32x4 (&S)[2][2]) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        S[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Kf[b]),
+                                                          __builtin_bit_cast(f16x8, Q[a]), Cn, 0, 0, 0);
+  };
+  f32x4 Snext[2][2];
+  if (PIPE) {
+    u32x4 K0[2];
+    kfrags(0, K0);
+    scores(K0, Snext);
+  }
+#pragma unroll(PIPE ? 2 : 1)
+  for (int t = 0; t < STEP_ITERS; ++t) {
+    const int buf = t & 1, kb = (t & 3) * 32;
+    u32x4 Kf[2], Vf[2];
+    f32x4 S[2][2];
+    if (PIPE) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) S[a][b] = Snext[a][b];
+      kfrags(t + 1, Kf);
+      scores(Kf, Snext);  // step t + 1, issued before the exponentials of step t
+    } else {
+      kfrags(t, Kf);
+      scores(Kf, S);
+    }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       u32x2 h[2];
@@ -160,13 +207,6 @@ __global__ __launch_bounds__(THREADS) void step_kernel(float* out, float seed) {
       }
       Vf[db] = u32x4{h[0][0], h[0][1], h[1][0], h[1][1]};
     }
-    f32x4 S[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        S[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Kf[b]),
-                                                          __builtin_bit_cast(f16x8, Q[a]), Cn, 0, 0, 0);
     uint32_t P[2][4], bits = 0u;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -245,15 +285,26 @@ int main() {
     fprintf(stderr, "pipe_rates: a HIP call failed\n");
     return 1;
   }
-  // attention step
-  float t_step = 1e30f;
+  float t_expfma;
+  if (!time_kernel<P_EXPFMA, P_EXPFMA>(C, reps, &t_expfma)) {
+    fprintf(stderr, "pipe_rates: a HIP call failed\n");
+    return 1;
+  }
+  // attention step, plain and software-pipelined
+  float t_step = 1e30f, t_pstep = 1e30f;
   for (int r = 0; r < reps; ++r) {
-    if (hipEventRecord(C.e0, nullptr) != hipSuccess) return 1;
-    hipLaunchKernelGGL(step_kernel, dim3(C.blocks), dim3(THREADS), 0, nullptr, C.buf, 0.5f);
-    if (hipEventRecord(C.e1, nullptr) != hipSuccess || hipEventSynchronize(C.e1) != hipSuccess) return 1;
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, C.e0, C.e1) != hipSuccess) return 1;
-    if (ms < t_step) t_step = ms;
+    for (int pipe = 0; pipe < 2; ++pipe) {
+      if (hipEventRecord(C.e0, nullptr) != hipSuccess) return 1;
+      if (pipe)
+        hipLaunchKernelGGL(step_kernel<true>, dim3(C.blocks), dim3(THREADS), 0, nullptr, C.buf, 0.5f);
+      else
+        hipLaunchKernelGGL(step_kernel<false>, dim3(C.blocks), dim3(THREADS), 0, nullptr, C.buf, 0.5f);
+      if (hipEventRecord(C.e1, nullptr) != hipSuccess || hipEventSynchronize(C.e1) != hipSuccess) return 1;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, C.e0, C.e1) != hipSuccess) return 1;
+      float& best = pipe ? t_pstep : t_step;
+      if (ms < best) best = ms;
+    }
   }
 
   // shader clock under MFMA load (cycles of s_memtime per 10 ns tick of s_memrealtime)
@@ -279,10 +330,13 @@ int main() {
   printf("{\"simds\": %d, \"shader_clock_ghz_mfma_load\": %.4f, \"waves_per_simd\": %.0f, \"ns_per_instruction\": {\"mfma_f32_16x16x32_bf16\": %.4f, "
          "\"exp_f32\": %.4f, \"fma_f32\": %.4f}, \"split_mfma_fma_ns_per_iteration\": %.4f, "
          "\"serial_mfma_fma_ns_per_iteration\": %.4f, \"interleaved_4mfma_16exp_ns\": %.4f, "
-         "\"serial_4mfma_16exp_ns\": %.4f, \"softmax_step_ns\": %.3f}\n",
+         "\"serial_4mfma_16exp_ns\": %.4f, \"expfma_same_wave_ns_per_iteration\": %.4f, "
+         "\"serial_exp_fma_ns_per_iteration\": %.4f, \"softmax_step_ns\": %.3f, "
+         "\"softmax_step_pipelined_ns\": %.3f}\n",
          simds, sclk_ghz, waves_per_simd, t_mfma * ns / (it_per_simd * 4), t_exp * ns / (it_per_simd * 16),
          t_fma * ns / (it_per_simd * 16), t_split * ns / it_per_simd,
          0.5 * (t_mfma + t_fma) * ns / it_per_simd, t_inter * ns / it_per_simd, (t_mfma + t_exp) * ns / it_per_simd,
-         t_step * ns / (waves_per_simd * STEP_ITERS));
+         t_expfma * ns / it_per_simd, (t_exp + t_fma) * ns / it_per_simd,
+         t_step * ns / (waves_per_simd * STEP_ITERS), t_pstep * ns / (waves_per_simd * STEP_ITERS));
   return 0;
 }
