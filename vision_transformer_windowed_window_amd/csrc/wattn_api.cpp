@@ -195,10 +195,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* out, float* 
   WattnPlan plan;
   WattnF32Plan fplan{};
   if (dtype != WATTN_FP32) {
-    // With the rank-16 bias the kernel holds 147-151 VGPRs at 4 waves (three 4-wave workgroups
-    // per CU) and 173-177 at 8 (a single 8-wave workgroup per CU): 4 waves measured 3-8% faster
-    // without RoPE.  (The 4-wave RoPE table holds windows up to 26 wide, so the bias with RoPE
-    // keeps the 8-wave kernel from M = 24 up.)
+    // With the rank-16 bias the 4-wave kernel fits four waves per SIMD (128 VGPRs) and the
+    // 8-wave one runs a single workgroup per CU (it spills at 128): without RoPE the 4-wave
+    // workgroups measured faster.  (The 4-wave RoPE table holds windows up to 26 wide, so the
+    // bias with RoPE keeps the 8-wave kernel from M = 24 up.)
     const int nw = (r && theta == nullptr) ? std::min(waves_for_window(M), 4) : waves_for_window(M);
     if (!build_plan(B, H, Hgrid, Wgrid, M, shift, plan, nw)) return WATTN_ERR_SHAPE;
   } else {
